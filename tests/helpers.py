@@ -1,0 +1,106 @@
+"""Test-side helpers: oracle-side cache construction and an independent
+NumPy/torch textbook attention used to pin the oracle.
+
+Nothing here touches the HIP library.
+"""
+import numpy as np
+import torch
+from scipy.special import logsumexp
+
+import oracle
+from paged_attention_fp8_amd import inputs as I
+
+FP8_NAN = 0x7F
+BF16_NAN = 0x7FC0
+
+
+def poison_value(kv_dtype):
+    return FP8_NAN if kv_dtype == oracle.KV_FP8 else BF16_NAN
+
+
+def padded_history(inp: I.DecodeInputs, reqs=None):
+    """[B][Tmax][Hkv][D] bf16 history (all tokens but this step's) and counts."""
+    reqs = list(range(inp.batch.batch)) if reqs is None else list(reqs)
+    w = inp.workload
+    counts = np.array([inp.k_tokens[b].shape[0] - 1 for b in reqs], np.int32)
+    T = max(1, int(counts.max()) if len(counts) else 1)
+    k = np.zeros((len(reqs), T, w.kv_heads, w.head_dim), np.uint16)
+    v = np.zeros_like(k)
+    for i, b in enumerate(reqs):
+        n = counts[i]
+        k[i, :n] = inp.k_tokens[b][:n]
+        v[i, :n] = inp.v_tokens[b][:n]
+    return k, v, counts
+
+
+def oracle_pool(inp: I.DecodeInputs, kv_dtype, poison=True, append=True, reqs=None):
+    """Build the oracle's copy of the cache: history via the bulk writer, this
+    step's token via the append (unless append=False)."""
+    w = inp.workload
+    fill = poison_value(kv_dtype) if poison else 0
+    pool = oracle.Pool(kv_dtype, inp.num_pages, w.kv_heads, w.page_size, w.head_dim, fill=fill)
+    reqs = list(range(inp.batch.batch)) if reqs is None else list(reqs)
+    ks = inp.k_scale if kv_dtype == oracle.KV_FP8 else None
+    vs = inp.v_scale if kv_dtype == oracle.KV_FP8 else None
+    table = inp.batch.page_table[reqs]
+    k, v, counts = padded_history(inp, reqs)
+    oracle.kv_write(pool, table, np.zeros(len(reqs), np.int32), counts, k, v, ks, vs)
+    if append:
+        oracle.kv_append(pool, table, inp.batch.context_lens[reqs], inp.k_new()[reqs],
+                         inp.v_new()[reqs], ks, vs)
+    return pool
+
+
+_E4M3 = None
+
+
+def e4m3_table_torch():
+    """Decode table from torch's float8_e4m3fn (independent of the oracle)."""
+    global _E4M3
+    if _E4M3 is None:
+        _E4M3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return _E4M3
+
+
+def dense_kv(pool, page_row, L, kv_dtype, k_scale=None, v_scale=None):
+    """Gather tokens [0, L) of one request from the pool by NumPy indexing of
+    the documented layout; returns fp64 K, V [L][Hkv][D]."""
+    t = np.arange(L)
+    pages = np.asarray(page_row)[t // pool.P]
+    slots = t % pool.P
+    kc = pool.k[pages, :, slots, :]
+    vc = pool.v[pages, :, :, slots]
+    if kv_dtype == oracle.KV_FP8:
+        tab = e4m3_table_torch()
+        K = tab[kc] * np.asarray(k_scale, np.float64)[None, :, None]
+        V = tab[vc] * np.asarray(v_scale, np.float64)[None, :, None]
+    else:
+        K = I.bf16_bits_to_f32(kc).astype(np.float64)
+        V = I.bf16_bits_to_f32(vc).astype(np.float64)
+    return K, V
+
+
+def textbook_attention(q_bf16, K, V, sm_scale):
+    """softmax(sm_scale * q K^T) V for all query heads of one request, fp64.
+    q: [Hq][D] bf16 bits; K, V: [L][Hkv][D]."""
+    q = I.bf16_bits_to_f32(q_bf16).astype(np.float64)
+    Hq, D = q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((Hq, D))
+    lse = np.zeros(Hq)
+    for h in range(Hq):
+        s = sm_scale * (K[:, h // G, :] @ q[h])
+        lse[h] = logsumexp(s)
+        out[h] = np.exp(s - lse[h]) @ V[:, h // G, :]
+    return out, lse
+
+
+def allclose_report(got, ref, atol=2e-3, rtol=1e-2):
+    """Element-wise |got - ref| <= atol + rtol*|ref|; returns (ok, max_abs, max_rel)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    ok = bool(np.all(err <= atol + rtol * np.abs(ref)))
+    rel = err / np.maximum(np.abs(ref), 1e-30)
+    return ok, float(err.max()) if err.size else 0.0, float(rel.max()) if rel.size else 0.0

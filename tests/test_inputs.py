@@ -1,0 +1,73 @@
+"""Host-side input recipe: bf16 rounding, determinism, the page pool."""
+import numpy as np
+import pytest
+import torch
+
+from paged_attention_fp8_amd import inputs as I
+
+
+def test_bf16_rounding_matches_torch():
+    g = np.random.default_rng(0)
+    x = np.concatenate([g.standard_normal(100_000).astype(np.float32) * 100,
+                        g.integers(0, 2 ** 32, 100_000, dtype=np.uint64).astype(np.uint32).view(np.float32),
+                        np.array([0.0, -0.0, np.inf, -np.inf, 3.4e38, -3.4e38, 1e-40], np.float32)])
+    fin = np.isfinite(x)
+    ours = I.f32_to_bf16_bits(x[fin])
+    ref = torch.from_numpy(x[fin]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    nan = I.f32_to_bf16_bits(np.array([np.nan], np.float32))
+    assert np.isnan(I.bf16_bits_to_f32(nan))[0]
+
+
+def test_inputs_are_deterministic_per_seed():
+    w = I.scaled(I.WORKLOADS["gqa4_4k_outliers"], batch=2, min_len=100, max_len=100)
+    a = I.make_decode_inputs(w, 42)
+    b = I.make_decode_inputs(w, 42)
+    c = I.make_decode_inputs(w, 43)
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.k_tokens[1], b.k_tokens[1])
+    assert np.array_equal(a.batch.page_table, b.batch.page_table)
+    assert not np.array_equal(a.q, c.q)
+
+
+def test_outlier_scale_uses_bulk_amax():
+    w = I.scaled(I.WORKLOADS["gqa4_4k_outliers"], batch=2, min_len=512, max_len=512)
+    inp = I.make_decode_inputs(w, 1)
+    allk = np.concatenate([I.bf16_bits_to_f32(k) for k in inp.k_tokens])
+    amax_all = np.abs(allk).max(axis=(0, 2))
+    assert np.all(amax_all > 448 * inp.k_scale)    # outliers exceed the range: saturation
+    assert np.all(inp.k_scale > 0) and inp.k_scale.dtype == np.float32
+
+
+def test_scale_closed_form():
+    s = I.fp8_scale_from_amax([448.0, 4.48, 0.0])
+    assert s[0] == np.float32(1.0) and s[1] == np.float32(4.48) / np.float32(448) and s[2] == 1.0
+
+
+def test_page_pool_alloc_tags_and_exhaustion():
+    pool = I.PagePool(10, seed=3)
+    a, ta = pool.alloc(4)
+    b, tb = pool.alloc(6)
+    assert len(set(a.tolist()) | set(b.tolist())) == 10
+    assert np.all(ta == 1) and np.all(tb == 1)
+    with pytest.raises(I.PoolExhausted):
+        pool.alloc(1)
+    pool.release(a[:2])
+    c, tc = pool.alloc(2)
+    assert sorted(c.tolist()) == sorted(a[:2].tolist()) and np.all(tc == 2)
+    pool.reallocate(int(b[0]))
+    assert pool.tags[b[0]] == 2
+
+
+def test_allocate_batch_shapes():
+    pool = I.PagePool(100, seed=0)
+    bt = I.allocate_batch(pool, [1, 16, 17, 33], 16)
+    assert bt.page_table.shape == (4, 3)
+    assert (bt.page_table[0, 1:] == -1).all() and (bt.page_table[3] >= 0).all()
+    assert bt.expected_tags[3].tolist() == [1, 1, 1]
+
+
+def test_workload_pool_sizes():
+    w = I.WORKLOADS["gqa8_16k_b64"]
+    assert w.pool_pages == 16384
+    assert I.sweep_workload(32, 2).pool_pages == 8192
+    assert I.WORKLOADS["gqa8_256k_b4"].group == 8

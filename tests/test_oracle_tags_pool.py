@@ -1,0 +1,238 @@
+"""Pins for the oracle's page-tag check (O6), pool writes (O4/O5) and combine
+(O8), and for the host page pool.
+
+The check follows the shared-cache protection section of Cloudflare's
+"Smaller, faster, safer: running Kimi and GLM at scale" ("共享 KV 缓存保护"):
+each physical page has a tag that changes on reallocation, each request
+records the pages and tags it expects, the mapping is verified before decode
+reads, and a mismatching request is terminated.  Its expected outcome is known
+by construction from host-side injection, and a plain Python brute force
+recomputes it.  The capacity invariants follow the KV cache quantization
+section ("KV 缓存量化"): e4m3 halves the cache, so the same memory holds twice
+the tokens, and the bf16 cache refuses the 33rd request where e4m3 reaches 64.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+import oracle
+from paged_attention_fp8_amd import inputs as I
+from helpers import e4m3_table_torch, oracle_pool
+
+
+def _brute_status(table, lens, expected, tags, P):
+    out = []
+    for b in range(len(lens)):
+        L = int(lens[b])
+        if L < 1 or L > table.shape[1] * P:
+            out.append(oracle.REQ_BAD_LEN)
+            continue
+        st = 0
+        for i in range(-(-L // P)):
+            p = int(table[b, i])
+            if not 0 <= p < len(tags):
+                st |= oracle.REQ_PAGE_OOB
+            elif int(tags[p]) != int(expected[b, i]):
+                st |= oracle.REQ_TAG_MISMATCH
+        out.append(st)
+    return np.array(out, np.int32)
+
+
+def test_tag_check_clean_batch_all_ok():
+    pool = I.PagePool(400, seed=1)
+    batch = I.allocate_batch(pool, [1, 16, 17, 100, 333], 16)
+    st = oracle.page_tag_check(batch.page_table, batch.context_lens, batch.expected_tags,
+                               pool.tags, 16)
+    assert np.all(st == 0)
+
+
+def test_tag_check_stale_oob_badlen_by_construction():
+    P = 16
+    pool = I.PagePool(1000, seed=2)
+    lens = np.array([40, 200, 16, 1, 500, 77, 300, 64], np.int32)
+    batch = I.allocate_batch(pool, lens, P)
+    I.make_stale(pool, batch, 1, 5)               # request 1: stale page
+    I.make_stale(pool, batch, 6, 0)               # request 6: stale first page
+    batch.page_table[3, 0] = 1000                 # request 3: page id beyond the pool
+    batch.page_table[4, 2] = -7                   # request 4: negative page id
+    I.make_stale(pool, batch, 4, 3)               #   ... and a stale page
+    lens2 = lens.copy()
+    lens2[5] = 0                                  # request 5: empty
+    lens2[7] = batch.max_pages * P + 1            # request 7: longer than its table
+    st = oracle.page_tag_check(batch.page_table, lens2, batch.expected_tags, pool.tags, P)
+    want = np.zeros(8, np.int32)
+    want[1] = want[6] = oracle.REQ_TAG_MISMATCH
+    want[3] = oracle.REQ_PAGE_OOB
+    want[4] = oracle.REQ_PAGE_OOB | oracle.REQ_TAG_MISMATCH
+    want[5] = want[7] = oracle.REQ_BAD_LEN
+    assert np.array_equal(st, want)
+    assert np.array_equal(st, _brute_status(batch.page_table, lens2, batch.expected_tags,
+                                            pool.tags, P))
+
+
+def test_tag_check_only_pages_in_use_are_checked():
+    # a stale tag on a page slot beyond the context is not the request's concern
+    P = 16
+    pool = I.PagePool(64, seed=3)
+    batch = I.allocate_batch(pool, [48], P, max_pages=4)
+    batch.page_table[0, 3] = 5
+    batch.expected_tags[0, 3] = 12345
+    st = oracle.page_tag_check(batch.page_table, batch.context_lens, batch.expected_tags,
+                               pool.tags, P)
+    assert st[0] == 0
+
+
+def test_tag_check_random_vs_brute():
+    g = np.random.default_rng(4)
+    for trial in range(20):
+        P = int(g.choice([16, 32, 64]))
+        B = int(g.integers(1, 40))
+        pool = I.PagePool(int(g.integers(200, 2000)), seed=trial)
+        lens = g.integers(1, 20 * P, B)
+        try:
+            batch = I.allocate_batch(pool, lens, P)
+        except I.PoolExhausted:
+            continue
+        for _ in range(int(g.integers(0, 5))):
+            b = int(g.integers(0, B))
+            I.make_stale(pool, batch, b, int(g.integers(0, I.pages_needed(lens[b], P))))
+        lens = lens.astype(np.int32)
+        lens[g.random(B) < 0.1] = 0
+        st = oracle.page_tag_check(batch.page_table, lens, batch.expected_tags, pool.tags, P)
+        assert np.array_equal(st, _brute_status(batch.page_table, lens, batch.expected_tags,
+                                                pool.tags, P))
+
+
+def test_tag_check_thousand_requests_one_stale():
+    """0.1% of 1000 requests (one) carries a stale tag: exactly it is flagged."""
+    P = 64
+    pool = I.PagePool(1000 * 64 + 10, seed=5)
+    batch = I.allocate_batch(pool, np.full(1000, 64 * 64, np.int32), P)
+    I.make_stale(pool, batch, 437, 17)
+    st = oracle.page_tag_check(batch.page_table, batch.context_lens, batch.expected_tags,
+                               pool.tags, P)
+    assert np.flatnonzero(st).tolist() == [437] and st[437] == oracle.REQ_TAG_MISMATCH
+
+
+# --- pool writes -----------------------------------------------------------------
+
+def test_pool_write_layout_and_codes():
+    """Tokens written through the oracle land at the documented offsets, as
+    torch's e4m3 encoding of f32(x)/scale."""
+    w = I.Workload("w", 2, 4, 2, 16, 8, 19, 30, pool_factor=2.0)
+    inp = I.make_decode_inputs(w, 3)
+    pool = oracle_pool(inp, oracle.KV_FP8, poison=False)
+    for b in range(2):
+        L = int(inp.batch.context_lens[b])
+        for t in range(L):
+            page = inp.batch.page_table[b, t // w.page_size]
+            slot = t % w.page_size
+            x_k = I.bf16_bits_to_f32(inp.k_tokens[b][t]) / inp.k_scale[:, None]
+            x_v = I.bf16_bits_to_f32(inp.v_tokens[b][t]) / inp.v_scale[:, None]
+            enc = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(pool.k[page, :, slot, :], enc(x_k))
+            assert np.array_equal(pool.v[page, :, :, slot], enc(x_v))
+            # flat offsets follow the same formula
+            flat = pool.k.reshape(-1)
+            assert flat[oracle.k_offset(int(page), 1, slot, 3, w.kv_heads, w.page_size, w.head_dim)] == pool.k[page, 1, slot, 3]
+            flatv = pool.v.reshape(-1)
+            assert flatv[oracle.v_offset(int(page), 1, slot, 3, w.kv_heads, w.page_size, w.head_dim)] == pool.v[page, 1, 3, slot]
+
+
+def test_append_equals_bulk_write_of_last_token():
+    w = I.Workload("w", 3, 4, 2, 16, 8, 5, 40, pool_factor=2.0)
+    inp = I.make_decode_inputs(w, 4)
+    a = oracle_pool(inp, oracle.KV_FP8, poison=False, append=True)
+    b = oracle_pool(inp, oracle.KV_FP8, poison=False, append=False)
+    lens = inp.batch.context_lens
+    oracle.kv_write(b, inp.batch.page_table, lens - 1, np.ones(3, np.int32),
+                    inp.k_new()[:, None], inp.v_new()[:, None], inp.k_scale, inp.v_scale)
+    assert np.array_equal(a.k, b.k) and np.array_equal(a.v, b.v)
+
+
+def test_append_skips_aborted_and_invalid():
+    w = I.Workload("w", 3, 4, 2, 16, 8, 20, 20, pool_factor=2.0)
+    inp = I.make_decode_inputs(w, 5)
+    base = oracle_pool(inp, oracle.KV_FP8, poison=False, append=False)
+    k0, v0 = base.k.copy(), base.v.copy()
+    lens = inp.batch.context_lens.copy()
+    lens[2] = 0
+    oracle.kv_append(base, inp.batch.page_table, lens, inp.k_new(), inp.v_new(), inp.k_scale,
+                     inp.v_scale, status=np.array([0, 1, 0], np.int32))
+    changed = np.argwhere(base.k != k0)
+    pages_changed = set(int(p) for p in changed[:, 0])
+    assert pages_changed == {int(inp.batch.page_table[0, 19 // 8])}
+    assert (base.v != v0).any()
+
+
+def test_bf16_append_copies_bits():
+    w = I.Workload("w", 2, 2, 2, 8, 16, 3, 9, pool_factor=2.0)
+    inp = I.make_decode_inputs(w, 6)
+    pool = oracle_pool(inp, oracle.KV_BF16, poison=False)
+    for b in range(2):
+        t = int(inp.batch.context_lens[b]) - 1
+        page, slot = inp.batch.page_table[b, t // 16], t % 16
+        assert np.array_equal(pool.k[page, :, slot, :], inp.k_new()[b])
+        assert np.array_equal(pool.v[page, :, :, slot], inp.v_new()[b])
+
+
+# --- capacity invariants ---------------------------------------------------------
+
+def test_fp8_cache_is_exactly_half_of_bf16():
+    a = oracle.Pool(oracle.KV_FP8, 37, 8, 64, 128)
+    b = oracle.Pool(oracle.KV_BF16, 37, 8, 64, 128)
+    assert 2 * (a.k.nbytes + a.v.nbytes) == b.k.nbytes + b.v.nbytes
+
+
+def test_same_budget_holds_64_fp8_or_32_bf16_requests():
+    n8 = I.pages_in_budget(I.SWEEP_BUDGET_BYTES, 8, 64, 128, 1)
+    n16 = I.pages_in_budget(I.SWEEP_BUDGET_BYTES, 8, 64, 128, 2)
+    assert n8 == 2 * n16 == 16384
+    fp8 = I.PagePool(n8, seed=0)
+    I.allocate_batch(fp8, [16384] * 64, 64)
+    assert fp8.free_pages == 0
+    bf = I.PagePool(n16, seed=0)
+    I.allocate_batch(bf, [16384] * 32, 64)
+    with pytest.raises(I.PoolExhausted):
+        bf.alloc(256)                               # the 33rd request does not fit
+
+
+# --- combine ----------------------------------------------------------------------
+
+def test_combine_single_split_is_identity():
+    g = np.random.default_rng(1)
+    po = g.standard_normal((2, 3, 1, 8)).astype(np.float32)
+    pl = g.standard_normal((2, 3, 1)).astype(np.float32)
+    o, l = oracle.splitk_combine(po, pl)
+    assert np.array_equal(o, po[:, :, 0].astype(np.float64))
+    assert np.array_equal(l, pl[:, :, 0].astype(np.float64))
+
+
+def test_combine_matches_scipy_logsumexp():
+    g = np.random.default_rng(2)
+    B, H, S, D = 3, 4, 7, 16
+    po = g.standard_normal((B, H, S, D)).astype(np.float32)
+    pl = (g.standard_normal((B, H, S)) * 30).astype(np.float32)
+    pl[0, 0, 2] = -np.inf
+    pl[1, 2, :] = -np.inf
+    o, l = oracle.splitk_combine(po, pl)
+    for b in range(B):
+        for h in range(H):
+            ls = pl[b, h].astype(np.float64)
+            if np.all(ls == -np.inf):
+                assert l[b, h] == -np.inf and np.all(o[b, h] == 0)
+                continue
+            LSE = logsumexp(ls)
+            w = np.exp(ls - LSE)
+            assert l[b, h] == pytest.approx(LSE, abs=1e-12)
+            assert np.allclose(o[b, h], (w[:, None] * po[b, h]).sum(0), rtol=1e-12, atol=1e-12)
+
+
+def test_combine_status_and_nan():
+    po = np.ones((2, 1, 3, 4), np.float32)
+    pl = np.zeros((2, 1, 3), np.float32)
+    pl[1, 0, 1] = np.nan
+    o, l = oracle.splitk_combine(po, pl, status=np.array([4, 0], np.int32))
+    assert np.all(o[0] == 0) and l[0, 0] == -np.inf
+    assert np.all(np.isnan(o[1])) and np.isnan(l[1, 0])
