@@ -1,0 +1,250 @@
+/*
+ * pafp8.h -- C ABI of libpafp8: FP8 (e4m3) paged decode attention on MI355X.
+ *
+ * What the library computes comes from Cloudflare's post "Smaller, faster,
+ * safer: running Kimi and GLM at scale" (3 Aug 2026) and its restatements:
+ *
+ *  - section "KV 缓存量化" (KV cache quantization): decode keeps its KV cache
+ *    as FP8 e4m3 instead of BF16, which halves the cache and doubles the
+ *    tokens it holds; the attention kernel converts the stored format when it
+ *    reads it.  A BF16-cache kernel is kept for direct comparison.
+ *  - section "共享 KV 缓存保护" (shared KV cache protection): many requests
+ *    read and write different pages of one physical KV cache; every physical
+ *    page has a tag that changes when the page is reallocated; the server
+ *    records the pages and tags each request expects and checks them before
+ *    decode reads the cache, terminating a request on mismatch.  The check is
+ *    a separate batched pass, not fused into attention; deployments that do
+ *    not enable it use a no-op tracker.
+ *  - remio.ai's analysis of the post (section on shared KV cache safety):
+ *    paged attention splits the cache into reusable blocks and keeps, for
+ *    every logical sequence, its mapping onto physical pages.
+ *
+ * The pages leave the numeric format, layout and arithmetic open; the
+ * readings taken here are stated with each call.
+ *
+ * Conventions for every call
+ *  - Pointers marked "device" are device memory owned by the caller (for
+ *    example torch tensors); the library never allocates or frees memory and
+ *    never keeps a pointer after the call returns.  Calls are asynchronous on
+ *    the caller's HIP stream; outputs are valid once that stream has reached
+ *    the call.  Pointers marked "host" are read before the call returns.
+ *  - A call that finds a problem on the host (NULL pointer, bad size,
+ *    unsupported shape, workspace too small) returns a status other than
+ *    PAFP8_OK and launches nothing; pafp8_last_error() then describes it.
+ *  - Problems in device data (page ids outside the pool, lengths outside a
+ *    request's page table, stale tags) never fault: they are reported per
+ *    request by page_tag_check, and the other calls neither read nor write
+ *    memory outside the pool for them (see each call).
+ *  - No float atomics: the same inputs and split count give bitwise
+ *    identical outputs.  The library has no global mutable state apart from a
+ *    thread-local error message and a per-device cache of the CU count.
+ *
+ * Pool layout (the "shared physical page pool"):
+ *   K pool: [num_pages][num_kv_heads][page_size][head_dim]   token-major
+ *   V pool: [num_pages][num_kv_heads][head_dim][page_size]   dim-major
+ * Elements are e4m3 codes (1 byte) or bf16 (2 bytes).  Token t of request b
+ * lives in physical page page_table[b][t / page_size], slot t % page_size.
+ * The same geometry therefore takes exactly half the bytes as e4m3.
+ */
+#ifndef PAFP8_H
+#define PAFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PAFP8_ABI_VERSION 1
+
+typedef int32_t pafp8_status;
+#define PAFP8_OK 0
+#define PAFP8_EINVAL 1        /* a pointer, size or value is invalid */
+#define PAFP8_EUNSUPPORTED 2  /* valid but not implemented (shape, dtype) */
+#define PAFP8_EHIP 3          /* a HIP runtime call or launch failed */
+
+/* Element type of the K/V pools. */
+#define PAFP8_KV_FP8_E4M3 0
+#define PAFP8_KV_BF16 1
+
+/* Per-request status flags written by page_tag_check (0 = OK). */
+#define PAFP8_REQ_TAG_MISMATCH 1  /* a page's tag differs from the recorded one */
+#define PAFP8_REQ_PAGE_OOB 2      /* a page id lies outside [0, num_pages) */
+#define PAFP8_REQ_BAD_LEN 4       /* context length < 1 or > max_pages_per_req * page_size */
+
+/* The shared physical page pool (layout above). */
+typedef struct pafp8_cache {
+    int32_t kv_dtype;      /* PAFP8_KV_FP8_E4M3 or PAFP8_KV_BF16 */
+    int32_t num_pages;     /* >= 1 */
+    int32_t page_size;     /* tokens per page: 16, 32, 64, 128 or 256 */
+    int32_t num_kv_heads;  /* >= 1 */
+    int32_t head_dim;      /* 64 or 128 */
+    int32_t reserved;      /* set to 0 */
+    void *k_pool;          /* device, K pool */
+    void *v_pool;          /* device, V pool */
+    const float *k_scale;  /* device [num_kv_heads]: value = decode(code) * k_scale[g]; e4m3 only */
+    const float *v_scale;  /* device [num_kv_heads]; e4m3 only.  Scales must be positive and finite. */
+} pafp8_cache;
+
+/* One decode step's batch: each request's logical-to-physical page mapping. */
+typedef struct pafp8_batch {
+    int32_t batch;              /* number of requests B >= 0 (0: calls do nothing) */
+    int32_t max_pages_per_req;  /* row length of page_table, >= 1 */
+    const int32_t *page_table;  /* device [B][max_pages_per_req]: physical page ids */
+    const int32_t *context_lens;/* device [B]: tokens attended this step, including the
+                                   token appended this step */
+    const int32_t *req_status;  /* device [B] from page_tag_check, or NULL for the
+                                   no-op tracker; a non-zero entry aborts the request */
+} pafp8_batch;
+
+/* ---------------------------------------------------------------------------
+ * page_tag_check -- the batched integrity check (section "共享 KV 缓存保护").
+ * For every request b with L = context_lens[b]:
+ *   if L < 1 or L > max_pages_per_req * page_size: status = PAFP8_REQ_BAD_LEN;
+ *   else, for each page index i < ceil(L / page_size), with
+ *   p = page_table[b][i]: PAFP8_REQ_PAGE_OOB if p is outside [0, num_pages),
+ *   else PAFP8_REQ_TAG_MISMATCH if page_tags[p] != expected_tags[b][i].
+ * req_status_out[b] is the OR of the flags (0 = the request may proceed).
+ * batch->req_status is ignored.  Run it before kv_quant_append and the
+ * attention call of the same step and pass req_status_out to them.
+ *   page_size      tokens per page (16, 32, 64, 128, 256)
+ *   page_tags      device uint32 [num_pages]: current tag of each physical page
+ *   expected_tags  device uint32 [B][max_pages_per_req]: tags the request recorded
+ *   req_status_out device int32 [B]
+ * Exact integer work: results are bit-exact.
+ * ------------------------------------------------------------------------- */
+pafp8_status page_tag_check(const pafp8_batch *batch, int32_t page_size,
+                            const uint32_t *page_tags, int32_t num_pages,
+                            const uint32_t *expected_tags, int32_t *req_status_out,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_quant_append -- write this step's K/V token of every request into its
+ * page (section "KV 缓存量化": the cache is stored as e4m3).
+ * The token goes to position pos = context_lens[b] - 1, i.e. page
+ * page_table[b][pos / page_size], slot pos % page_size.
+ * e4m3 pools: code = e4m3(f32(x) / scale[g]) with an IEEE single-precision
+ * division and round-to-nearest-even; magnitudes >= 448 and infinities
+ * saturate to +-448; NaN becomes 0x7F|sign.  bf16 pools: the bits are copied.
+ *   k_new, v_new  device bf16 bit patterns [B][num_kv_heads][head_dim]
+ * Requests with a non-zero batch->req_status entry, an invalid length or a
+ * page id outside the pool are skipped (nothing is written for them).
+ * Bit-exact.
+ * ------------------------------------------------------------------------- */
+pafp8_status kv_quant_append(const pafp8_cache *cache, const pafp8_batch *batch,
+                             const uint16_t *k_new, const uint16_t *v_new,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_quant_fill -- write a block of tokens per request (the prefill-to-decode
+ * hand-off: prefill keeps a BF16 cache, decode stores e4m3; section
+ * "KV 缓存量化").  Source token j < token_count[b] of request b goes to
+ * position token_start[b] + j, encoded as in kv_quant_append.
+ *   token_start, token_count  device int32 [B]
+ *   src_tokens                T, the row count of the source arrays (>= 1)
+ *   k_src, v_src              device bf16 [B][T][num_kv_heads][head_dim]
+ * Requires token_count[b] <= T (larger counts are clipped to T).  Positions
+ * outside [0, max_pages_per_req * page_size), page ids outside the pool and
+ * requests with a non-zero batch->req_status are skipped.  context_lens is
+ * not read.  Bit-exact.
+ * ------------------------------------------------------------------------- */
+pafp8_status kv_quant_fill(const pafp8_cache *cache, const pafp8_batch *batch,
+                           const int32_t *token_start, const int32_t *token_count,
+                           int32_t src_tokens, const uint16_t *k_src, const uint16_t *v_src,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Split-K (flash-decoding) sizing.  With num_splits = S > 1 each request's
+ * pages are cut into S consecutive chunks of ceil(max_pages_per_req / S)
+ * pages; each chunk produces a partial (o, lse) in the workspace and
+ * splitk_combine merges them.  pafp8_decode_workspace_bytes gives the
+ * workspace size (0 when S == 1); pafp8_default_num_splits picks S so that
+ * batch * num_kv_heads * S work-groups fill the GPU (num_cus <= 0: query
+ * the current device).  Pure host functions.
+ * ------------------------------------------------------------------------- */
+size_t pafp8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t num_splits);
+int32_t pafp8_default_num_splits(int32_t batch, int32_t num_kv_heads,
+                                 int32_t max_pages_per_req, int32_t page_size,
+                                 int32_t num_cus);
+
+/* ---------------------------------------------------------------------------
+ * paged_decode_attn_fp8 / paged_decode_attn_bf16 -- decode attention over the
+ * paged cache, converting e4m3 on read (section "KV 缓存量化"); the bf16 entry
+ * is the direct-comparison kernel over a bf16 pool.
+ * For request b, query head h, KV head g = h / G (G = num_q_heads /
+ * num_kv_heads, consecutive query heads share a KV head), L = context_lens[b]:
+ *   k_t = decode(K code) * k_scale[g]   (bf16 pool: the bf16 value)
+ *   s_t = sm_scale * sum_d q[b][h][d] * k_t[d]              t < L
+ *   lse[b][h] = log(sum_t exp(s_t))       (natural log)
+ *   out[b][h][:] = sum_t exp(s_t - lse) * v_t
+ * Arithmetic: K/V are decoded exactly; products and sums accumulate in fp32.
+ *   q        device bf16 bits [B][num_q_heads][head_dim]
+ *   sm_scale positive, finite (typically 1/sqrt(head_dim))
+ *   num_splits S >= 1 (0: pafp8_default_num_splits); S > 1 needs workspace
+ *   out      device fp32 [B][num_q_heads][head_dim]
+ *   lse      device fp32 [B][num_q_heads], or NULL
+ * G must be 1..16; cache->kv_dtype must match the entry point.
+ * Aborted requests (batch->req_status[b] != 0): out = 0, lse = -inf, and
+ * none of their pages are read.  With req_status NULL (no tracker) a request
+ * whose length is outside [0, max_pages_per_req * page_size] or whose pages
+ * include an id outside the pool gets NaN outputs instead of a fault; a
+ * request with length 0 gets out = 0, lse = -inf.
+ * ------------------------------------------------------------------------- */
+pafp8_status paged_decode_attn_fp8(const pafp8_cache *cache, const pafp8_batch *batch,
+                                   const uint16_t *q, int32_t num_q_heads, float sm_scale,
+                                   int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                   float *out, float *lse, hipStream_t stream);
+
+pafp8_status paged_decode_attn_bf16(const pafp8_cache *cache, const pafp8_batch *batch,
+                                    const uint16_t *q, int32_t num_q_heads, float sm_scale,
+                                    int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                    float *out, float *lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * splitk_combine -- merge per-split softmax partials (flash-decoding; not on
+ * the pages, which leave long-context scheduling open).  For each (b, h):
+ *   LSE = log sum_s exp(part_lse[b][h][s])
+ *   out[b][h][:] = sum_s exp(part_lse[b][h][s] - LSE) * part_o[b][h][s][:]
+ * Partials are normalised: part_o is the attention output over the split's
+ * tokens alone.  Splits with lse = -inf are empty; if every split is empty,
+ * out = 0 and lse = -inf.  A NaN partial lse makes (b, h) NaN.  A non-zero
+ * req_status[b] (nullable) gives out = 0, lse = -inf.
+ *   part_o   device fp32 [B][num_q_heads][num_splits][head_dim]
+ *   part_lse device fp32 [B][num_q_heads][num_splits]
+ *   out      device fp32 [B][num_q_heads][head_dim];  lse device fp32 [B][num_q_heads] or NULL
+ * head_dim must be a multiple of 4 and at most 1024.
+ * ------------------------------------------------------------------------- */
+pafp8_status splitk_combine(const float *part_o, const float *part_lse, int32_t batch,
+                            int32_t num_q_heads, int32_t num_splits, int32_t head_dim,
+                            const int32_t *req_status, float *out, float *lse,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * The device e4m3 codec the kernels use, exposed for conformance testing.
+ * pafp8_e4m3_encode: codes[i] = e4m3(x[i]) (rounding as kv_quant_append).
+ * pafp8_e4m3_decode: for each code, the value as produced by each of the
+ *   three decode routes the kernels use (direct to fp32, via fp16, via
+ *   bf16), widened to fp32; any output pointer may be NULL.
+ * All pointers device; n >= 0 elements.
+ * ------------------------------------------------------------------------- */
+pafp8_status pafp8_e4m3_encode(const float *x, uint8_t *codes, int64_t n, hipStream_t stream);
+pafp8_status pafp8_e4m3_decode(const uint8_t *codes, float *out_f32, float *out_via_f16,
+                               float *out_via_bf16, int64_t n, hipStream_t stream);
+
+/* Short name of a status code (static string). */
+const char *pafp8_status_string(pafp8_status status);
+/* Description of the last failure on the calling thread ("" if none). */
+const char *pafp8_last_error(void);
+/* PAFP8_ABI_VERSION of the built library, and sizeof of the two structs, so a
+ * binding can check it agrees with this header. */
+int32_t pafp8_abi_version(size_t *sizeof_cache, size_t *sizeof_batch);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAFP8_H */

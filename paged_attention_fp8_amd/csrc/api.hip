@@ -1,0 +1,416 @@
+// api.hip -- the C ABI declared in include/pafp8.h.
+//
+// Validation happens here, on the host, before anything is launched; a
+// rejected call returns a status and a message (pafp8_last_error) and touches
+// no device state.  Validation makes no HIP call, so it can be exercised on a
+// machine without a GPU.
+#include "pafp8.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "pafp8_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+pafp8_status fail(pafp8_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+pafp8_status ok()
+{
+    g_err[0] = '\0';
+    return PAFP8_OK;
+}
+
+pafp8_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess)
+        return ok();
+    return fail(PAFP8_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int log2_exact(int v)
+{
+    for (int k = 0; k < 31; ++k)
+        if (v == (1 << k))
+            return k;
+    return -1;
+}
+
+bool page_size_ok(int P) { return P == 16 || P == 32 || P == 64 || P == 128 || P == 256; }
+
+pafp8_status check_batch(const pafp8_batch *b, bool need_lens)
+{
+    if (b == nullptr)
+        return fail(PAFP8_EINVAL, "batch descriptor is NULL");
+    if (b->batch < 0)
+        return fail(PAFP8_EINVAL, "batch = %d < 0", b->batch);
+    if (b->max_pages_per_req < 1)
+        return fail(PAFP8_EINVAL, "max_pages_per_req = %d < 1", b->max_pages_per_req);
+    if (b->batch > 0 && b->page_table == nullptr)
+        return fail(PAFP8_EINVAL, "page_table is NULL");
+    if (need_lens && b->batch > 0 && b->context_lens == nullptr)
+        return fail(PAFP8_EINVAL, "context_lens is NULL");
+    return PAFP8_OK;
+}
+
+pafp8_status check_cache(const pafp8_cache *c, int want_dtype)
+{
+    if (c == nullptr)
+        return fail(PAFP8_EINVAL, "cache descriptor is NULL");
+    if (c->kv_dtype != PAFP8_KV_FP8_E4M3 && c->kv_dtype != PAFP8_KV_BF16)
+        return fail(PAFP8_EINVAL, "kv_dtype = %d is not a known pool type", c->kv_dtype);
+    if (want_dtype >= 0 && c->kv_dtype != want_dtype)
+        return fail(PAFP8_EINVAL, "pool type %s does not match this entry point (%s)",
+                    c->kv_dtype == PAFP8_KV_BF16 ? "bf16" : "e4m3",
+                    want_dtype == PAFP8_KV_BF16 ? "bf16" : "e4m3");
+    if (c->num_pages < 1)
+        return fail(PAFP8_EINVAL, "num_pages = %d < 1", c->num_pages);
+    if (!page_size_ok(c->page_size))
+        return fail(PAFP8_EUNSUPPORTED, "page_size = %d (supported: 16, 32, 64, 128, 256)",
+                    c->page_size);
+    if (c->num_kv_heads < 1)
+        return fail(PAFP8_EINVAL, "num_kv_heads = %d < 1", c->num_kv_heads);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(PAFP8_EUNSUPPORTED, "head_dim = %d (supported: 64, 128)", c->head_dim);
+    if (c->k_pool == nullptr || c->v_pool == nullptr)
+        return fail(PAFP8_EINVAL, "k_pool or v_pool is NULL");
+    if (!aligned16(c->k_pool) || !aligned16(c->v_pool))
+        return fail(PAFP8_EINVAL, "k_pool and v_pool must be 16-byte aligned");
+    if (c->kv_dtype == PAFP8_KV_FP8_E4M3 && (c->k_scale == nullptr || c->v_scale == nullptr))
+        return fail(PAFP8_EINVAL, "e4m3 pools need k_scale and v_scale");
+    const int64_t elems = static_cast<int64_t>(c->num_pages) * c->num_kv_heads * c->page_size *
+                          c->head_dim;
+    if (elems / c->num_pages / c->num_kv_heads != static_cast<int64_t>(c->page_size) * c->head_dim)
+        return fail(PAFP8_EINVAL, "pool geometry overflows");
+    return PAFP8_OK;
+}
+
+pafp8_status check_attn(const pafp8_cache *cache, const pafp8_batch *batch, const uint16_t *q,
+                        int32_t Hq, float sm_scale, int32_t S, void *ws, size_t ws_bytes,
+                        const float *out, int want_dtype)
+{
+    pafp8_status st = check_cache(cache, want_dtype);
+    if (st != PAFP8_OK)
+        return st;
+    if ((st = check_batch(batch, true)) != PAFP8_OK)
+        return st;
+    if (Hq < 1 || Hq % cache->num_kv_heads != 0)
+        return fail(PAFP8_EINVAL, "num_q_heads = %d is not a positive multiple of num_kv_heads = %d",
+                    Hq, cache->num_kv_heads);
+    const int G = Hq / cache->num_kv_heads;
+    if (G > 16)
+        return fail(PAFP8_EUNSUPPORTED, "query group size %d > 16", G);
+    if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f)
+        return fail(PAFP8_EINVAL, "sm_scale must be positive and finite");
+    if (S < 0)
+        return fail(PAFP8_EINVAL, "num_splits = %d < 0", S);
+    if (batch->batch > 0 && (q == nullptr || out == nullptr))
+        return fail(PAFP8_EINVAL, "q or out is NULL");
+    if (batch->batch > 0 && (!aligned16(q) || !aligned16(out)))
+        return fail(PAFP8_EINVAL, "q and out must be 16-byte aligned");
+    (void)ws;
+    (void)ws_bytes;
+    return PAFP8_OK;
+}
+
+// CU count per device, cached (the only process-wide state besides the
+// thread-local error text)
+std::mutex g_cu_mu;
+std::vector<int> g_cu;
+
+int device_cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 256;
+    std::lock_guard<std::mutex> lk(g_cu_mu);
+    if (dev >= static_cast<int>(g_cu.size()))
+        g_cu.resize(dev + 1, 0);
+    if (g_cu[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        g_cu[dev] = n;
+    }
+    return g_cu[dev];
+}
+
+pafp8_status attn_impl(const pafp8_cache *cache, const pafp8_batch *batch, const uint16_t *q,
+                       int32_t Hq, float sm_scale, int32_t S, void *ws, size_t ws_bytes,
+                       float *out, float *lse, hipStream_t stream, int want_dtype)
+{
+    pafp8_status st = check_attn(cache, batch, q, Hq, sm_scale, S, ws, ws_bytes, out, want_dtype);
+    if (st != PAFP8_OK)
+        return st;
+    if (batch->batch == 0)
+        return ok();
+    if (S == 0)
+        S = pafp8_default_num_splits(batch->batch, cache->num_kv_heads, batch->max_pages_per_req,
+                                     cache->page_size, 0);
+    if (S > batch->max_pages_per_req)
+        S = batch->max_pages_per_req;  // more splits than pages would all be empty
+    const size_t need = pafp8_decode_workspace_bytes(batch->batch, Hq, cache->head_dim, S);
+    if (need > 0) {
+        if (ws == nullptr || ws_bytes < need)
+            return fail(PAFP8_EINVAL, "num_splits = %d needs a workspace of %zu bytes (got %zu)",
+                        S, need, ws == nullptr ? size_t{0} : ws_bytes);
+        if (!aligned16(ws))
+            return fail(PAFP8_EINVAL, "workspace must be 16-byte aligned");
+    }
+    pafp8::AttnParams p{};
+    p.k_pool = static_cast<const uint8_t *>(cache->k_pool);
+    p.v_pool = static_cast<const uint8_t *>(cache->v_pool);
+    p.k_scale = cache->kv_dtype == PAFP8_KV_FP8_E4M3 ? cache->k_scale : nullptr;
+    p.v_scale = cache->kv_dtype == PAFP8_KV_FP8_E4M3 ? cache->v_scale : nullptr;
+    p.page_table = batch->page_table;
+    p.context_lens = batch->context_lens;
+    p.req_status = batch->req_status;
+    p.q = q;
+    p.out = out;
+    p.lse = lse;
+    p.num_pages = cache->num_pages;
+    p.log2_page = log2_exact(cache->page_size);
+    p.num_kv_heads = cache->num_kv_heads;
+    p.batch = batch->batch;
+    p.max_pages = batch->max_pages_per_req;
+    p.num_q_heads = Hq;
+    p.group = Hq / cache->num_kv_heads;
+    p.num_splits = S;
+    p.pages_per_split = (batch->max_pages_per_req + S - 1) / S;
+    p.sm_scale = sm_scale;
+    if (S > 1) {
+        p.part_o = static_cast<float *>(ws);
+        p.part_lse = p.part_o + static_cast<size_t>(batch->batch) * Hq * S * cache->head_dim;
+    }
+    hipError_t e = pafp8::launch_decode_attn(cache->kv_dtype == PAFP8_KV_BF16, cache->head_dim, p,
+                                             stream);
+    if (e != hipSuccess)
+        return hip_status(e, "paged_decode_attn launch");
+    if (S > 1) {
+        e = pafp8::launch_splitk_combine(p.part_o, p.part_lse, batch->batch, Hq, S,
+                                         cache->head_dim, batch->req_status, out, lse, stream);
+        if (e != hipSuccess)
+            return hip_status(e, "splitk_combine launch");
+    }
+    return ok();
+}
+
+pafp8_status write_impl(const pafp8_cache *cache, const pafp8_batch *batch, bool append,
+                        const int32_t *start, const int32_t *count, int32_t T,
+                        const uint16_t *k_src, const uint16_t *v_src, hipStream_t stream)
+{
+    pafp8_status st = check_cache(cache, -1);
+    if (st != PAFP8_OK)
+        return st;
+    if ((st = check_batch(batch, append)) != PAFP8_OK)
+        return st;
+    if (batch->batch == 0)
+        return ok();
+    if (k_src == nullptr || v_src == nullptr)
+        return fail(PAFP8_EINVAL, "source K/V is NULL");
+    if (!append) {
+        if (start == nullptr || count == nullptr)
+            return fail(PAFP8_EINVAL, "token_start or token_count is NULL");
+        if (T < 1)
+            return fail(PAFP8_EINVAL, "src_tokens = %d < 1", T);
+    }
+    pafp8::WriteParams p{};
+    p.k_pool = static_cast<uint8_t *>(cache->k_pool);
+    p.v_pool = static_cast<uint8_t *>(cache->v_pool);
+    p.k_scale = cache->k_scale;
+    p.v_scale = cache->v_scale;
+    p.page_table = batch->page_table;
+    p.req_status = batch->req_status;
+    p.context_lens = append ? batch->context_lens : nullptr;
+    p.token_start = start;
+    p.token_count = count;
+    p.k_src = k_src;
+    p.v_src = v_src;
+    p.src_tokens = append ? 1 : T;
+    p.num_pages = cache->num_pages;
+    p.log2_page = log2_exact(cache->page_size);
+    p.num_kv_heads = cache->num_kv_heads;
+    p.batch = batch->batch;
+    p.max_pages = batch->max_pages_per_req;
+    return hip_status(pafp8::launch_kv_write(cache->kv_dtype == PAFP8_KV_BF16, cache->head_dim, p,
+                                             stream),
+                      append ? "kv_quant_append launch" : "kv_quant_fill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+pafp8_status page_tag_check(const pafp8_batch *batch, int32_t page_size,
+                            const uint32_t *page_tags, int32_t num_pages,
+                            const uint32_t *expected_tags, int32_t *req_status_out,
+                            hipStream_t stream)
+{
+    pafp8_status st = check_batch(batch, true);
+    if (st != PAFP8_OK)
+        return st;
+    if (!page_size_ok(page_size))
+        return fail(PAFP8_EUNSUPPORTED, "page_size = %d (supported: 16, 32, 64, 128, 256)",
+                    page_size);
+    if (num_pages < 0)
+        return fail(PAFP8_EINVAL, "num_pages = %d < 0", num_pages);
+    if (batch->batch == 0)
+        return ok();
+    if (expected_tags == nullptr || req_status_out == nullptr || (num_pages > 0 && page_tags == nullptr))
+        return fail(PAFP8_EINVAL, "expected_tags, page_tags or req_status_out is NULL");
+    return hip_status(pafp8::launch_tag_check(batch->batch, batch->max_pages_per_req, page_size,
+                                              batch->page_table, batch->context_lens,
+                                              expected_tags, page_tags, num_pages,
+                                              req_status_out, stream),
+                      "page_tag_check launch");
+}
+
+pafp8_status kv_quant_append(const pafp8_cache *cache, const pafp8_batch *batch,
+                             const uint16_t *k_new, const uint16_t *v_new, hipStream_t stream)
+{
+    return write_impl(cache, batch, true, nullptr, nullptr, 1, k_new, v_new, stream);
+}
+
+pafp8_status kv_quant_fill(const pafp8_cache *cache, const pafp8_batch *batch,
+                           const int32_t *token_start, const int32_t *token_count,
+                           int32_t src_tokens, const uint16_t *k_src, const uint16_t *v_src,
+                           hipStream_t stream)
+{
+    return write_impl(cache, batch, false, token_start, token_count, src_tokens, k_src, v_src,
+                      stream);
+}
+
+size_t pafp8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t num_splits)
+{
+    if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 1)
+        return 0;
+    const size_t rows = static_cast<size_t>(batch) * num_q_heads * num_splits;
+    return rows * static_cast<size_t>(head_dim) * sizeof(float) + rows * sizeof(float);
+}
+
+int32_t pafp8_default_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_pages_per_req,
+                                 int32_t page_size, int32_t num_cus)
+{
+    if (batch <= 0 || num_kv_heads <= 0 || max_pages_per_req <= 0 || page_size <= 0)
+        return 1;
+    if (num_cus <= 0)
+        num_cus = device_cu_count();
+    // aim for about two work-groups per CU, without splits shorter than
+    // 1024 tokens (each wave then still gets a few tiles)
+    const int64_t units = static_cast<int64_t>(batch) * num_kv_heads;
+    const int64_t want = 2LL * num_cus;
+    int64_t S = (want + units - 1) / units;
+    const int64_t tokens = static_cast<int64_t>(max_pages_per_req) * page_size;
+    int64_t s_max = tokens / 1024;
+    if (s_max < 1)
+        s_max = 1;
+    if (S > s_max)
+        S = s_max;
+    if (S > max_pages_per_req)
+        S = max_pages_per_req;
+    return static_cast<int32_t>(S < 1 ? 1 : S);
+}
+
+pafp8_status paged_decode_attn_fp8(const pafp8_cache *cache, const pafp8_batch *batch,
+                                   const uint16_t *q, int32_t num_q_heads, float sm_scale,
+                                   int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                   float *out, float *lse, hipStream_t stream)
+{
+    return attn_impl(cache, batch, q, num_q_heads, sm_scale, num_splits, workspace,
+                     workspace_bytes, out, lse, stream, PAFP8_KV_FP8_E4M3);
+}
+
+pafp8_status paged_decode_attn_bf16(const pafp8_cache *cache, const pafp8_batch *batch,
+                                    const uint16_t *q, int32_t num_q_heads, float sm_scale,
+                                    int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                    float *out, float *lse, hipStream_t stream)
+{
+    return attn_impl(cache, batch, q, num_q_heads, sm_scale, num_splits, workspace,
+                     workspace_bytes, out, lse, stream, PAFP8_KV_BF16);
+}
+
+pafp8_status splitk_combine(const float *part_o, const float *part_lse, int32_t batch,
+                            int32_t num_q_heads, int32_t num_splits, int32_t head_dim,
+                            const int32_t *req_status, float *out, float *lse,
+                            hipStream_t stream)
+{
+    if (batch < 0 || num_q_heads < 1 || num_splits < 1)
+        return fail(PAFP8_EINVAL, "batch, num_q_heads or num_splits out of range");
+    if (head_dim < 4 || head_dim > 1024 || head_dim % 4 != 0)
+        return fail(PAFP8_EUNSUPPORTED, "head_dim = %d (need a multiple of 4 up to 1024)", head_dim);
+    if (batch == 0)
+        return ok();
+    if (part_o == nullptr || part_lse == nullptr || out == nullptr)
+        return fail(PAFP8_EINVAL, "part_o, part_lse or out is NULL");
+    if (!aligned16(part_o) || !aligned16(out))
+        return fail(PAFP8_EINVAL, "part_o and out must be 16-byte aligned");
+    return hip_status(pafp8::launch_splitk_combine(part_o, part_lse, batch, num_q_heads,
+                                                   num_splits, head_dim, req_status, out, lse,
+                                                   stream),
+                      "splitk_combine launch");
+}
+
+pafp8_status pafp8_e4m3_encode(const float *x, uint8_t *codes, int64_t n, hipStream_t stream)
+{
+    if (n < 0)
+        return fail(PAFP8_EINVAL, "n = %lld < 0", static_cast<long long>(n));
+    if (n == 0)
+        return ok();
+    if (x == nullptr || codes == nullptr)
+        return fail(PAFP8_EINVAL, "x or codes is NULL");
+    return hip_status(pafp8::launch_e4m3_encode(x, codes, n, stream), "pafp8_e4m3_encode launch");
+}
+
+pafp8_status pafp8_e4m3_decode(const uint8_t *codes, float *out_f32, float *out_via_f16,
+                               float *out_via_bf16, int64_t n, hipStream_t stream)
+{
+    if (n < 0)
+        return fail(PAFP8_EINVAL, "n = %lld < 0", static_cast<long long>(n));
+    if (n == 0)
+        return ok();
+    if (codes == nullptr)
+        return fail(PAFP8_EINVAL, "codes is NULL");
+    return hip_status(pafp8::launch_e4m3_decode(codes, out_f32, out_via_f16, out_via_bf16, n,
+                                                stream),
+                      "pafp8_e4m3_decode launch");
+}
+
+const char *pafp8_status_string(pafp8_status status)
+{
+    switch (status) {
+    case PAFP8_OK: return "PAFP8_OK";
+    case PAFP8_EINVAL: return "PAFP8_EINVAL";
+    case PAFP8_EUNSUPPORTED: return "PAFP8_EUNSUPPORTED";
+    case PAFP8_EHIP: return "PAFP8_EHIP";
+    default: return "PAFP8_UNKNOWN";
+    }
+}
+
+const char *pafp8_last_error(void) { return g_err; }
+
+int32_t pafp8_abi_version(size_t *sizeof_cache, size_t *sizeof_batch)
+{
+    if (sizeof_cache)
+        *sizeof_cache = sizeof(pafp8_cache);
+    if (sizeof_batch)
+        *sizeof_batch = sizeof(pafp8_batch);
+    return PAFP8_ABI_VERSION;
+}
+
+}  // extern "C"

@@ -1,0 +1,754 @@
+// decode_attn.hip -- decode-phase paged attention over an e4m3 (or bf16) KV
+// cache, converting on read, with split-K partitions and a log-sum-exp
+// combine.
+//
+// What is computed: Cloudflare, "Smaller, faster, safer: running Kimi and GLM
+// at scale", section "KV 缓存量化" (KV cache quantization) -- decode reads a
+// KV cache stored as FP8 e4m3 and the attention kernel converts the format as
+// it reads; a BF16-cache kernel is kept for direct comparison.  Pages follow
+// the per-sequence logical-to-physical mapping of paged attention (remio.ai
+// analysis of the post, section on shared KV cache safety).  A request
+// aborted by the separate page-tag check (section "共享 KV 缓存保护") is
+// neither read nor computed: its output is 0 with lse = -inf.
+//
+// gfx950 design (the kernels the pages measured were written for H200):
+//  * one work-group = 4 wave64s = one (request, KV head, split); the split's
+//    tokens are dealt to the waves in tiles of 64 tokens (32 for bf16 pools,
+//    so that a tile is 16 KB of K+V either way) and the four partial softmax
+//    states are merged through LDS at the end;
+//  * every lane issues 16-byte loads; a wave keeps the next tile's 16 KB in
+//    flight while it computes the current one (register double buffering);
+//    page ids arrive through scalar loads issued a tile ahead, so they never
+//    queue behind the vector loads;
+//  * G >= 2 (grouped query heads): Q.K^T and P.V run on 16x16x32 MFMAs and
+//    the whole query group shares one K/V tile held in registers.  Q.K^T takes
+//    the tile's tokens as rows and the group's heads as columns (K decoded
+//    exactly to bf16; Q is bf16 already); P.V takes head dims as rows (V
+//    decoded exactly to fp16, P rounded to fp16; bf16 pools split P into a
+//    bf16 high and low part).  Token order inside a tile is permuted so that
+//    the scores an MFMA leaves in a lane are exactly the P operand that lane
+//    feeds to the next MFMA, and the head a lane owns never changes: the
+//    online softmax needs two cross-lane max exchanges per tile and no other
+//    data movement;
+//  * G == 1: there is no contraction to speak of, so a vector path does the
+//    dot products with FMAs (lane = token for Q.K, lane = head dim for P.V).
+// Arithmetic: scores and outputs accumulate in fp32, softmax in the exp2
+// domain; the result is exact up to fp32 rounding.
+#include "pafp8_device.hpp"
+#include "pafp8_internal.hpp"
+
+namespace pafp8 {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Tokens [t0, t1) a work-group covers, and the request's verdict.
+struct SplitRange {
+    int64_t t0, t1;
+    int64_t p_last;  // index of the split's last page
+    int state;       // 0 = compute, 1 = aborted (0 / -inf), 2 = invalid (NaN)
+};
+
+__device__ __forceinline__ SplitRange split_range(const AttnParams &p, int b, int s)
+{
+    SplitRange r{0, 0, 0, 0};
+    if (p.req_status != nullptr && p.req_status[b] != 0) {
+        r.state = 1;
+        return r;
+    }
+    const int64_t L = p.context_lens[b];
+    const int64_t cap = static_cast<int64_t>(p.max_pages) << p.log2_page;
+    if (L < 0 || L > cap) {
+        r.state = 2;
+        return r;
+    }
+    const int64_t n_pages = (L + (int64_t{1} << p.log2_page) - 1) >> p.log2_page;
+    const int64_t p0 = static_cast<int64_t>(s) * p.pages_per_split;
+    int64_t p1 = p0 + p.pages_per_split;
+    if (p1 > n_pages)
+        p1 = n_pages;
+    if (p0 >= p1)
+        return r;  // nothing to attend in this split
+    r.t0 = p0 << p.log2_page;
+    r.t1 = p1 << p.log2_page;
+    if (r.t1 > L)
+        r.t1 = L;
+    r.p_last = p1 - 1;
+    return r;
+}
+
+// Physical pages of the four token groups of a tile (group q covers tokens
+// T0 + q*tpg .. + tpg, always inside one page).  The page ids are
+// wave-uniform and come in through scalar loads; they are fetched a tile ahead
+// and only checked (pages_ok) when the tile's loads are issued, so the fetch
+// never waits for its own result.
+struct TilePages {
+    int32_t pid[4];
+};
+
+__device__ __forceinline__ TilePages fetch_pages(const int32_t *__restrict__ row, int64_t T0,
+                                                 int tpg, int log2_page, int64_t p_last)
+{
+    TilePages t;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        int64_t idx = (T0 + q * tpg) >> log2_page;
+        if (idx > p_last)
+            idx = p_last;  // past the split (or no such tile): any page of the split is safe
+        t.pid[q] = row[idx];
+    }
+    return t;
+}
+
+// Replace page ids outside the pool by page 0 and record that it happened.
+__device__ __forceinline__ TilePages pages_ok(TilePages t, int num_pages, int &bad)
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const bool ok = t.pid[q] >= 0 && t.pid[q] < num_pages;
+        bad |= ok ? 0 : 1;
+        t.pid[q] = ok ? t.pid[q] : 0;
+    }
+    return t;
+}
+
+// pid[q] for a per-lane q in 0..3, as register arithmetic (a select chain
+// would be turned into a lookup table in scratch memory).
+__device__ __forceinline__ int32_t select4(int q, const TilePages &t)
+{
+    const int32_t m1 = -(q & 1), m2 = -((q >> 1) & 1);
+    const int32_t a = t.pid[0] ^ ((t.pid[0] ^ t.pid[1]) & m1);
+    const int32_t b = t.pid[2] ^ ((t.pid[2] ^ t.pid[3]) & m1);
+    return a ^ ((a ^ b) & m2);
+}
+
+// keep the first n bytes (n in [0, 16]) of a 16-byte register
+__device__ __forceinline__ u32x4 keep_bytes(u32x4 w, int n)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = n - 4 * i;  // bytes of dword i to keep
+        const uint32_t m = k >= 4 ? 0xFFFFFFFFu : (k <= 0 ? 0u : ((1u << (8 * k)) - 1u));
+        w[i] &= m;
+    }
+    return w;
+}
+
+// ===========================================================================
+// MFMA path (G >= 2)
+// ===========================================================================
+template <bool BF16, int D>
+struct Geo {
+    static constexpr int E = BF16 ? 2 : 1;          // bytes per element
+    static constexpr int TT = BF16 ? 32 : 64;       // tokens per wave tile
+    static constexpr int TPG = TT / 4;              // tokens per lane group (lane / 16)
+    static constexpr int NJ = TT / 16;              // Q.K^T MFMAs along tokens
+    static constexpr int NC = D / 32;               // Q.K^T MFMAs along the head dim
+    static constexpr int NDT = D / 16;              // P.V MFMAs along the head dim
+    static constexpr int NPC = TT / 32;             // P.V MFMAs along tokens
+    static constexpr int KL = (D / 4) * E / 16;     // 16-byte K loads per lane per token row
+    static_assert(TPG * E == 16, "a lane group's V run must be one 16-byte load");
+};
+
+template <bool BF16, int D>
+struct MfmaTile {
+    u32x4 k[Geo<BF16, D>::NJ][Geo<BF16, D>::KL];
+    u32x4 v[Geo<BF16, D>::NDT];
+};
+
+template <bool BF16, int D>
+struct MfmaCtx {
+    const uint8_t *k_head;  // k_pool + g * head block
+    const uint8_t *v_head;
+    int64_t page_bytes;     // bytes of one page of one pool (all heads)
+    int log2_page;
+    int lane_r, lane_g;     // lane % 16, lane / 16
+};
+
+template <bool BF16, int D>
+__device__ __forceinline__ void mfma_load(MfmaTile<BF16, D> &t, const MfmaCtx<BF16, D> &c,
+                                          int64_t T0, const TilePages &pg)
+{
+    using G_ = Geo<BF16, D>;
+    const int P = 1 << c.log2_page;
+    // K: this lane supplies token rows of group r/4, head dims [g*D/4, (g+1)*D/4)
+    const int kq = c.lane_r >> 2;
+    const int kslot = static_cast<int>((T0 + kq * G_::TPG) & (P - 1)) + (c.lane_r & 3);
+    const uint8_t *kp = c.k_head + static_cast<int64_t>(select4(kq, pg)) * c.page_bytes +
+                        static_cast<int64_t>(kslot) * (D * G_::E) + c.lane_g * (D / 4) * G_::E;
+#pragma unroll
+    for (int j = 0; j < G_::NJ; ++j)
+#pragma unroll
+        for (int l = 0; l < G_::KL; ++l)
+            t.k[j][l] = load16_stream(kp + j * 4 * (D * G_::E) + 16 * l);
+    // V: this lane supplies head dim dt*16 + r over the tokens of group g
+    const int vslot = static_cast<int>((T0 + c.lane_g * G_::TPG) & (P - 1));
+    const uint8_t *vp = c.v_head + static_cast<int64_t>(select4(c.lane_g, pg)) * c.page_bytes +
+                        (static_cast<int64_t>(c.lane_r) * P + vslot) * G_::E;
+#pragma unroll
+    for (int dt = 0; dt < G_::NDT; ++dt)
+        t.v[dt] = load16_stream(vp + static_cast<int64_t>(dt) * 16 * P * G_::E);
+}
+
+template <bool BF16, int D>
+struct MfmaState {
+    f32x4 o[Geo<BF16, D>::NDT];  // O^T: lane holds head r, dims dt*16 + 4g + 0..3
+    float m;                     // running max (log2 units) of head r
+    float l;                     // this lane's share of the softmax denominator
+};
+
+template <bool BF16, int D>
+__device__ __forceinline__ void mfma_compute(const MfmaTile<BF16, D> &t, MfmaState<BF16, D> &st,
+                                             const bf16x8 (&qop)[Geo<BF16, D>::NC], float cs,
+                                             int64_t T0, int64_t t1, int lane_g)
+{
+    using G_ = Geo<BF16, D>;
+    // ---- S^T = K Q^T: rows = tokens, columns = heads -------------------------
+    f32x4 sacc[G_::NJ];
+#pragma unroll
+    for (int j = 0; j < G_::NJ; ++j) {
+        sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < G_::NC; ++c) {
+            bf16x8 a;
+            if constexpr (BF16) {
+                a = __builtin_bit_cast(bf16x8, t.k[j][c]);
+            } else {
+                const u32x4 w = t.k[j][c >> 1];
+                a = e4m3x8_to_bf16x8(w[(c & 1) * 2], w[(c & 1) * 2 + 1]);
+            }
+            sacc[j] = mfma_bf16(a, qop[c], sacc[j]);
+        }
+    }
+    // lane holds the scores of tokens T0 + lane_g*TPG + n, n = 4j + v
+    float s[G_::TPG];
+#pragma unroll
+    for (int j = 0; j < G_::NJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            s[4 * j + v] = sacc[j][v];
+    const int64_t g0 = T0 + lane_g * G_::TPG;
+    const bool tail = T0 + G_::TT > t1;
+    int nvalid = G_::TPG;
+    if (tail) {
+        const int64_t nv = t1 - g0;
+        nvalid = nv < 0 ? 0 : (nv > G_::TPG ? G_::TPG : static_cast<int>(nv));
+#pragma unroll
+        for (int n = 0; n < G_::TPG; ++n)
+            s[n] = n < nvalid ? s[n] : kNegInf;
+    }
+    // ---- online softmax -----------------------------------------------------------
+    float mx = s[0];
+#pragma unroll
+    for (int n = 1; n < G_::TPG; ++n)
+        mx = __builtin_fmaxf(mx, s[n]);
+    mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32));
+    const float m_new = __builtin_fmaxf(st.m, mx * cs);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    float pr[G_::TPG];
+    float psum = 0.f;
+#pragma unroll
+    for (int n = 0; n < G_::TPG; ++n) {
+        pr[n] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n], cs, -m_new));
+        psum += pr[n];
+    }
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+#pragma unroll
+    for (int dt = 0; dt < G_::NDT; ++dt)
+        st.o[dt] *= alpha;
+    // ---- O^T += V^T P^T: rows = head dims, columns = heads ------------------------
+#pragma unroll
+    for (int c = 0; c < G_::NPC; ++c) {
+        if constexpr (BF16) {
+            u32x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = pr[c * 8 + 2 * e], b = pr[c * 8 + 2 * e + 1];
+                hi[e] = pack_bf16x2(a, b);
+                lo[e] = pack_bf16x2(a - bf16_lo(hi[e]), b - bf16_hi(hi[e]));
+            }
+            const bf16x8 phi = __builtin_bit_cast(bf16x8, hi);
+            const bf16x8 plo = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+            for (int dt = 0; dt < G_::NDT; ++dt) {
+                u32x4 w = t.v[dt];
+                if (tail)
+                    w = keep_bytes(w, nvalid * 2);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, w);
+                st.o[dt] = mfma_bf16(a, phi, st.o[dt]);
+                st.o[dt] = mfma_bf16(a, plo, st.o[dt]);
+            }
+        } else {
+            u32x4 pw;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                pw[e] = pack_f16x2(pr[c * 8 + 2 * e], pr[c * 8 + 2 * e + 1]);
+            const f16x8 pb = __builtin_bit_cast(f16x8, pw);
+#pragma unroll
+            for (int dt = 0; dt < G_::NDT; ++dt) {
+                u32x4 w = t.v[dt];
+                if (tail)
+                    w = keep_bytes(w, nvalid);
+                const f16x8 a = e4m3x8_to_f16x8(w[2 * c], w[2 * c + 1]);
+                st.o[dt] = mfma_f16(a, pb, st.o[dt]);
+            }
+        }
+    }
+}
+
+// Shared end of both paths: merge the waves' states and write the result.
+template <int D>
+struct MergeSmem {
+    float o[kWaves][16][D + 4];
+    float m[kWaves][16];
+    float l[kWaves][16];
+};
+
+template <int D>
+__device__ __forceinline__ void merge_and_write(const AttnParams &p, MergeSmem<D> &sm, int b,
+                                                int g, int s, int nheads, int state, int bad,
+                                                float v_scale)
+{
+    const int Hq = p.num_q_heads;
+    for (int idx = threadIdx.x; idx < nheads * (D / 4); idx += kThreads) {
+        const int h = idx / (D / 4);
+        const int d4 = (idx % (D / 4)) * 4;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        float lse = kNegInf;
+        if (state == 0) {
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+                M = __builtin_fmaxf(M, sm.m[w][h]);
+            if (M != kNegInf) {
+                float Ls = 0.f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    const float mw = sm.m[w][h];
+                    const float wt = mw == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+                    Ls += wt * sm.l[w][h];
+                    const f32x4 ow = *reinterpret_cast<const f32x4 *>(&sm.o[w][h][d4]);
+                    o += wt * ow;
+                }
+                o *= v_scale / Ls;
+                lse = (M + __log2f(Ls)) * kLn2;
+            }
+        }
+        if (state == 2 || bad) {
+            const float nan = __builtin_nanf("");
+            o = f32x4{nan, nan, nan, nan};
+            lse = nan;
+        }
+        const int64_t bh = static_cast<int64_t>(b) * Hq + static_cast<int64_t>(g) * nheads + h;
+        if (p.num_splits == 1) {
+            *reinterpret_cast<f32x4 *>(p.out + bh * D + d4) = o;
+            if (d4 == 0 && p.lse != nullptr)
+                p.lse[bh] = lse;
+        } else {
+            const int64_t row = bh * p.num_splits + s;
+            *reinterpret_cast<f32x4 *>(p.part_o + row * D + d4) = o;
+            if (d4 == 0)
+                p.part_lse[row] = lse;
+        }
+    }
+}
+
+// PIPE selects register double buffering (two tiles per wave, two waves per
+// SIMD) over single buffering (one tile per wave, three waves per SIMD).
+#ifndef PAFP8_MFMA_PIPELINE
+#define PAFP8_MFMA_PIPELINE 0
+#endif
+constexpr bool kPipe = PAFP8_MFMA_PIPELINE != 0;
+
+template <bool BF16, int D, bool PIPE>
+__global__ __launch_bounds__(kThreads, PIPE ? 2 : 3) void decode_attn_mfma_kernel(AttnParams p)
+{
+    using G_ = Geo<BF16, D>;
+    __shared__ MergeSmem<D> sm;
+
+    int idx = blockIdx.x;
+    const int s = idx % p.num_splits;
+    idx /= p.num_splits;
+    const int g = idx % p.num_kv_heads;
+    const int b = idx / p.num_kv_heads;
+    const int G = p.group;
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+
+    const SplitRange rng = split_range(p, b, s);
+    MfmaState<BF16, D> st;
+#pragma unroll
+    for (int dt = 0; dt < G_::NDT; ++dt)
+        st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m = kNegInf;
+    st.l = 0.f;
+    int bad = 0;
+
+    const int64_t ntok = rng.t1 - rng.t0;
+    const int ntiles = rng.state == 0 ? static_cast<int>((ntok + G_::TT - 1) / G_::TT) : 0;
+    if (wave < ntiles) {
+        MfmaCtx<BF16, D> c;
+        const int64_t head_bytes = (int64_t{1} << p.log2_page) * D * G_::E;
+        c.page_bytes = head_bytes * p.num_kv_heads;
+        c.k_head = p.k_pool + g * head_bytes;
+        c.v_head = p.v_pool + g * head_bytes;
+        c.log2_page = p.log2_page;
+        c.lane_r = lane & 15;
+        c.lane_g = lane >> 4;
+        // Q operand: head r of the group, head dims [g*D/4, (g+1)*D/4)
+        bf16x8 qop[G_::NC];
+        {
+            const int r = c.lane_r;
+            const uint16_t *qrow = p.q + (static_cast<int64_t>(b) * p.num_q_heads + g * G + r) * D +
+                                   c.lane_g * (D / 4);
+#pragma unroll
+            for (int cc = 0; cc < G_::NC; ++cc) {
+                const u32x4 w = r < G ? load16(qrow + 8 * cc) : u32x4{0u, 0u, 0u, 0u};
+                qop[cc] = __builtin_bit_cast(bf16x8, w);
+            }
+        }
+        const float cs = (BF16 ? 1.0f : p.k_scale[g]) * p.sm_scale * kLog2e;
+        const int32_t *row = p.page_table + static_cast<int64_t>(b) * p.max_pages;
+        const int stride = kWaves * G_::TT;
+
+        if constexpr (PIPE) {
+            // Register double buffering: while tile i is computed from one
+            // buffer, tile i + kWaves streams into the other and the page ids
+            // of tile i + 2*kWaves are fetched.  The last tile is peeled off so
+            // that the steady-state loads are unconditional and the compiler
+            // waits for exactly the loads a computation needs.
+            MfmaTile<BF16, D> ta, tb;
+            int i = wave;
+            int64_t T0 = rng.t0 + static_cast<int64_t>(i) * G_::TT;
+            TilePages pg = pages_ok(fetch_pages(row, T0, G_::TPG, p.log2_page, rng.p_last),
+                                    p.num_pages, bad);
+            mfma_load(ta, c, T0, pg);
+            pg = fetch_pages(row, T0 + stride, G_::TPG, p.log2_page, rng.p_last);
+            while (true) {
+                if (i + kWaves >= ntiles) {
+                    mfma_compute(ta, st, qop, cs, T0, rng.t1, c.lane_g);
+                    break;
+                }
+                mfma_load(tb, c, T0 + stride, pages_ok(pg, p.num_pages, bad));
+                pg = fetch_pages(row, T0 + 2 * stride, G_::TPG, p.log2_page, rng.p_last);
+                mfma_compute(ta, st, qop, cs, T0, rng.t1, c.lane_g);
+                i += kWaves;
+                T0 += stride;
+                if (i + kWaves >= ntiles) {
+                    mfma_compute(tb, st, qop, cs, T0, rng.t1, c.lane_g);
+                    break;
+                }
+                mfma_load(ta, c, T0 + stride, pages_ok(pg, p.num_pages, bad));
+                pg = fetch_pages(row, T0 + 2 * stride, G_::TPG, p.log2_page, rng.p_last);
+                mfma_compute(tb, st, qop, cs, T0, rng.t1, c.lane_g);
+                i += kWaves;
+                T0 += stride;
+            }
+        } else {
+            // One tile buffer per wave; latency is hidden by the other waves
+            // resident on the CU (three per SIMD).  Page ids still arrive a
+            // tile ahead.
+            int64_t T0 = rng.t0 + static_cast<int64_t>(wave) * G_::TT;
+            TilePages pg = fetch_pages(row, T0, G_::TPG, p.log2_page, rng.p_last);
+            for (int i = wave; i < ntiles; i += kWaves, T0 += stride) {
+                MfmaTile<BF16, D> t;
+                mfma_load(t, c, T0, pages_ok(pg, p.num_pages, bad));
+                pg = fetch_pages(row, T0 + stride, G_::TPG, p.log2_page, rng.p_last);
+                mfma_compute(t, st, qop, cs, T0, rng.t1, c.lane_g);
+            }
+        }
+    }
+    // the four lanes of a head each hold a quarter of its denominator
+    float l = st.l + shfl_xor_f(st.l, 16);
+    l += shfl_xor_f(l, 32);
+    {
+        const int r = lane & 15, lg = lane >> 4;
+        if (lg == 0) {
+            sm.m[wave][r] = st.m;
+            sm.l[wave][r] = l;
+        }
+#pragma unroll
+        for (int dt = 0; dt < G_::NDT; ++dt)
+            *reinterpret_cast<f32x4 *>(&sm.o[wave][r][dt * 16 + lg * 4]) = st.o[dt];
+    }
+    bad = __syncthreads_or(bad);
+    merge_and_write<D>(p, sm, b, g, s, G, rng.state, bad, BF16 ? 1.0f : p.v_scale[g]);
+}
+
+// ===========================================================================
+// vector path (G == 1)
+// ===========================================================================
+template <bool BF16, int D>
+struct VecGeo {
+    static constexpr int E = BF16 ? 2 : 1;
+    static constexpr int TT = 64;                 // tokens per wave tile, lane = token
+    static constexpr int KL = D * E / 16;         // 16-byte loads per K row
+    static constexpr int ROWS = D / 64;           // V rows (head dims) per lane
+    static constexpr int VL = 16 * E / 16;        // 16-byte loads per 16-token V run
+};
+
+// 16 bytes -> 16 (fp8) or 8 (bf16) floats, dot with q[base..] from LDS
+template <bool BF16>
+__device__ __forceinline__ float dot16(u32x4 w, const float *__restrict__ qs, float acc)
+{
+    if constexpr (BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = __builtin_fmaf(bf16_lo(w[e]), qs[2 * e], acc);
+            acc = __builtin_fmaf(bf16_hi(w[e]), qs[2 * e + 1], acc);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f32x2 a = e4m3x2_to_f32x2<false>(w[e]);
+            const f32x2 b = e4m3x2_to_f32x2<true>(w[e]);
+            acc = __builtin_fmaf(a[0], qs[4 * e], acc);
+            acc = __builtin_fmaf(a[1], qs[4 * e + 1], acc);
+            acc = __builtin_fmaf(b[0], qs[4 * e + 2], acc);
+            acc = __builtin_fmaf(b[1], qs[4 * e + 3], acc);
+        }
+    }
+    return acc;
+}
+
+template <int D>
+struct VecSmem {
+    MergeSmem<D> merge;
+    float q[D];
+    float p[kWaves][64];
+};
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads) void decode_attn_vec_kernel(AttnParams p)
+{
+    using V_ = VecGeo<BF16, D>;
+    __shared__ VecSmem<D> sm;
+
+    int idx = blockIdx.x;
+    const int s = idx % p.num_splits;
+    idx /= p.num_splits;
+    const int g = idx % p.num_kv_heads;
+    const int b = idx / p.num_kv_heads;
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+
+    const SplitRange rng = split_range(p, b, s);
+    for (int d = threadIdx.x; d < D; d += kThreads)
+        sm.q[d] = __uint_as_float(static_cast<uint32_t>(p.q[(static_cast<int64_t>(b) * p.num_q_heads + g) * D + d]) << 16);
+    __syncthreads();
+
+    float acc[V_::ROWS];
+#pragma unroll
+    for (int r = 0; r < V_::ROWS; ++r)
+        acc[r] = 0.f;
+    float m = kNegInf, l = 0.f;
+    int bad = 0;
+    const int64_t ntok = rng.t1 - rng.t0;
+    const int ntiles = rng.state == 0 ? static_cast<int>((ntok + V_::TT - 1) / V_::TT) : 0;
+    const float cs = (BF16 ? 1.0f : p.k_scale[g]) * p.sm_scale * kLog2e;
+    const int P = 1 << p.log2_page;
+    const int64_t head_bytes = static_cast<int64_t>(P) * D * V_::E;
+    const int64_t page_bytes = head_bytes * p.num_kv_heads;
+    const uint8_t *k_head = p.k_pool + g * head_bytes;
+    const uint8_t *v_head = p.v_pool + g * head_bytes;
+    const int32_t *row = p.page_table + static_cast<int64_t>(b) * p.max_pages;
+
+    for (int i = wave; i < ntiles; i += kWaves) {
+        const int64_t T0 = rng.t0 + static_cast<int64_t>(i) * V_::TT;
+        const TilePages pg = pages_ok(fetch_pages(row, T0, 16, p.log2_page, rng.p_last),
+                                      p.num_pages, bad);
+        // K row of token T0 + lane
+        const int q = lane >> 4;
+        const int kslot = static_cast<int>((T0 + q * 16) & (P - 1)) + (lane & 15);
+        const uint8_t *kp = k_head + static_cast<int64_t>(select4(q, pg)) * page_bytes +
+                            static_cast<int64_t>(kslot) * D * V_::E;
+        u32x4 kr[V_::KL];
+#pragma unroll
+        for (int e = 0; e < V_::KL; ++e)
+            kr[e] = load16_stream(kp + 16 * e);
+        // V: rows lane + 64*r, four 16-token runs
+        u32x4 vr[V_::ROWS][4][V_::VL];
+#pragma unroll
+        for (int r = 0; r < V_::ROWS; ++r)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int vslot = static_cast<int>((T0 + qq * 16) & (P - 1));
+                const uint8_t *vp = v_head + static_cast<int64_t>(pg.pid[qq]) * page_bytes +
+                                    (static_cast<int64_t>(lane + 64 * r) * P + vslot) * V_::E;
+#pragma unroll
+                for (int e = 0; e < V_::VL; ++e)
+                    vr[r][qq][e] = load16_stream(vp + 16 * e);
+            }
+        // score of token T0 + lane
+        float sc = 0.f;
+        constexpr int PER = BF16 ? 8 : 16;  // elements per 16-byte load
+#pragma unroll
+        for (int e = 0; e < V_::KL; ++e)
+            sc = dot16<BF16>(kr[e], &sm.q[e * PER], sc);
+        const bool valid = T0 + lane < rng.t1;
+        sc = valid ? sc : kNegInf;
+        const float mx = wave_max(sc);
+        const float m_new = __builtin_fmaxf(m, mx * cs);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc, cs, -m_new));
+        l = l * alpha + pv;
+        m = m_new;
+        sm.p[wave][lane] = pv;  // this wave's 64 weights, read back by every lane
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int r = 0; r < V_::ROWS; ++r) {
+            float a = acc[r] * alpha;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int64_t nv64 = rng.t1 - (T0 + qq * 16);
+                const int nv = nv64 <= 0 ? 0 : (nv64 >= 16 ? 16 : static_cast<int>(nv64));
+#pragma unroll
+                for (int e = 0; e < V_::VL; ++e) {
+                    u32x4 w = vr[r][qq][e];
+                    if (nv < 16)
+                        w = keep_bytes(w, BF16 ? (nv - 8 * e) * 2 : nv);
+                    const float *ps = &sm.p[wave][qq * 16 + e * PER];
+                    if constexpr (BF16) {
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            a = __builtin_fmaf(bf16_lo(w[x]), ps[2 * x], a);
+                            a = __builtin_fmaf(bf16_hi(w[x]), ps[2 * x + 1], a);
+                        }
+                    } else {
+                        a = dot16<false>(w, ps, a);
+                    }
+                }
+            }
+            acc[r] = a;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+        sm.merge.m[wave][0] = m;
+        sm.merge.l[wave][0] = l;
+    }
+#pragma unroll
+    for (int r = 0; r < V_::ROWS; ++r)
+        sm.merge.o[wave][0][lane + 64 * r] = acc[r];
+    bad = __syncthreads_or(bad);
+    merge_and_write<D>(p, sm.merge, b, g, s, 1, rng.state, bad, BF16 ? 1.0f : p.v_scale[g]);
+}
+
+// ===========================================================================
+// split-K combine: one wave per (request, query head)
+// ===========================================================================
+__global__ __launch_bounds__(kThreads) void splitk_combine_kernel(
+    const float *__restrict__ part_o, const float *__restrict__ part_lse, int bh_total, int Hq,
+    int S, int D, const int32_t *__restrict__ req_status, float *__restrict__ out,
+    float *__restrict__ lse_out)
+{
+    const int bh = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (bh >= bh_total)
+        return;
+    const int b = bh / Hq;
+    const float *pl = part_lse + static_cast<int64_t>(bh) * S;
+    const float *po = part_o + static_cast<int64_t>(bh) * S * D;
+    float *o = out + static_cast<int64_t>(bh) * D;
+    const bool aborted = req_status != nullptr && req_status[b] != 0;
+    float M = kNegInf;
+    int has_nan = 0;
+    if (!aborted) {
+        for (int k = lane; k < S; k += 64) {
+            const float v = pl[k];
+            has_nan |= v != v;
+            M = __builtin_fmaxf(M, v);
+        }
+        M = wave_max(M);
+        has_nan = __any(has_nan);
+    }
+    if (aborted || has_nan || M == kNegInf) {
+        const float fill = has_nan ? __builtin_nanf("") : 0.f;
+        for (int d = lane; d < D; d += 64)
+            o[d] = fill;
+        if (lane == 0 && lse_out != nullptr)
+            lse_out[bh] = has_nan ? fill : kNegInf;
+        return;
+    }
+    float sum = 0.f;
+    for (int k = lane; k < S; k += 64)
+        sum += __expf(pl[k] - M);
+    sum = wave_sum(sum);
+    const float LSE = M + __logf(sum);
+    // each lane owns head dims lane*4 + 256*i
+    constexpr int kMaxVec = 4;  // D <= 1024
+    f32x4 acc[kMaxVec];
+#pragma unroll
+    for (int i = 0; i < kMaxVec; ++i)
+        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < S; k0 += 64) {
+        const float lk = k0 + lane < S ? pl[k0 + lane] : kNegInf;
+        const float wk = lk == kNegInf ? 0.f : __expf(lk - LSE);
+        const int kn = S - k0 < 64 ? S - k0 : 64;
+        for (int k = 0; k < kn; ++k) {
+            const float w = __shfl(wk, k, 64);
+            const float lsk = __shfl(lk, k, 64);
+            if (lsk == kNegInf)
+                continue;  // empty split: contributes nothing
+            const float *src = po + static_cast<int64_t>(k0 + k) * D;
+#pragma unroll
+            for (int i = 0; i < kMaxVec; ++i) {
+                const int d = lane * 4 + 256 * i;
+                if (d < D)
+                    acc[i] += w * *reinterpret_cast<const f32x4 *>(src + d);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxVec; ++i) {
+        const int d = lane * 4 + 256 * i;
+        if (d < D)
+            *reinterpret_cast<f32x4 *>(o + d) = acc[i];
+    }
+    if (lane == 0 && lse_out != nullptr)
+        lse_out[bh] = LSE;
+}
+
+template <bool BF16, int D>
+hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
+{
+    const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_splits;
+    if (blocks > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    if (p.group == 1)
+        hipLaunchKernelGGL((decode_attn_vec_kernel<BF16, D>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, kPipe>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_attn(bool bf16_pool, int head_dim, const AttnParams &p,
+                              hipStream_t stream)
+{
+    if (bf16_pool)
+        return head_dim == 64 ? launch_attn_t<true, 64>(p, stream) : launch_attn_t<true, 128>(p, stream);
+    return head_dim == 64 ? launch_attn_t<false, 64>(p, stream) : launch_attn_t<false, 128>(p, stream);
+}
+
+hipError_t launch_splitk_combine(const float *part_o, const float *part_lse, int batch,
+                                 int num_q_heads, int num_splits, int head_dim,
+                                 const int32_t *req_status, float *out, float *lse,
+                                 hipStream_t stream)
+{
+    const int bh = batch * num_q_heads;
+    const int blocks = (bh + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(splitk_combine_kernel, dim3(blocks), dim3(kThreads), 0, stream, part_o,
+                       part_lse, bh, num_q_heads, num_splits, head_dim, req_status, out, lse);
+    return hipGetLastError();
+}
+
+}  // namespace pafp8

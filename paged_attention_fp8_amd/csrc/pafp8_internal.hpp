@@ -1,0 +1,82 @@
+// pafp8_internal.hpp -- launchers shared between the C-ABI layer and the
+// kernel translation units.  Host-side validation happens in api.hip before
+// any of these is called; they assume their arguments are consistent.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pafp8 {
+
+// Decode attention over one batch (both pool types).
+struct AttnParams {
+    const uint8_t *k_pool;
+    const uint8_t *v_pool;
+    const float *k_scale;  // nullptr for bf16 pools
+    const float *v_scale;
+    const int32_t *page_table;
+    const int32_t *context_lens;
+    const int32_t *req_status;  // nullable
+    const uint16_t *q;
+    float *out;        // final [B][Hq][D] (when S == 1)
+    float *lse;        // final [B][Hq] or nullptr (when S == 1)
+    float *part_o;     // [B][Hq][S][D] (when S > 1)
+    float *part_lse;   // [B][Hq][S]
+    int32_t num_pages;
+    int32_t log2_page;  // page_size = 1 << log2_page
+    int32_t num_kv_heads;
+    int32_t batch;
+    int32_t max_pages;
+    int32_t num_q_heads;
+    int32_t group;            // num_q_heads / num_kv_heads
+    int32_t num_splits;       // S
+    int32_t pages_per_split;  // ceil(max_pages / S)
+    float sm_scale;
+};
+
+hipError_t launch_decode_attn(bool bf16_pool, int head_dim, const AttnParams &p,
+                              hipStream_t stream);
+
+hipError_t launch_splitk_combine(const float *part_o, const float *part_lse, int batch,
+                                 int num_q_heads, int num_splits, int head_dim,
+                                 const int32_t *req_status, float *out, float *lse,
+                                 hipStream_t stream);
+
+hipError_t launch_tag_check(int batch, int max_pages, int page_size, const int32_t *page_table,
+                            const int32_t *context_lens, const uint32_t *expected_tags,
+                            const uint32_t *page_tags, int num_pages, int32_t *status,
+                            hipStream_t stream);
+
+// Quantise-on-write.  append mode (context_lens != nullptr): one token per
+// request at context_lens[b] - 1 from src [B][1][Hkv][D]; fill mode: tokens
+// token_start[b] + j, j < min(token_count[b], src_tokens), from
+// src [B][src_tokens][Hkv][D].
+struct WriteParams {
+    uint8_t *k_pool;
+    uint8_t *v_pool;
+    const float *k_scale;
+    const float *v_scale;
+    const int32_t *page_table;
+    const int32_t *req_status;    // nullable
+    const int32_t *context_lens;  // append mode
+    const int32_t *token_start;   // fill mode
+    const int32_t *token_count;   // fill mode
+    const uint16_t *k_src;
+    const uint16_t *v_src;
+    int32_t src_tokens;
+    int32_t num_pages;
+    int32_t log2_page;
+    int32_t num_kv_heads;
+    int32_t batch;
+    int32_t max_pages;
+};
+
+hipError_t launch_kv_write(bool bf16_pool, int head_dim, const WriteParams &p,
+                           hipStream_t stream);
+
+hipError_t launch_e4m3_encode(const float *x, uint8_t *codes, int64_t n, hipStream_t stream);
+hipError_t launch_e4m3_decode(const uint8_t *codes, float *f32, float *via_f16, float *via_bf16,
+                              int64_t n, hipStream_t stream);
+
+}  // namespace pafp8

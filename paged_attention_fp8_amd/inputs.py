@@ -314,3 +314,87 @@ def make_decode_inputs(w: Workload, seed: int, lengths: Optional[Sequence[int]] 
             stale.append(b)
     return DecodeInputs(w, seed, q, ks, vs, fp8_scale_from_amax(k_amax),
                         fp8_scale_from_amax(v_amax), pool, batch, stale)
+
+
+# ----------------------------------------------------------------------------
+# the same recipe drawn on the GPU (for full-size workloads)
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class DeviceDecodeInputs:
+    """A decode step drawn with torch's generator on the GPU.  Token data is
+    [B][Tmax][Hkv][D] bf16 (row L_b - 1 is this step's token; rows past L_b
+    are zero); scales are fp32 [Hkv] on the device and on the host."""
+    workload: Workload
+    seed: int
+    q: "object"            # torch bf16 [B][Hq][D]
+    k_tokens: "object"     # torch bf16 [B][Tmax][Hkv][D]
+    v_tokens: "object"
+    k_scale: np.ndarray
+    v_scale: np.ndarray
+    pool: PagePool
+    batch: PagedBatch
+    stale: List[int]
+
+    @property
+    def num_pages(self) -> int:
+        return self.pool.num_pages
+
+
+def _torch_gen(device, seed: int, *stream: int):
+    import torch
+    ss = np.random.SeedSequence([int(seed), *map(int, stream)])
+    g = torch.Generator(device=device)
+    g.manual_seed(int(ss.generate_state(1, dtype=np.uint64)[0] & 0x7FFFFFFFFFFFFFFF))
+    return g
+
+
+def _device_normal_bf16(g, shape, device, outlier_frac, outlier_mult):
+    """N(0,1) -> bf16 (nearest even), outliers after the bulk amax; returns
+    (bf16 tensor, per-head bulk amax over all but the head axis (axis -2))."""
+    import torch
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    bulk = x.to(torch.bfloat16)
+    amax = bulk.abs().float().amax(dim=tuple(i for i in range(len(shape)) if i != len(shape) - 2))
+    if outlier_frac > 0.0:
+        mask = torch.rand(shape, generator=g, device=device, dtype=torch.float32) < outlier_frac
+        bulk = torch.where(mask, x * outlier_mult, x).to(torch.bfloat16)
+    return bulk, amax
+
+
+def make_device_decode_inputs(w: Workload, seed: int, device="cuda",
+                              lengths: Optional[Sequence[int]] = None,
+                              pool_order: str = "shuffled") -> DeviceDecodeInputs:
+    """Draw a decode step for workload w directly on the GPU (seeded per request)."""
+    import torch
+    lens = np.asarray(lengths if lengths is not None else context_lengths(w, seed), dtype=np.int32)
+    B, Hq, Hkv, D, P = len(lens), w.q_heads, w.kv_heads, w.head_dim, w.page_size
+    need = sum(pages_needed(L, P) for L in lens)
+    num_pages = w.pool_pages if w.pool_pages is not None else int(math.ceil(need * w.pool_factor))
+    num_pages = max(num_pages, need)
+    pool = PagePool(num_pages, seed=seed, order=pool_order)
+    batch = allocate_batch(pool, lens, P)
+    T = int(lens.max()) if B else 1
+    q, _ = _device_normal_bf16(_torch_gen(device, seed, 2), (B, Hq, D), device, 0.0, 1.0)
+    k = torch.zeros((B, T, Hkv, D), dtype=torch.bfloat16, device=device)
+    v = torch.zeros_like(k)
+    k_amax = torch.zeros(Hkv, dtype=torch.float32, device=device)
+    v_amax = torch.zeros_like(k_amax)
+    for b in range(B):
+        L = int(lens[b])
+        g = _torch_gen(device, seed, 1, b)
+        kb, ka = _device_normal_bf16(g, (L, Hkv, D), device, w.outlier_frac, w.outlier_mult)
+        vb, va = _device_normal_bf16(g, (L, Hkv, D), device, w.outlier_frac, w.outlier_mult)
+        k[b, :L] = kb
+        v[b, :L] = vb
+        k_amax = torch.maximum(k_amax, ka)
+        v_amax = torch.maximum(v_amax, va)
+    stale = []
+    if w.stale_requests:
+        pick = rng(seed, 5).choice(B, size=min(w.stale_requests, B), replace=False)
+        for b in sorted(int(x) for x in pick):
+            i = int(rng(seed, 6, b).integers(0, pages_needed(lens[b], P)))
+            make_stale(pool, batch, b, i)
+            stale.append(b)
+    return DeviceDecodeInputs(w, seed, q, k, v, fp8_scale_from_amax(k_amax.cpu().numpy()),
+                              fp8_scale_from_amax(v_amax.cpu().numpy()), pool, batch, stale)

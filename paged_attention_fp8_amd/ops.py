@@ -1,0 +1,358 @@
+"""Python binding of libpafp8 (include/pafp8.h): argument marshalling only.
+
+Every function checks the torch tensors it is given (device, dtype, shape,
+contiguity), passes their device pointers and the current HIP stream to the
+C entry point of the same name, and raises if that call reports an error.
+All computation happens in the library's HIP kernels; there is no fallback.
+The library is loaded on first use and must have been built
+(``python -m paged_attention_fp8_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PAFP8_LIB", os.path.join(_PKG, "libpafp8.so"))
+
+KV_FP8_E4M3 = 0
+KV_BF16 = 1
+REQ_TAG_MISMATCH = 1
+REQ_PAGE_OOB = 2
+REQ_BAD_LEN = 4
+ABI_VERSION = 1
+
+
+class Pafp8Error(RuntimeError):
+    pass
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("kv_dtype", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+class _Batch(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_pages_per_req", ctypes.c_int32),
+                ("page_table", ctypes.c_void_p), ("context_lens", ctypes.c_void_p),
+                ("req_status", ctypes.c_void_p)]
+
+
+_V, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_CP, _BP = ctypes.POINTER(_Cache), ctypes.POINTER(_Batch)
+
+_SIGNATURES = {
+    "page_tag_check": (_I32, [_BP, _I32, _V, _I32, _V, _V, _V]),
+    "kv_quant_append": (_I32, [_CP, _BP, _V, _V, _V]),
+    "kv_quant_fill": (_I32, [_CP, _BP, _V, _V, _I32, _V, _V, _V]),
+    "pafp8_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "pafp8_default_num_splits": (_I32, [_I32, _I32, _I32, _I32, _I32]),
+    "paged_decode_attn_fp8": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V]),
+    "paged_decode_attn_bf16": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V]),
+    "splitk_combine": (_I32, [_V, _V, _I32, _I32, _I32, _I32, _V, _V, _V, _V]),
+    "pafp8_e4m3_encode": (_I32, [_V, _V, _I64, _V]),
+    "pafp8_e4m3_decode": (_I32, [_V, _V, _V, _V, _I64, _V]),
+    "pafp8_status_string": (ctypes.c_char_p, [_I32]),
+    "pafp8_last_error": (ctypes.c_char_p, []),
+    "pafp8_abi_version": (_I32, [ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpafp8.so (after torch, so that both use torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise Pafp8Error(f"{LIB_PATH} is not built; run `python -m paged_attention_fp8_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    sc, sb = _SZ(0), _SZ(0)
+    ver = L.pafp8_abi_version(ctypes.byref(sc), ctypes.byref(sb))
+    if ver != ABI_VERSION or sc.value != ctypes.sizeof(_Cache) or sb.value != ctypes.sizeof(_Batch):
+        raise Pafp8Error(f"libpafp8 ABI mismatch: version {ver}, struct sizes {sc.value}/{sb.value}")
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        L = lib()
+        raise Pafp8Error(f"{what}: {L.pafp8_status_string(status).decode()}: "
+                         f"{L.pafp8_last_error().decode()}")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+# ----------------------------------------------------------------------------
+# the two objects of the ABI
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PagedKVCache:
+    """The shared physical page pool: K [pages][Hkv][P][D], V [pages][Hkv][D][P]."""
+    k_pool: torch.Tensor           # uint8 (e4m3 codes) or bfloat16
+    v_pool: torch.Tensor
+    k_scale: Optional[torch.Tensor] = None   # float32 [Hkv], e4m3 only
+    v_scale: Optional[torch.Tensor] = None
+
+    @property
+    def kv_dtype(self) -> int:
+        return KV_BF16 if self.k_pool.dtype == torch.bfloat16 else KV_FP8_E4M3
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k_pool.shape[1])
+
+    @property
+    def page_size(self) -> int:
+        return int(self.k_pool.shape[2])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.k_pool.shape[3])
+
+    @property
+    def device(self) -> torch.device:
+        return self.k_pool.device
+
+    @staticmethod
+    def allocate(num_pages, num_kv_heads, page_size, head_dim, kv_dtype=KV_FP8_E4M3,
+                 device="cuda", k_scale=None, v_scale=None) -> "PagedKVCache":
+        dt = torch.uint8 if kv_dtype == KV_FP8_E4M3 else torch.bfloat16
+        k = torch.empty((num_pages, num_kv_heads, page_size, head_dim), dtype=dt, device=device)
+        v = torch.empty((num_pages, num_kv_heads, head_dim, page_size), dtype=dt, device=device)
+        return PagedKVCache(k, v, k_scale, v_scale)
+
+    def _struct(self) -> _Cache:
+        P, Hkv, D = self.page_size, self.num_kv_heads, self.head_dim
+        if self.kv_dtype == KV_FP8_E4M3:
+            _need(self.k_pool, "k_pool", torch.uint8)
+        else:
+            _need(self.k_pool, "k_pool", torch.bfloat16)
+        _need(self.v_pool, "v_pool", self.k_pool.dtype, (self.num_pages, Hkv, D, P), self.device)
+        scales = (None, None)
+        if self.kv_dtype == KV_FP8_E4M3:
+            if self.k_scale is None or self.v_scale is None:
+                raise ValueError("an e4m3 cache needs k_scale and v_scale")
+            _need(self.k_scale, "k_scale", torch.float32, (Hkv,), self.device)
+            _need(self.v_scale, "v_scale", torch.float32, (Hkv,), self.device)
+            scales = (self.k_scale.data_ptr(), self.v_scale.data_ptr())
+        return _Cache(self.kv_dtype, self.num_pages, P, Hkv, D, 0, self.k_pool.data_ptr(),
+                      self.v_pool.data_ptr(), scales[0], scales[1])
+
+
+@dataclasses.dataclass
+class DecodeBatch:
+    """One decode step's requests: page tables, lengths, and (optionally) the
+    per-request verdict of page_tag_check (None = no-op tracker)."""
+    page_table: torch.Tensor                 # int32 [B][max_pages]
+    context_lens: torch.Tensor               # int32 [B]
+    req_status: Optional[torch.Tensor] = None  # int32 [B]
+
+    @property
+    def batch(self) -> int:
+        return int(self.page_table.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.page_table.shape[1])
+
+    def with_status(self, req_status: Optional[torch.Tensor]) -> "DecodeBatch":
+        return DecodeBatch(self.page_table, self.context_lens, req_status)
+
+    def _struct(self, device) -> _Batch:
+        B = self.batch
+        _need(self.page_table, "page_table", torch.int32, device=device)
+        if self.page_table.dim() != 2:
+            raise ValueError("page_table must be [B][max_pages]")
+        _need(self.context_lens, "context_lens", torch.int32, (B,), device)
+        if self.req_status is not None:
+            _need(self.req_status, "req_status", torch.int32, (B,), device)
+        return _Batch(B, self.max_pages, self.page_table.data_ptr(),
+                      self.context_lens.data_ptr(), _ptr(self.req_status))
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+
+def page_tag_check(batch: DecodeBatch, page_size: int, page_tags: torch.Tensor,
+                   expected_tags: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-request status (0 = OK, else PAFP8_REQ_* flags)."""
+    dev = batch.page_table.device
+    bs = batch._struct(dev)
+    # tags are 32-bit patterns; int32 and uint32 tensors are both accepted
+    tag_dtype = page_tags.dtype if page_tags.dtype in (torch.int32, torch.uint32) else torch.int32
+    _need(page_tags, "page_tags", tag_dtype, device=dev)
+    _need(expected_tags, "expected_tags", tag_dtype, tuple(batch.page_table.shape), dev)
+    if out is None:
+        out = torch.empty(batch.batch, dtype=torch.int32, device=dev)
+    _need(out, "req_status_out", torch.int32, (batch.batch,), dev)
+    _check(lib().page_tag_check(ctypes.byref(bs), page_size, page_tags.data_ptr(),
+                                page_tags.numel(), expected_tags.data_ptr(), out.data_ptr(),
+                                _stream(dev)), "page_tag_check")
+    return out
+
+
+def _kv_src(t, name, shape, dev):
+    _need(t, name, torch.bfloat16, shape, dev)
+
+
+def kv_quant_append(cache: PagedKVCache, batch: DecodeBatch, k_new: torch.Tensor,
+                    v_new: torch.Tensor) -> None:
+    """Write this step's token (bf16 [B][Hkv][D]) of every request into its page."""
+    dev = cache.device
+    cs, bs = cache._struct(), batch._struct(dev)
+    shape = (batch.batch, cache.num_kv_heads, cache.head_dim)
+    _kv_src(k_new, "k_new", shape, dev)
+    _kv_src(v_new, "v_new", shape, dev)
+    _check(lib().kv_quant_append(ctypes.byref(cs), ctypes.byref(bs), k_new.data_ptr(),
+                                 v_new.data_ptr(), _stream(dev)), "kv_quant_append")
+
+
+def kv_quant_fill(cache: PagedKVCache, batch: DecodeBatch, token_start: torch.Tensor,
+                  token_count: torch.Tensor, k_src: torch.Tensor, v_src: torch.Tensor) -> None:
+    """Write source token j < token_count[b] of request b (bf16 [B][T][Hkv][D])
+    at position token_start[b] + j."""
+    dev = cache.device
+    cs, bs = cache._struct(), batch._struct(dev)
+    B = batch.batch
+    if k_src.dim() != 4:
+        raise ValueError("k_src must be [B][T][Hkv][D]")
+    T = int(k_src.shape[1])
+    shape = (B, T, cache.num_kv_heads, cache.head_dim)
+    _kv_src(k_src, "k_src", shape, dev)
+    _kv_src(v_src, "v_src", shape, dev)
+    _need(token_start, "token_start", torch.int32, (B,), dev)
+    _need(token_count, "token_count", torch.int32, (B,), dev)
+    _check(lib().kv_quant_fill(ctypes.byref(cs), ctypes.byref(bs), token_start.data_ptr(),
+                               token_count.data_ptr(), T, k_src.data_ptr(), v_src.data_ptr(),
+                               _stream(dev)), "kv_quant_fill")
+
+
+def workspace_bytes(batch: int, num_q_heads: int, head_dim: int, num_splits: int) -> int:
+    return int(lib().pafp8_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits))
+
+
+def default_num_splits(batch: int, num_kv_heads: int, max_pages: int, page_size: int,
+                       num_cus: int = 0) -> int:
+    return int(lib().pafp8_default_num_splits(batch, num_kv_heads, max_pages, page_size, num_cus))
+
+
+def paged_decode_attn(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor, sm_scale: float,
+                      num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      return_lse: bool = True):
+    """Decode attention over the paged cache; dispatches to
+    paged_decode_attn_fp8 or paged_decode_attn_bf16 by the pool's dtype.
+    Returns (out fp32 [B][Hq][D], lse fp32 [B][Hq] or None)."""
+    dev = cache.device
+    cs, bs = cache._struct(), batch._struct(dev)
+    if q.dim() != 3:
+        raise ValueError("q must be [B][Hq][D]")
+    B, Hq, D = (int(x) for x in q.shape)
+    _need(q, "q", torch.bfloat16, (batch.batch, Hq, cache.head_dim), dev)
+    if num_splits == 0:
+        num_splits = default_num_splits(B, cache.num_kv_heads, batch.max_pages, cache.page_size)
+    num_splits = min(num_splits, batch.max_pages)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, Hq, D), dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq), dev)
+    need = workspace_bytes(B, Hq, D, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", workspace.dtype, device=dev)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    fn = lib().paged_decode_attn_bf16 if cache.kv_dtype == KV_BF16 else lib().paged_decode_attn_fp8
+    _check(fn(ctypes.byref(cs), ctypes.byref(bs), q.data_ptr(), Hq, float(sm_scale), num_splits,
+              ws_ptr, ws_bytes, out.data_ptr(), _ptr(lse), _stream(dev)),
+           "paged_decode_attn")
+    return out, lse
+
+
+def splitk_combine(part_o: torch.Tensor, part_lse: torch.Tensor,
+                   req_status: Optional[torch.Tensor] = None, out=None, lse=None):
+    """Merge fp32 partials [B][Hq][S][D] / [B][Hq][S]; returns (out, lse)."""
+    dev = part_o.device
+    if part_o.dim() != 4:
+        raise ValueError("part_o must be [B][Hq][S][D]")
+    B, Hq, S, D = (int(x) for x in part_o.shape)
+    _need(part_o, "part_o", torch.float32, device=dev)
+    _need(part_lse, "part_lse", torch.float32, (B, Hq, S), dev)
+    if req_status is not None:
+        _need(req_status, "req_status", torch.int32, (B,), dev)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, Hq, D), dev)
+    _need(lse, "lse", torch.float32, (B, Hq), dev)
+    _check(lib().splitk_combine(part_o.data_ptr(), part_lse.data_ptr(), B, Hq, S, D,
+                                _ptr(req_status), out.data_ptr(), lse.data_ptr(), _stream(dev)),
+           "splitk_combine")
+    return out, lse
+
+
+def e4m3_encode(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device codec: fp32 -> e4m3 codes (uint8)."""
+    _need(x, "x", torch.float32)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _need(out, "codes", torch.uint8, tuple(x.shape), x.device)
+    _check(lib().pafp8_e4m3_encode(x.data_ptr(), out.data_ptr(), x.numel(), _stream(x.device)),
+           "pafp8_e4m3_encode")
+    return out
+
+
+def e4m3_decode(codes: torch.Tensor):
+    """Device codec: codes -> (fp32 direct, via fp16, via bf16), each widened to fp32."""
+    _need(codes, "codes", torch.uint8)
+    outs = [torch.empty(codes.shape, dtype=torch.float32, device=codes.device) for _ in range(3)]
+    _check(lib().pafp8_e4m3_decode(codes.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(),
+                                   outs[2].data_ptr(), codes.numel(), _stream(codes.device)),
+           "pafp8_e4m3_decode")
+    return tuple(outs)

@@ -1,0 +1,158 @@
+"""The C-ABI library loads, exports every function include/pafp8.h declares,
+and its host-side logic (sizing, split choice, argument validation) works
+without a GPU: validation runs before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (loads torch's HIP runtime first, as the binding does)
+
+from paged_attention_fp8_amd import build as B
+from paged_attention_fp8_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pafp8.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?(?:pafp8_status|size_t|int32_t|char)\s*\*?\s*(\w+)\s*\(",
+                      text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB):
+        B.build()
+    return ops.lib()
+
+
+def test_header_declares_the_path():
+    names = set(declared_functions())
+    for n in ["page_tag_check", "kv_quant_append", "kv_quant_fill", "paged_decode_attn_fp8",
+              "paged_decode_attn_bf16", "splitk_combine", "pafp8_decode_workspace_bytes",
+              "pafp8_default_num_splits", "pafp8_status_string", "pafp8_last_error",
+              "pafp8_abi_version", "pafp8_e4m3_encode", "pafp8_e4m3_decode"]:
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(L):
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    # and the binding wraps each of them
+    assert set(declared_functions()) <= set(ops._SIGNATURES)
+
+
+def test_single_hip_runtime_mapped(L):
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths
+
+
+def test_abi_version_and_struct_sizes(L):
+    sc, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.pafp8_abi_version(ctypes.byref(sc), ctypes.byref(sb)) == ops.ABI_VERSION
+    assert sc.value == ctypes.sizeof(ops._Cache) == 56
+    assert sb.value == ctypes.sizeof(ops._Batch) == 32
+
+
+def test_status_strings(L):
+    assert L.pafp8_status_string(0) == b"PAFP8_OK"
+    assert L.pafp8_status_string(1) == b"PAFP8_EINVAL"
+    assert L.pafp8_status_string(2) == b"PAFP8_EUNSUPPORTED"
+    assert L.pafp8_status_string(3) == b"PAFP8_EHIP"
+    assert L.pafp8_status_string(77) == b"PAFP8_UNKNOWN"
+
+
+def test_workspace_bytes(L):
+    assert L.pafp8_decode_workspace_bytes(64, 64, 128, 1) == 0
+    assert L.pafp8_decode_workspace_bytes(64, 64, 128, 2) == 64 * 64 * 2 * (128 + 1) * 4
+    assert L.pafp8_decode_workspace_bytes(0, 64, 128, 8) == 0
+
+
+def test_default_split_choice(L):
+    # 64 x 8 units on 256 CUs: already two per CU
+    assert L.pafp8_default_num_splits(64, 8, 256, 64, 256) == 1
+    # 4 long requests: split to fill the GPU
+    assert L.pafp8_default_num_splits(4, 8, 4096, 64, 256) == 16
+    # short contexts are not split below ~1024 tokens per split
+    assert L.pafp8_default_num_splits(1, 4, 16, 16, 256) == 1
+    assert L.pafp8_default_num_splits(8, 8, 256, 16, 256) == 4
+
+
+def _cache(**kw):
+    c = ops._Cache(0, 16, 64, 8, 128, 0, 256, 256 + 4096, 64, 128)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _batch(**kw):
+    b = ops._Batch(4, 16, 1024, 2048, None)
+    for k, v in kw.items():
+        setattr(b, k, v)
+    return b
+
+
+def _attn(L, cache, batch, hq=64, sm=0.1, splits=1, q=4096, out=8192, fn="paged_decode_attn_fp8"):
+    return getattr(L, fn)(ctypes.byref(cache) if cache is not None else None,
+                          ctypes.byref(batch) if batch is not None else None,
+                          q, hq, sm, splits, None, 0, out, None, None)
+
+
+@pytest.mark.parametrize("case,status,msg", [
+    (dict(cache=None), 1, "cache descriptor is NULL"),
+    (dict(batch=None), 1, "batch descriptor is NULL"),
+    (dict(cache_kw=dict(kv_dtype=1)), 1, "does not match"),
+    (dict(cache_kw=dict(page_size=48)), 2, "page_size"),
+    (dict(cache_kw=dict(head_dim=96)), 2, "head_dim"),
+    (dict(cache_kw=dict(k_scale=None)), 1, "k_scale"),
+    (dict(cache_kw=dict(k_pool=257)), 1, "aligned"),
+    (dict(batch_kw=dict(max_pages_per_req=0)), 1, "max_pages_per_req"),
+    (dict(batch_kw=dict(page_table=None)), 1, "page_table"),
+    (dict(hq=60), 1, "multiple of num_kv_heads"),
+    (dict(hq=8 * 17), 2, "group size"),
+    (dict(sm=0.0), 1, "sm_scale"),
+    (dict(sm=float("nan")), 1, "sm_scale"),
+    (dict(splits=-1), 1, "num_splits"),
+    (dict(splits=4), 1, "workspace"),
+    (dict(q=0), 1, "q or out is NULL"),
+])
+def test_attention_validation_without_gpu(L, case, status, msg):
+    cache = None if case.get("cache", 1) is None else _cache(**case.get("cache_kw", {}))
+    batch = None if case.get("batch", 1) is None else _batch(**case.get("batch_kw", {}))
+    st = _attn(L, cache, batch, hq=case.get("hq", 64), sm=case.get("sm", 0.1),
+               splits=case.get("splits", 1), q=case.get("q", 4096))
+    assert st == status
+    assert msg in L.pafp8_last_error().decode()
+
+
+def test_bf16_entry_rejects_fp8_pool(L):
+    assert _attn(L, _cache(), _batch(), fn="paged_decode_attn_bf16") == 1
+    assert b"does not match" in L.pafp8_last_error()
+
+
+def test_other_entry_points_validate_without_gpu(L):
+    c, b = _cache(), _batch()
+    assert L.kv_quant_append(ctypes.byref(c), ctypes.byref(b), None, 64, None) == 1
+    assert L.kv_quant_fill(ctypes.byref(c), ctypes.byref(b), None, 64, 8, 64, 64, None) == 1
+    assert L.kv_quant_fill(ctypes.byref(c), ctypes.byref(b), 64, 64, 0, 64, 64, None) == 1
+    assert L.page_tag_check(ctypes.byref(_batch(batch=-1)), 64, 64, 10, 64, 64, None) == 1
+    assert L.page_tag_check(ctypes.byref(b), 24, 64, 10, 64, 64, None) == 2
+    assert L.page_tag_check(ctypes.byref(b), 64, 64, 10, None, 64, None) == 1
+    assert L.splitk_combine(64, 64, 1, 8, 2, 6, None, 64, None, None) == 2
+    assert L.splitk_combine(None, 64, 1, 8, 2, 128, None, 64, None, None) == 1
+    assert L.pafp8_e4m3_encode(None, None, -1, None) == 1
+    # empty work is OK and launches nothing
+    assert L.pafp8_e4m3_encode(None, None, 0, None) == 0
+    assert _attn(L, _cache(), _batch(batch=0)) == 0
+    assert L.page_tag_check(ctypes.byref(_batch(batch=0)), 64, None, 0, None, None, None) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ops, "_lib", None)
+    with pytest.raises(ops.Pafp8Error, match="not built"):
+        ops.lib()
