@@ -1,0 +1,317 @@
+"""Benchmark of the decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-extras] [--sweep] [--copy-calibration]
+                    [--traffic-from DIR]
+
+One step = one pass of the path over one batch: the batched page-tag check,
+the quantise-on-append of this step's token for every request, and e4m3 paged
+decode attention (with its split-K combine when the library splits).  The
+workload is the concurrency point the target is quoted on: 64 requests of
+16,384 tokens, 64 query heads on 8 KV heads, head_dim 128, 64-token pages, in
+a 2 GiB pool that holds exactly 64 e4m3 requests (or 32 bf16 ones).  Inputs
+are seeded synthetic data drawn on the GPU and resident in HBM before timing.
+
+Prints one JSON line.  value = attention tokens/s (one decode token per
+request through one attention layer per step).  roofline.achieved is the
+algorithmic bytes of one attention launch divided by its mean duration,
+measured with HIP events on the launch stream over the timed steps.  The
+bf16 twin (32 requests: the same KV bytes) and the tag-check overhead against
+the no-op tracker are reported beside it; cpu_baseline times the CPU oracle
+on a bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+SEED = 1003
+METRIC = "decode attention tokens/s and achieved HBM GB/s (% of peak), FP8 vs BF16 KV"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--batch", type=int, default=64, help="requests (e4m3 headline point)")
+    ap.add_argument("--splits", type=int, default=0, help="split-K count (0: library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the oracle sample")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the bf16 twin and the check-overhead measurement")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also run the 1/8/16/32/64 concurrency sweep (both dtypes)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--traffic-from", default=None,
+                    help="directory with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE results")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources: counter figures taken on other sources are stale."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "paged_attention_fp8_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(lens, Hq, Hkv, D, P, kv_elem_bytes, checked=True):
+    """Bytes one attention launch must move: K+V of every attended token,
+    the page-table entries, Q, out + lse, scales, lengths, status."""
+    kv = sum(int(L) for L in lens) * Hkv * D * 2 * kv_elem_bytes
+    table = sum((int(L) + P - 1) // P for L in lens) * 4
+    B = len(lens)
+    return (kv + table + B * Hq * D * 2 + B * Hq * (D + 1) * 4 + 2 * Hkv * 4 + B * 4
+            + (B * 4 if checked else 0))
+
+
+class Point:
+    """One decode step's device state for a batch size and pool type."""
+
+    def __init__(self, batch, kv_dtype, device, seed=SEED):
+        from paged_attention_fp8_amd import harness as H
+        from paged_attention_fp8_amd import inputs as I
+        from paged_attention_fp8_amd import ops
+        self.ops, self.H = ops, H
+        self.kv_dtype = kv_dtype
+        elem = 1 if kv_dtype == ops.KV_FP8_E4M3 else 2
+        self.w = I.sweep_workload(batch, elem)
+        log(f"drawing {self.w.name} ({'e4m3' if kv_dtype == ops.KV_FP8_E4M3 else 'bf16'})")
+        self.inp = I.make_device_decode_inputs(self.w, seed, device)
+        self.step = H.build_step(self.inp, kv_dtype, device, poison=False)
+        log(f"cache built: {self.step.cache.num_pages} pages")
+        self.sm = 1.0 / math.sqrt(self.w.head_dim)
+        B, Hq, D = batch, self.w.q_heads, self.w.head_dim
+        self.lens = self.inp.batch.context_lens
+        self.bytes = algorithmic_bytes(self.lens, Hq, self.w.kv_heads, D, self.w.page_size, elem)
+
+    def run(self, steps, warmup, splits, check=True, events=True):
+        import torch
+        ops, H, st = self.ops, self.H, self.step
+        B, Hq, D = st.batch.batch, self.w.q_heads, self.w.head_dim
+        dev = st.q.device
+        S = splits or ops.default_num_splits(B, self.w.kv_heads, st.batch.max_pages,
+                                             self.w.page_size)
+        S = min(S, st.batch.max_pages)
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        status = torch.empty((B,), dtype=torch.int32, device=dev)
+        nws = ops.workspace_bytes(B, Hq, D, S)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+
+        def one(i=None):
+            stat = None
+            if check:
+                stat = ops.page_tag_check(st.batch, self.w.page_size, st.page_tags,
+                                          st.expected_tags, out=status)
+            b = st.batch.with_status(stat)
+            ops.kv_quant_append(st.cache, b, st.k_new, st.v_new)
+            if i is not None and events:
+                ev[i][0].record()
+            ops.paged_decode_attn(st.cache, b, st.q, self.sm, S, ws, out, lse)
+            if i is not None and events:
+                ev[i][1].record()
+
+        for _ in range(warmup):
+            one()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            one(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        attn_ms = [a.elapsed_time(b) for a, b in ev] if events else []
+        return {"splits": S, "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
+                "attn_ms": attn_ms, "out": out, "lse": lse, "status": status}
+
+
+def cpu_baseline(point, target_s):
+    """Time the CPU oracle on the first n requests of the same batch (n grows
+    until one call takes about target_s seconds)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    inp, w = point.inp, point.w
+    Hkv, D, P = w.kv_heads, w.head_dim, w.page_size
+    pool = oracle.Pool(oracle.KV_FP8, inp.num_pages, Hkv, P, D)
+    table = inp.batch.page_table
+    lens = inp.batch.context_lens
+    q = inp.q.view(torch.int16).cpu().numpy().view(np.uint16)
+    done = 0
+
+    def ensure(n):
+        nonlocal done
+        for b in range(done, n):
+            L = int(lens[b])
+            k = inp.k_tokens[b, :L].view(torch.int16).cpu().numpy().view(np.uint16)
+            v = inp.v_tokens[b, :L].view(torch.int16).cpu().numpy().view(np.uint16)
+            oracle.kv_write(pool, table[b:b + 1], np.zeros(1, np.int32),
+                            np.array([L], np.int32), k[None], v[None], inp.k_scale, inp.v_scale)
+        done = max(done, n)
+
+    def timed(n):
+        ensure(n)
+        log(f"cpu baseline: oracle on {n} request(s)")
+        t0 = time.perf_counter()
+        oracle.paged_attention(pool, q[:n], table[:n], lens[:n], point.sm, inp.k_scale,
+                               inp.v_scale)
+        return time.perf_counter() - t0
+
+    n = 1
+    t = timed(n)
+    while t < 0.5 * target_s and n < len(lens):
+        n = min(len(lens), max(n + 1, int(n * target_s / max(t, 1e-3))))
+        t = timed(n)
+    return {"value": n / t, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {n} of {len(lens)} requests of the same batch (all 64 heads, "
+                      f"16384 tokens each), fp64 oracle, one call, {t:.1f} s"}
+
+
+def read_traffic(directory, kernel_substr, launches_bytes):
+    """Per-dispatch FETCH_SIZE + WRITE_SIZE (KiB) of the attention kernel from
+    rocprofv3 --pmc outputs, scaled by the copy-kernel calibration factors."""
+    if directory is None:
+        return None
+    path = os.path.join(directory, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None  # counters were taken on other kernel sources
+    return t.get("bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the path shards by request or KV head with no exchange (see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    from paged_attention_fp8_amd import ops
+    dev = torch.device("cuda:0")
+
+    p = Point(args.batch, ops.KV_FP8_E4M3, dev)
+    r = p.run(args.steps, args.warmup, args.splits)
+    log(f"e4m3 B={args.batch}: {r['ms_per_step']:.3f} ms/step")
+    if not torch.all(r["status"] == 0):
+        raise SystemExit("tag check flagged requests in a clean batch")
+    if not torch.isfinite(r["out"]).all():
+        raise SystemExit("non-finite attention output")
+    attn_ms = statistics.mean(r["attn_ms"])
+    achieved = p.bytes / (attn_ms * 1e-3) / 1e9
+    B = args.batch
+    result = {
+        "metric": METRIC,
+        "value": B / (r["ms_per_step"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": f"gqa8_16k_b{B}: {B} requests x 16384 tokens, 64 query / 8 KV heads, "
+                        "head_dim 128, 64-token pages, 2 GiB e4m3 pool, tag check + append + attention",
+            "batch": B, "context": 16384, "q_heads": 64, "kv_heads": 8, "head_dim": 128,
+            "page_size": 64, "num_splits": r["splits"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": read_traffic(args.traffic_from, "decode_attn", p.bytes),
+            "kernel": "decode_attn_mfma_kernel<e4m3, 128>",
+            "algorithmic_bytes_per_launch": p.bytes,
+            "launch_ms_mean": attn_ms,
+            "launch_ms_p10_p90": [sorted(r["attn_ms"])[len(r["attn_ms"]) // 10],
+                                  sorted(r["attn_ms"])[(9 * len(r["attn_ms"])) // 10]],
+        },
+        "context_tokens_per_s": float(sum(int(L) for L in p.lens)) / (attn_ms * 1e-3),
+    }
+    if not args.no_extras:
+        r0 = p.run(args.steps, args.warmup, args.splits, check=False)
+        result["check_overhead_pct"] = 100.0 * (r["ms_per_step"] - r0["ms_per_step"]) / r0["ms_per_step"]
+        result["no_tracker_ms_per_step"] = r0["ms_per_step"]
+        del r0
+        q = Point(32, ops.KV_BF16, dev)
+        rb = q.run(args.steps, args.warmup, args.splits)
+        bms = statistics.mean(rb["attn_ms"])
+        result["bf16_twin"] = {
+            "workload": "gqa8_16k_b32: 32 requests x 16384 tokens in the same 2 GiB as bf16 "
+                        "(64 do not fit)",
+            "tokens_per_s": 32 / (rb["ms_per_step"] * 1e-3),
+            "ms_per_step": rb["ms_per_step"],
+            "attn_GBps": q.bytes / (bms * 1e-3) / 1e9,
+            "attn_frac": q.bytes / (bms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "num_splits": rb["splits"],
+        }
+        del q
+        torch.cuda.empty_cache()
+    if args.sweep:
+        sweep = []
+        for kv_dtype, name in ((ops.KV_FP8_E4M3, "fp8"), (ops.KV_BF16, "bf16")):
+            for b in (1, 8, 16, 32, 64):
+                if kv_dtype == ops.KV_BF16 and b > 32:
+                    sweep.append({"dtype": name, "batch": b, "result": "out of pool memory"})
+                    continue
+                pt = Point(b, kv_dtype, dev)
+                rr = pt.run(args.steps, args.warmup, 0)
+                ms = statistics.mean(rr["attn_ms"])
+                sweep.append({"dtype": name, "batch": b, "tokens_per_s": b / (rr["ms_per_step"] * 1e-3),
+                              "attn_GBps": pt.bytes / (ms * 1e-3) / 1e9, "splits": rr["splits"]})
+                del pt
+                torch.cuda.empty_cache()
+        result["sweep"] = sweep
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

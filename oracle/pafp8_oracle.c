@@ -229,22 +229,24 @@ void oracle_kv_write(int kv_dtype, int B, int maxP, int P, int Hkv, int D, int n
                      const float *k_scale, const float *v_scale,
                      void *k_pool, void *v_pool)
 {
-    int b;
-    for (b = 0; b < B; ++b) {
-        int j;
-        if (status && status[b] != 0)
-            continue;
-        for (j = 0; j < count[b]; ++j) {
-            int64_t t = (int64_t)start[b] + j;
-            int64_t pi = t / P;
-            int slot = (int)(t % P), g, d;
-            int32_t page;
-            if (t < 0 || pi >= maxP)
+    int b, g;
+    /* heads write disjoint bytes: one thread per head */
+#pragma omp parallel for schedule(static) private(b)
+    for (g = 0; g < Hkv; ++g) {
+        for (b = 0; b < B; ++b) {
+            int j;
+            if (status && status[b] != 0)
                 continue;
-            page = page_table[(int64_t)b * maxP + pi];
-            if (page < 0 || page >= num_pages)
-                continue;
-            for (g = 0; g < Hkv; ++g) {
+            for (j = 0; j < count[b]; ++j) {
+                int64_t t = (int64_t)start[b] + j;
+                int64_t pi = t / P;
+                int slot = (int)(t % P), d;
+                int32_t page;
+                if (t < 0 || pi >= maxP)
+                    continue;
+                page = page_table[(int64_t)b * maxP + pi];
+                if (page < 0 || page >= num_pages)
+                    continue;
                 for (d = 0; d < D; ++d) {
                     int64_t src = (((int64_t)b * T_src + j) * Hkv + g) * D + d;
                     int64_t ko = k_offset(page, g, slot, d, Hkv, P, D);
