@@ -37,6 +37,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+COUNTERS_SUMMARY = os.path.join(ROOT, "profiles", "decode_attn_e4m3_gqa8_16k_b64_counters.md")
+ATTN_KERNEL = "decode_attn_mfma_kernel<false, 128"
+COPY_BYTES = 1 << 30
 SEED = 1003
 METRIC = "decode attention tokens/s and achieved HBM GB/s (% of peak), FP8 vs BF16 KV"
 
@@ -61,8 +64,11 @@ def parse_args():
                     help="also run the 1/8/16/32/64 concurrency sweep (both dtypes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--traffic-from", default=None,
-                    help="directory with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE results")
+    ap.add_argument("--traffic-from", default=COUNTERS_SUMMARY,
+                    help="counter summary written by --summarize-counters")
+    ap.add_argument("--summarize-counters", nargs=4, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn four rocprofv3 --pmc runs into the counter summary and exit")
     return ap.parse_args()
 
 
@@ -190,24 +196,88 @@ def cpu_baseline(point, target_s):
                       f"16384 tokens each), fp64 oracle, one call, {t:.1f} s"}
 
 
-def read_traffic(directory, kernel_substr, launches_bytes):
-    """Per-dispatch FETCH_SIZE + WRITE_SIZE (KiB) of the attention kernel from
-    rocprofv3 --pmc outputs, scaled by the copy-kernel calibration factors."""
-    if directory is None:
+def _pmc_values(directory, counter, kernel_substr):
+    """Per-dispatch values of one counter for kernels whose name contains
+    kernel_substr, from a rocprofv3 --pmc csv run directory."""
+    import csv
+    vals = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == counter and kernel_substr in row.get("Kernel_Name", ""):
+                    vals.append(float(row["Counter_Value"]))
+    return vals
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel,
+    scaled by what the same counters read for a plain 1 GiB device copy."""
+    f = _pmc_values(fetch_dir, "FETCH_SIZE", ATTN_KERNEL)
+    w = _pmc_values(write_dir, "WRITE_SIZE", ATTN_KERNEL)
+    cf = _pmc_values(copy_fetch_dir, "FETCH_SIZE", "copy")
+    cw = _pmc_values(copy_write_dir, "WRITE_SIZE", "copy")
+    if not (f and w and cf and cw):
+        raise SystemExit(f"missing counter rows: fetch {len(f)} write {len(w)} copy {len(cf)}/{len(cw)}")
+    # the copy moves COPY_BYTES each way; its largest dispatches are the copies
+    cf_kib, cw_kib = max(cf), max(cw)
+    kf = COPY_BYTES / (cf_kib * 1024.0)
+    kw = COPY_BYTES / (cw_kib * 1024.0)
+    fetch = statistics.median(f) * 1024.0 * kf
+    write = statistics.median(w) * 1024.0 * kw
+    lines = [
+        "# HBM traffic counters: e4m3 paged decode attention, 64 requests x 16384 tokens",
+        "",
+        "Commands (MI355X, repository root; one counter per run):",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- \\",
+        "        python bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extras",
+        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- \\",
+        "        python bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extras",
+        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copy_fetch -o run -- \\",
+        "        python bench.py --copy-calibration",
+        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_write -o run -- \\",
+        "        python bench.py --copy-calibration",
+        "    python bench.py --summarize-counters gpurun_out/pmc_fetch gpurun_out/pmc_write \\",
+        "        gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write",
+        "",
+        f"attention dispatches: {len(f)} (FETCH_SIZE), {len(w)} (WRITE_SIZE)",
+        f"attention FETCH_SIZE median: {statistics.median(f):.1f} KiB per dispatch",
+        f"attention WRITE_SIZE median: {statistics.median(w):.1f} KiB per dispatch",
+        f"copy calibration: 1 GiB copy reads FETCH_SIZE {cf_kib:.1f} KiB, WRITE_SIZE {cw_kib:.1f} KiB",
+        f"scale factors (known bytes / counter bytes): fetch {kf:.4f}, write {kw:.4f}",
+        f"traffic_bytes_per_launch: {fetch + write:.0f}",
+        f"fetch_bytes_per_launch: {fetch:.0f}",
+        f"write_bytes_per_launch: {write:.0f}",
+        f"source_hash: {source_hash()}",
+        "",
+    ]
+    with open(COUNTERS_SUMMARY, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def read_traffic(summary_path):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when there is none or it was taken on other kernel sources."""
+    if not summary_path or not os.path.exists(summary_path):
         return None
-    path = os.path.join(directory, "traffic.json")
-    if not os.path.exists(path):
+    vals = {}
+    with open(summary_path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash():
         return None
-    with open(path) as f:
-        t = json.load(f)
-    if t.get("source_hash") != source_hash():
-        return None  # counters were taken on other kernel sources
-    return t.get("bytes_per_launch")
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def copy_calibration():
     import torch
-    n = 1 << 30
+    n = COPY_BYTES
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(5):
@@ -223,6 +293,9 @@ def main():
               "the path shards by request or KV head with no exchange (see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     import torch
     if args.copy_calibration:
         copy_calibration()
@@ -265,7 +338,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": read_traffic(args.traffic_from, "decode_attn", p.bytes),
+            "traffic": read_traffic(args.traffic_from),
             "kernel": "decode_attn_mfma_kernel<e4m3, 128>",
             "algorithmic_bytes_per_launch": p.bytes,
             "launch_ms_mean": attn_ms,

@@ -286,8 +286,9 @@ def make_decode_inputs(w: Workload, seed: int, lengths: Optional[Sequence[int]] 
     lens = np.asarray(lengths if lengths is not None else context_lengths(w, seed), dtype=np.int32)
     B, Hq, Hkv, D, P = len(lens), w.q_heads, w.kv_heads, w.head_dim, w.page_size
     need = sum(pages_needed(L, P) for L in lens)
-    num_pages = w.pool_pages if w.pool_pages is not None else int(math.ceil(need * w.pool_factor))
-    num_pages = max(num_pages, need)
+    # a fixed budget (pool_pages) is never enlarged: requests that do not fit
+    # raise PoolExhausted, the capacity ceiling of that budget
+    num_pages = w.pool_pages if w.pool_pages is not None else max(need, int(math.ceil(need * w.pool_factor)))
     pool = PagePool(num_pages, seed=seed, order=pool_order)
     batch = allocate_batch(pool, lens, P)
     q, _ = normal_bf16(rng(seed, 2), (B, Hq, D))
@@ -370,8 +371,9 @@ def make_device_decode_inputs(w: Workload, seed: int, device="cuda",
     lens = np.asarray(lengths if lengths is not None else context_lengths(w, seed), dtype=np.int32)
     B, Hq, Hkv, D, P = len(lens), w.q_heads, w.kv_heads, w.head_dim, w.page_size
     need = sum(pages_needed(L, P) for L in lens)
-    num_pages = w.pool_pages if w.pool_pages is not None else int(math.ceil(need * w.pool_factor))
-    num_pages = max(num_pages, need)
+    # a fixed budget (pool_pages) is never enlarged: requests that do not fit
+    # raise PoolExhausted, the capacity ceiling of that budget
+    num_pages = w.pool_pages if w.pool_pages is not None else max(need, int(math.ceil(need * w.pool_factor)))
     pool = PagePool(num_pages, seed=seed, order=pool_order)
     batch = allocate_batch(pool, lens, P)
     T = int(lens.max()) if B else 1

@@ -71,3 +71,10 @@ def test_workload_pool_sizes():
     assert w.pool_pages == 16384
     assert I.sweep_workload(32, 2).pool_pages == 8192
     assert I.WORKLOADS["gqa8_256k_b4"].group == 8
+
+
+def test_fixed_pool_budget_is_never_enlarged():
+    with pytest.raises(I.PoolExhausted):
+        I.make_decode_inputs(I.Workload("w", 3, 2, 2, 64, 16, 64, 64, pool_pages=11), 0)
+    inp = I.make_decode_inputs(I.Workload("w", 3, 2, 2, 64, 16, 64, 64, pool_pages=12), 0)
+    assert inp.num_pages == 12 and inp.pool.free_pages == 0
