@@ -16,10 +16,11 @@
 //    tokens are dealt to the waves in tiles of 64 tokens (32 for bf16 pools,
 //    so that a tile is 16 KB of K+V either way) and the four partial softmax
 //    states are merged through LDS at the end;
-//  * every lane issues 16-byte loads; a wave keeps the next tile's 16 KB in
-//    flight while it computes the current one (register double buffering);
-//    page ids arrive through scalar loads issued a tile ahead, so they never
-//    queue behind the vector loads;
+//  * every lane issues 16-byte loads; a wave keeps about one tile (16 KB) in
+//    flight at all times with a single register buffer: the next tile's K
+//    loads go out as soon as Q.K^T has consumed this tile's K, its V loads as
+//    soon as P.V has consumed this tile's V; page ids arrive through scalar
+//    loads a tile ahead, so they never queue behind the vector loads;
 //  * G >= 2 (grouped query heads): Q.K^T and P.V run on 16x16x32 MFMAs and
 //    the whole query group shares one K/V tile held in registers.  Q.K^T takes
 //    the tile's tokens as rows and the group's heads as columns (K decoded
@@ -167,13 +168,27 @@ struct MfmaCtx {
     int lane_r, lane_g;     // lane % 16, lane / 16
 };
 
+// 16-byte KV loads.  e4m3 tiles stream past the caches (each 128-byte line
+// is consumed by one wave's back-to-back loads); bf16 loads stay cacheable:
+// a bf16 tile covers only half of each V line, the other half belonging to
+// the next tile (another wave), and on MI355X streaming bf16 loads (K or V)
+// cost 15-25% of the bandwidth.
+template <bool STREAM>
+__device__ __forceinline__ u32x4 load16_kv(const void *p)
+{
+    if constexpr (STREAM)
+        return load16_stream(p);
+    else
+        return load16(p);
+}
+
 template <bool BF16, int D>
-__device__ __forceinline__ void mfma_load(MfmaTile<BF16, D> &t, const MfmaCtx<BF16, D> &c,
-                                          int64_t T0, const TilePages &pg)
+__device__ __forceinline__ void mfma_load_k(MfmaTile<BF16, D> &t, const MfmaCtx<BF16, D> &c,
+                                            int64_t T0, const TilePages &pg)
 {
     using G_ = Geo<BF16, D>;
     const int P = 1 << c.log2_page;
-    // K: this lane supplies token rows of group r/4, head dims [g*D/4, (g+1)*D/4)
+    // this lane supplies token rows of group r/4, head dims [g*D/4, (g+1)*D/4)
     const int kq = c.lane_r >> 2;
     const int kslot = static_cast<int>((T0 + kq * G_::TPG) & (P - 1)) + (c.lane_r & 3);
     const uint8_t *kp = c.k_head + static_cast<int64_t>(select4(kq, pg)) * c.page_bytes +
@@ -182,14 +197,22 @@ __device__ __forceinline__ void mfma_load(MfmaTile<BF16, D> &t, const MfmaCtx<BF
     for (int j = 0; j < G_::NJ; ++j)
 #pragma unroll
         for (int l = 0; l < G_::KL; ++l)
-            t.k[j][l] = load16_stream(kp + j * 4 * (D * G_::E) + 16 * l);
-    // V: this lane supplies head dim dt*16 + r over the tokens of group g
+            t.k[j][l] = load16_kv<!BF16>(kp + j * 4 * (D * G_::E) + 16 * l);
+}
+
+template <bool BF16, int D>
+__device__ __forceinline__ void mfma_load_v(MfmaTile<BF16, D> &t, const MfmaCtx<BF16, D> &c,
+                                            int64_t T0, const TilePages &pg)
+{
+    using G_ = Geo<BF16, D>;
+    const int P = 1 << c.log2_page;
+    // this lane supplies head dim dt*16 + r over the tokens of group g
     const int vslot = static_cast<int>((T0 + c.lane_g * G_::TPG) & (P - 1));
     const uint8_t *vp = c.v_head + static_cast<int64_t>(select4(c.lane_g, pg)) * c.page_bytes +
                         (static_cast<int64_t>(c.lane_r) * P + vslot) * G_::E;
 #pragma unroll
     for (int dt = 0; dt < G_::NDT; ++dt)
-        t.v[dt] = load16_stream(vp + static_cast<int64_t>(dt) * 16 * P * G_::E);
+        t.v[dt] = load16_kv<!BF16>(vp + static_cast<int64_t>(dt) * 16 * P * G_::E);
 }
 
 template <bool BF16, int D>
@@ -199,14 +222,13 @@ struct MfmaState {
     float l;                     // this lane's share of the softmax denominator
 };
 
+// S^T = K Q^T for one tile: rows = tokens, columns = the group's heads.
 template <bool BF16, int D>
-__device__ __forceinline__ void mfma_compute(const MfmaTile<BF16, D> &t, MfmaState<BF16, D> &st,
-                                             const bf16x8 (&qop)[Geo<BF16, D>::NC], float cs,
-                                             int64_t T0, int64_t t1, int lane_g)
+__device__ __forceinline__ void mfma_qk(const MfmaTile<BF16, D> &t,
+                                        const bf16x8 (&qop)[Geo<BF16, D>::NC],
+                                        f32x4 (&sacc)[Geo<BF16, D>::NJ])
 {
     using G_ = Geo<BF16, D>;
-    // ---- S^T = K Q^T: rows = tokens, columns = heads -------------------------
-    f32x4 sacc[G_::NJ];
 #pragma unroll
     for (int j = 0; j < G_::NJ; ++j) {
         sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -222,6 +244,18 @@ __device__ __forceinline__ void mfma_compute(const MfmaTile<BF16, D> &t, MfmaSta
             sacc[j] = mfma_bf16(a, qop[c], sacc[j]);
         }
     }
+}
+
+// Online softmax of one tile's scores, then O^T += V^T P^T (rows = head dims,
+// columns = heads).  TAIL masks tokens at or past t1 (only a split's last
+// tile can hold such tokens).
+template <bool BF16, int D, bool TAIL>
+__device__ __forceinline__ void mfma_softmax_pv(const MfmaTile<BF16, D> &t,
+                                                const f32x4 (&sacc)[Geo<BF16, D>::NJ],
+                                                MfmaState<BF16, D> &st, float cs, int64_t T0,
+                                                int64_t t1, int lane_g)
+{
+    using G_ = Geo<BF16, D>;
     // lane holds the scores of tokens T0 + lane_g*TPG + n, n = 4j + v
     float s[G_::TPG];
 #pragma unroll
@@ -229,17 +263,14 @@ __device__ __forceinline__ void mfma_compute(const MfmaTile<BF16, D> &t, MfmaSta
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             s[4 * j + v] = sacc[j][v];
-    const int64_t g0 = T0 + lane_g * G_::TPG;
-    const bool tail = T0 + G_::TT > t1;
     int nvalid = G_::TPG;
-    if (tail) {
-        const int64_t nv = t1 - g0;
+    if constexpr (TAIL) {
+        const int64_t nv = t1 - (T0 + lane_g * G_::TPG);
         nvalid = nv < 0 ? 0 : (nv > G_::TPG ? G_::TPG : static_cast<int>(nv));
 #pragma unroll
         for (int n = 0; n < G_::TPG; ++n)
             s[n] = n < nvalid ? s[n] : kNegInf;
     }
-    // ---- online softmax -----------------------------------------------------------
     float mx = s[0];
 #pragma unroll
     for (int n = 1; n < G_::TPG; ++n)
@@ -260,7 +291,6 @@ __device__ __forceinline__ void mfma_compute(const MfmaTile<BF16, D> &t, MfmaSta
 #pragma unroll
     for (int dt = 0; dt < G_::NDT; ++dt)
         st.o[dt] *= alpha;
-    // ---- O^T += V^T P^T: rows = head dims, columns = heads ------------------------
 #pragma unroll
     for (int c = 0; c < G_::NPC; ++c) {
         if constexpr (BF16) {
@@ -276,7 +306,7 @@ __device__ __forceinline__ void mfma_compute(const MfmaTile<BF16, D> &t, MfmaSta
 #pragma unroll
             for (int dt = 0; dt < G_::NDT; ++dt) {
                 u32x4 w = t.v[dt];
-                if (tail)
+                if constexpr (TAIL)
                     w = keep_bytes(w, nvalid * 2);
                 const bf16x8 a = __builtin_bit_cast(bf16x8, w);
                 st.o[dt] = mfma_bf16(a, phi, st.o[dt]);
@@ -291,7 +321,7 @@ __device__ __forceinline__ void mfma_compute(const MfmaTile<BF16, D> &t, MfmaSta
 #pragma unroll
             for (int dt = 0; dt < G_::NDT; ++dt) {
                 u32x4 w = t.v[dt];
-                if (tail)
+                if constexpr (TAIL)
                     w = keep_bytes(w, nvalid);
                 const f16x8 a = e4m3x8_to_f16x8(w[2 * c], w[2 * c + 1]);
                 st.o[dt] = mfma_f16(a, pb, st.o[dt]);
@@ -357,15 +387,8 @@ __device__ __forceinline__ void merge_and_write(const AttnParams &p, MergeSmem<D
     }
 }
 
-// PIPE selects register double buffering (two tiles per wave, two waves per
-// SIMD) over single buffering (one tile per wave, three waves per SIMD).
-#ifndef PAFP8_MFMA_PIPELINE
-#define PAFP8_MFMA_PIPELINE 0
-#endif
-constexpr bool kPipe = PAFP8_MFMA_PIPELINE != 0;
-
-template <bool BF16, int D, bool PIPE>
-__global__ __launch_bounds__(kThreads, PIPE ? 2 : 3) void decode_attn_mfma_kernel(AttnParams p)
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads, 3) void decode_attn_mfma_kernel(AttnParams p)
 {
     using G_ = Geo<BF16, D>;
     __shared__ MergeSmem<D> sm;
@@ -415,52 +438,45 @@ __global__ __launch_bounds__(kThreads, PIPE ? 2 : 3) void decode_attn_mfma_kerne
         const int32_t *row = p.page_table + static_cast<int64_t>(b) * p.max_pages;
         const int stride = kWaves * G_::TT;
 
-        if constexpr (PIPE) {
-            // Register double buffering: while tile i is computed from one
-            // buffer, tile i + kWaves streams into the other and the page ids
-            // of tile i + 2*kWaves are fetched.  The last tile is peeled off so
-            // that the steady-state loads are unconditional and the compiler
-            // waits for exactly the loads a computation needs.
-            MfmaTile<BF16, D> ta, tb;
-            int i = wave;
-            int64_t T0 = rng.t0 + static_cast<int64_t>(i) * G_::TT;
-            TilePages pg = pages_ok(fetch_pages(row, T0, G_::TPG, p.log2_page, rng.p_last),
-                                    p.num_pages, bad);
-            mfma_load(ta, c, T0, pg);
-            pg = fetch_pages(row, T0 + stride, G_::TPG, p.log2_page, rng.p_last);
-            while (true) {
-                if (i + kWaves >= ntiles) {
-                    mfma_compute(ta, st, qop, cs, T0, rng.t1, c.lane_g);
-                    break;
-                }
-                mfma_load(tb, c, T0 + stride, pages_ok(pg, p.num_pages, bad));
-                pg = fetch_pages(row, T0 + 2 * stride, G_::TPG, p.log2_page, rng.p_last);
-                mfma_compute(ta, st, qop, cs, T0, rng.t1, c.lane_g);
-                i += kWaves;
-                T0 += stride;
-                if (i + kWaves >= ntiles) {
-                    mfma_compute(tb, st, qop, cs, T0, rng.t1, c.lane_g);
-                    break;
-                }
-                mfma_load(ta, c, T0 + stride, pages_ok(pg, p.num_pages, bad));
-                pg = fetch_pages(row, T0 + 2 * stride, G_::TPG, p.log2_page, rng.p_last);
-                mfma_compute(tb, st, qop, cs, T0, rng.t1, c.lane_g);
-                i += kWaves;
-                T0 += stride;
-            }
-        } else {
-            // One tile buffer per wave; latency is hidden by the other waves
-            // resident on the CU (three per SIMD).  Page ids still arrive a
-            // tile ahead.
-            int64_t T0 = rng.t0 + static_cast<int64_t>(wave) * G_::TT;
-            TilePages pg = fetch_pages(row, T0, G_::TPG, p.log2_page, rng.p_last);
-            for (int i = wave; i < ntiles; i += kWaves, T0 += stride) {
-                MfmaTile<BF16, D> t;
-                mfma_load(t, c, T0, pages_ok(pg, p.num_pages, bad));
-                pg = fetch_pages(row, T0 + stride, G_::TPG, p.log2_page, rng.p_last);
-                mfma_compute(t, st, qop, cs, T0, rng.t1, c.lane_g);
-            }
+        // Staggered pipeline, one tile buffer per wave: the next tile's K is
+        // loaded as soon as Q.K^T has consumed this tile's K, and its V as
+        // soon as P.V has consumed this tile's V, so each wave always has about
+        // one tile (16 KB) in flight without a second register buffer.  Page
+        // ids come a tile ahead.  The steady-state loop has no conditional
+        // loads (the last tile is peeled), so the compiler waits for exactly
+        // the loads each step needs.
+        MfmaTile<BF16, D> t;
+        f32x4 sacc[G_::NJ];
+        int i = wave;
+        int64_t T0 = rng.t0 + static_cast<int64_t>(i) * G_::TT;
+        {
+            const TilePages pg = pages_ok(fetch_pages(row, T0, G_::TPG, p.log2_page, rng.p_last),
+                                          p.num_pages, bad);
+            mfma_load_k(t, c, T0, pg);
+            mfma_load_v(t, c, T0, pg);
         }
+        TilePages pgn = fetch_pages(row, T0 + stride, G_::TPG, p.log2_page, rng.p_last);
+        while (i + kWaves < ntiles) {
+            const TilePages pn = pages_ok(pgn, p.num_pages, bad);
+            mfma_qk(t, qop, sacc);
+            // keep each load batch where it is: hoisting it above the
+            // computation that frees its registers would need a second buffer
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_load_k(t, c, T0 + stride, pn);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_softmax_pv<BF16, D, false>(t, sacc, st, cs, T0, rng.t1, c.lane_g);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_load_v(t, c, T0 + stride, pn);
+            __builtin_amdgcn_sched_barrier(0);
+            pgn = fetch_pages(row, T0 + 2 * stride, G_::TPG, p.log2_page, rng.p_last);
+            i += kWaves;
+            T0 += stride;
+        }
+        mfma_qk(t, qop, sacc);
+        if (T0 + G_::TT > rng.t1)
+            mfma_softmax_pv<BF16, D, true>(t, sacc, st, cs, T0, rng.t1, c.lane_g);
+        else
+            mfma_softmax_pv<BF16, D, false>(t, sacc, st, cs, T0, rng.t1, c.lane_g);
     }
     // the four lanes of a head each hold a quarter of its denominator
     float l = st.l + shfl_xor_f(st.l, 16);
@@ -640,77 +656,81 @@ __global__ __launch_bounds__(kThreads) void decode_attn_vec_kernel(AttnParams p)
 }
 
 // ===========================================================================
-// split-K combine: one wave per (request, query head)
+// split-K combine: one work-group per (request, query head).  Threads split
+// the head dims four at a time and the splits among themselves; partial
+// sums meet in LDS.
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void splitk_combine_kernel(
-    const float *__restrict__ part_o, const float *__restrict__ part_lse, int bh_total, int Hq,
-    int S, int D, const int32_t *__restrict__ req_status, float *__restrict__ out,
-    float *__restrict__ lse_out)
+__device__ __forceinline__ float block_reduce(float v, float *red, bool is_max)
 {
-    const int bh = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (bh >= bh_total)
-        return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = is_max ? wave_max(v) : wave_sum(v);
+    __syncthreads();  // red may still be read by a previous reduction
+    if (lane == 0)
+        red[w] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i)
+        r = is_max ? __builtin_fmaxf(r, red[i]) : r + red[i];
+    return r;
+}
+
+__global__ __launch_bounds__(kThreads) void splitk_combine_kernel(
+    const float *__restrict__ part_o, const float *__restrict__ part_lse, int Hq, int S, int D,
+    const int32_t *__restrict__ req_status, float *__restrict__ out, float *__restrict__ lse_out)
+{
+    __shared__ float red[kWaves];
+    __shared__ f32x4 acc_sm[kThreads];
+    const int bh = blockIdx.x;
     const int b = bh / Hq;
     const float *pl = part_lse + static_cast<int64_t>(bh) * S;
     const float *po = part_o + static_cast<int64_t>(bh) * S * D;
     float *o = out + static_cast<int64_t>(bh) * D;
+    const int nd4 = D / 4;                 // float4 columns
+    const int ngrp = kThreads / nd4;       // split groups (>= 1 since D <= 1024)
+    const int col = threadIdx.x % nd4, grp = threadIdx.x / nd4;
+
     const bool aborted = req_status != nullptr && req_status[b] != 0;
     float M = kNegInf;
     int has_nan = 0;
-    if (!aborted) {
-        for (int k = lane; k < S; k += 64) {
-            const float v = pl[k];
-            has_nan |= v != v;
-            M = __builtin_fmaxf(M, v);
-        }
-        M = wave_max(M);
-        has_nan = __any(has_nan);
+    for (int k = threadIdx.x; k < S; k += kThreads) {
+        const float v = pl[k];
+        has_nan |= v != v;
+        M = __builtin_fmaxf(M, v);
     }
+    M = block_reduce(M, red, true);
+    has_nan = __syncthreads_or(has_nan);
     if (aborted || has_nan || M == kNegInf) {
-        const float fill = has_nan ? __builtin_nanf("") : 0.f;
-        for (int d = lane; d < D; d += 64)
+        const float fill = (has_nan && !aborted) ? __builtin_nanf("") : 0.f;
+        for (int d = threadIdx.x; d < D; d += kThreads)
             o[d] = fill;
-        if (lane == 0 && lse_out != nullptr)
-            lse_out[bh] = has_nan ? fill : kNegInf;
+        if (threadIdx.x == 0 && lse_out != nullptr)
+            lse_out[bh] = (has_nan && !aborted) ? fill : kNegInf;
         return;
     }
     float sum = 0.f;
-    for (int k = lane; k < S; k += 64)
+    for (int k = threadIdx.x; k < S; k += kThreads)
         sum += __expf(pl[k] - M);
-    sum = wave_sum(sum);
+    sum = block_reduce(sum, red, false);
     const float LSE = M + __logf(sum);
-    // each lane owns head dims lane*4 + 256*i
-    constexpr int kMaxVec = 4;  // D <= 1024
-    f32x4 acc[kMaxVec];
-#pragma unroll
-    for (int i = 0; i < kMaxVec; ++i)
-        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < S; k0 += 64) {
-        const float lk = k0 + lane < S ? pl[k0 + lane] : kNegInf;
-        const float wk = lk == kNegInf ? 0.f : __expf(lk - LSE);
-        const int kn = S - k0 < 64 ? S - k0 : 64;
-        for (int k = 0; k < kn; ++k) {
-            const float w = __shfl(wk, k, 64);
-            const float lsk = __shfl(lk, k, 64);
-            if (lsk == kNegInf)
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (grp < ngrp) {
+        for (int k = grp; k < S; k += ngrp) {
+            const float lk = pl[k];
+            if (lk == kNegInf)
                 continue;  // empty split: contributes nothing
-            const float *src = po + static_cast<int64_t>(k0 + k) * D;
-#pragma unroll
-            for (int i = 0; i < kMaxVec; ++i) {
-                const int d = lane * 4 + 256 * i;
-                if (d < D)
-                    acc[i] += w * *reinterpret_cast<const f32x4 *>(src + d);
-            }
+            acc += __expf(lk - LSE) * *reinterpret_cast<const f32x4 *>(po + static_cast<int64_t>(k) * D + col * 4);
         }
     }
-#pragma unroll
-    for (int i = 0; i < kMaxVec; ++i) {
-        const int d = lane * 4 + 256 * i;
-        if (d < D)
-            *reinterpret_cast<f32x4 *>(o + d) = acc[i];
+    acc_sm[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x < nd4) {
+        f32x4 t = acc_sm[threadIdx.x];
+        for (int gi = 1; gi < ngrp; ++gi)
+            t += acc_sm[gi * nd4 + threadIdx.x];
+        *reinterpret_cast<f32x4 *>(o + threadIdx.x * 4) = t;
     }
-    if (lane == 0 && lse_out != nullptr)
+    if (threadIdx.x == 0 && lse_out != nullptr)
         lse_out[bh] = LSE;
 }
 
@@ -724,7 +744,7 @@ hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
         hipLaunchKernelGGL((decode_attn_vec_kernel<BF16, D>), dim3(static_cast<unsigned>(blocks)),
                            dim3(kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, kPipe>), dim3(static_cast<unsigned>(blocks)),
+        hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D>), dim3(static_cast<unsigned>(blocks)),
                            dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
@@ -744,10 +764,12 @@ hipError_t launch_splitk_combine(const float *part_o, const float *part_lse, int
                                  const int32_t *req_status, float *out, float *lse,
                                  hipStream_t stream)
 {
-    const int bh = batch * num_q_heads;
-    const int blocks = (bh + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL(splitk_combine_kernel, dim3(blocks), dim3(kThreads), 0, stream, part_o,
-                       part_lse, bh, num_q_heads, num_splits, head_dim, req_status, out, lse);
+    const int64_t bh = static_cast<int64_t>(batch) * num_q_heads;
+    if (bh > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(splitk_combine_kernel, dim3(static_cast<unsigned>(bh)), dim3(kThreads), 0,
+                       stream, part_o, part_lse, num_q_heads, num_splits, head_dim, req_status, out,
+                       lse);
     return hipGetLastError();
 }
 

@@ -73,13 +73,16 @@ def test_workspace_bytes(L):
 
 
 def test_default_split_choice(L):
-    # 64 x 8 units on 256 CUs: already two per CU
+    # about one work-group per CU
     assert L.pafp8_default_num_splits(64, 8, 256, 64, 256) == 1
-    # 4 long requests: split to fill the GPU
-    assert L.pafp8_default_num_splits(4, 8, 4096, 64, 256) == 16
-    # short contexts are not split below ~1024 tokens per split
+    assert L.pafp8_default_num_splits(32, 8, 256, 64, 256) == 1
+    assert L.pafp8_default_num_splits(16, 8, 256, 64, 256) == 2
+    assert L.pafp8_default_num_splits(8, 8, 256, 64, 256) == 4
+    assert L.pafp8_default_num_splits(4, 8, 4096, 64, 256) == 8
+    # no split shorter than 512 tokens
+    assert L.pafp8_default_num_splits(1, 8, 256, 64, 256) == 32
     assert L.pafp8_default_num_splits(1, 4, 16, 16, 256) == 1
-    assert L.pafp8_default_num_splits(8, 8, 256, 16, 256) == 4
+    assert L.pafp8_default_num_splits(2, 8, 64, 16, 256) == 2
 
 
 def _cache(**kw):
