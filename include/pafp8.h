@@ -40,12 +40,26 @@
  *    thread-local error message and a per-device cache of the CU count.
  *
  * Pool layout (the "shared physical page pool"):
- *   K pool: [num_pages][num_kv_heads][page_size][head_dim]   token-major
- *   V pool: [num_pages][num_kv_heads][head_dim][page_size]   dim-major
- * Elements are e4m3 codes (1 byte) or bf16 (2 bytes).  Token t of request b
- * lives in physical page page_table[b][t / page_size], slot t % page_size.
- * The same geometry therefore takes exactly half the bytes as e4m3.
- */
+ *   K pool and V pool: [num_pages][num_kv_heads][block], one block of
+ *   page_size * head_dim elements per (page, KV head).  Token t of request b
+ *   lives in physical page page_table[b][t / page_size], slot t % page_size.
+ *   Elements are e4m3 codes (e = 1 byte) or bf16 (e = 2 bytes), so the same
+ *   geometry takes exactly half the bytes as e4m3.
+ *   A block is cut into segments of SEG = min(page_size, 64 / e) consecutive
+ *   slots (64 e4m3 or 32 bf16 tokens; the whole page when it is smaller).
+ *   V segment: [head_dim][SEG], dim-major: slot u, dim d at d * SEG + u.
+ *   K segment: 16-byte chunks arranged so that one 16-byte load per lane of
+ *   a 64-lane wave reads 1 KiB of consecutive memory.  A K row of head_dim * e
+ *   bytes is R = head_dim * e / 16 chunks; chunk c = q * KL + l (KL = R / 4,
+ *   q < 4 the quarter of the row).  Slot u = TG * s + 4 * j + a of a segment
+ *   (TG = 16 / e tokens per group, a < 4) keeps chunk c at chunk position
+ *       ((j * KL + l) * 4 + q) * (4 * SEG / TG) + 4 * s + a
+ *   of the segment; byte i of the chunk holds byte i of the row's chunk.
+ *   page_size is a power of two >= 16, so every segment holds a whole number
+ *   of token groups.  The cache is only meant to be written by
+ *   kv_quant_append / kv_quant_fill; the layout is stated for tools that read
+ *   it back.
+  */
 #ifndef PAFP8_H
 #define PAFP8_H
 
@@ -58,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PAFP8_ABI_VERSION 1
+#define PAFP8_ABI_VERSION 2  /* 2: segmented block layout */
 
 typedef int32_t pafp8_status;
 #define PAFP8_OK 0

@@ -79,9 +79,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_quantize.restype = ctypes.c_uint8
         L.oracle_quantize.argtypes = [ctypes.c_uint16, _F]
         L.oracle_k_offset.restype = _I64
-        L.oracle_k_offset.argtypes = [_I64, _I, _I, _I, _I, _I, _I]
+        L.oracle_k_offset.argtypes = [_I, _I64, _I, _I, _I, _I, _I, _I]
         L.oracle_v_offset.restype = _I64
-        L.oracle_v_offset.argtypes = [_I64, _I, _I, _I, _I, _I, _I]
+        L.oracle_v_offset.argtypes = [_I, _I64, _I, _I, _I, _I, _I, _I]
         L.oracle_kv_write.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P,
                                       _P, _P, _P, _P, _P, _P]
         L.oracle_kv_append.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
@@ -152,11 +152,18 @@ def quantize(x_bf16: int, scale: float) -> int:
 class Pool:
     """Host copy of the physical page pool in the documented layout.
 
-    K: [num_pages][Hkv][P][D], V: [num_pages][Hkv][D][P]; uint8 e4m3 codes
-    (kv_dtype 0) or uint16 bf16 bit patterns (kv_dtype 1).
+    Arrays of shape [num_pages][Hkv][P][D] (K) and [num_pages][Hkv][D][P]
+    (V), the device tensors' shapes; the last two axes hold one head's block
+    of a page in the element order the library documents (see k_offset /
+    v_offset), which is not [slot][dim] / [dim][slot] in general.
+    uint8 e4m3 codes (kv_dtype 0) or uint16 bf16 bit patterns (kv_dtype 1).
     """
 
     def __init__(self, kv_dtype, num_pages, Hkv, P, D, fill=0):
+        e = 1 if kv_dtype == KV_FP8 else 2
+        if (D * e) % 64 or P % (16 // e) or P & (P - 1):
+            raise ValueError(f"the pool layout needs head_dim*e % 64 == 0 and a power-of-two page "
+                             f"of at least {16 // e} tokens (got D={D}, P={P})")
         self.kv_dtype, self.num_pages, self.Hkv, self.P, self.D = kv_dtype, num_pages, Hkv, P, D
         dt = np.uint8 if kv_dtype == KV_FP8 else np.uint16
         self.k = np.full((num_pages, Hkv, P, D), fill, dtype=dt)
@@ -190,12 +197,14 @@ def kv_append(pool: Pool, page_table, context_lens, k_new, v_new, k_scale=None, 
                            _ptr(_c(v_scale, np.float32)), _ptr(pool.k), _ptr(pool.v))
 
 
-def k_offset(page, g, slot, d, Hkv, P, D) -> int:
-    return lib().oracle_k_offset(page, g, slot, d, Hkv, P, D)
+def k_offset(kv_dtype, page, g, slot, d, Hkv, P, D) -> int:
+    """Element offset of K (page, head g, slot, dim d) in the pool."""
+    return lib().oracle_k_offset(kv_dtype, page, g, slot, d, Hkv, P, D)
 
 
-def v_offset(page, g, slot, d, Hkv, P, D) -> int:
-    return lib().oracle_v_offset(page, g, slot, d, Hkv, P, D)
+def v_offset(kv_dtype, page, g, slot, d, Hkv, P, D) -> int:
+    """Element offset of V (page, head g, slot, dim d) in the pool."""
+    return lib().oracle_v_offset(kv_dtype, page, g, slot, d, Hkv, P, D)
 
 
 # --- O6: tag check --------------------------------------------------------------

@@ -190,29 +190,47 @@ uint8_t oracle_quantize(uint16_t x_bf16, float scale)
 
 /* ------------------------------------------------------------------------ */
 /* O5. addressing of token t of request b in the shared physical pool [PAG]. */
-/*   page = page_table[b][t / P], slot = t mod P                             */
-/*   K element (page, g, slot, d) at ((page*Hkv + g)*P + slot)*D + d          */
-/*   V element (page, g, slot, d) at ((page*Hkv + g)*D + d)*P + slot          */
-/* (offsets in elements; the element size is 1 byte for e4m3, 2 for bf16)    */
+/*   page = page_table[b][t / P], slot = t mod P.                            */
+/* Within a page, each KV head owns a K block and a V block of P*D elements  */
+/* (e bytes each: 1 for e4m3, 2 for bf16), laid out as the library documents. */
+/* Both blocks are cut into segments of SEG = min(P, 64/e) tokens.            */
+/*   K: a token row of D*e bytes is R = D*e/16 chunks of 16 bytes, chunk      */
+/*      c = q*KL + l with KL = R/4.  Token u of a segment, u = TG*s + 4j + a  */
+/*      with TG = 16/e and a < 4, has chunk c at chunk position               */
+/*      ((j*KL + l)*4 + q)*(4*NS) + 4s + a of the segment, NS = SEG/TG.       */
+/*   V: a segment is [D][SEG]: element (u, d) at d*SEG + u.                   */
+/* Offsets below are in elements from the start of the pool.                 */
 /* ------------------------------------------------------------------------ */
-static int64_t k_offset(int64_t page, int g, int slot, int d, int Hkv, int P, int D)
+static int64_t k_offset(int kv_dtype, int64_t page, int g, int slot, int d, int Hkv, int P, int D)
 {
-    return ((page * Hkv + g) * (int64_t)P + slot) * (int64_t)D + d;
+    int e = kv_dtype == 0 ? 1 : 2;
+    int SEG = 64 / e < P ? 64 / e : P;
+    int TG = 16 / e, NS = SEG / TG, R = D * e / 16, KL = R / 4;
+    int seg = slot / SEG, u = slot % SEG;
+    int sub = u / TG, w = u % TG, j = w / 4, a = w % 4;
+    int byte = d * e, c = byte / 16, q = c / KL, l = c % KL;
+    int64_t block = (page * Hkv + g) * (int64_t)P * D * e;            /* bytes */
+    int64_t in_block = (int64_t)seg * SEG * D * e                     /* whole segments */
+                       + ((int64_t)((j * KL + l) * 4 + q) * (4 * NS) + 4 * sub + a) * 16
+                       + byte % 16;
+    return (block + in_block) / e;
 }
 
-static int64_t v_offset(int64_t page, int g, int slot, int d, int Hkv, int P, int D)
+static int64_t v_offset(int kv_dtype, int64_t page, int g, int slot, int d, int Hkv, int P, int D)
 {
-    return ((page * Hkv + g) * (int64_t)D + d) * (int64_t)P + slot;
+    int e = kv_dtype == 0 ? 1 : 2;
+    int SEG = 64 / e < P ? 64 / e : P;
+    return (page * Hkv + g) * (int64_t)P * D + ((int64_t)(slot / SEG) * D + d) * SEG + slot % SEG;
 }
 
-int64_t oracle_k_offset(int64_t page, int g, int slot, int d, int Hkv, int P, int D)
+int64_t oracle_k_offset(int kv_dtype, int64_t page, int g, int slot, int d, int Hkv, int P, int D)
 {
-    return k_offset(page, g, slot, d, Hkv, P, D);
+    return k_offset(kv_dtype, page, g, slot, d, Hkv, P, D);
 }
 
-int64_t oracle_v_offset(int64_t page, int g, int slot, int d, int Hkv, int P, int D)
+int64_t oracle_v_offset(int kv_dtype, int64_t page, int g, int slot, int d, int Hkv, int P, int D)
 {
-    return v_offset(page, g, slot, d, Hkv, P, D);
+    return v_offset(kv_dtype, page, g, slot, d, Hkv, P, D);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -249,8 +267,8 @@ void oracle_kv_write(int kv_dtype, int B, int maxP, int P, int Hkv, int D, int n
                     continue;
                 for (d = 0; d < D; ++d) {
                     int64_t src = (((int64_t)b * T_src + j) * Hkv + g) * D + d;
-                    int64_t ko = k_offset(page, g, slot, d, Hkv, P, D);
-                    int64_t vo = v_offset(page, g, slot, d, Hkv, P, D);
+                    int64_t ko = k_offset(kv_dtype, page, g, slot, d, Hkv, P, D);
+                    int64_t vo = v_offset(kv_dtype, page, g, slot, d, Hkv, P, D);
                     if (kv_dtype == 0) {
                         ((uint8_t *)k_pool)[ko] = oracle_quantize(k_src[src], k_scale[g]);
                         ((uint8_t *)v_pool)[vo] = oracle_quantize(v_src[src], v_scale[g]);
@@ -333,7 +351,8 @@ static double kv_value(int kv_dtype, int is_v, const void *pool, const float *sc
         *bad = 1;
         return NAN;
     }
-    off = is_v ? v_offset(page, g, slot, d, Hkv, P, D) : k_offset(page, g, slot, d, Hkv, P, D);
+    off = is_v ? v_offset(kv_dtype, page, g, slot, d, Hkv, P, D)
+               : k_offset(kv_dtype, page, g, slot, d, Hkv, P, D);
     if (kv_dtype == 0)
         return oracle_e4m3_decode(((const uint8_t *)pool)[off]) * (double)scale[g];
     return (double)bf16_value(((const uint16_t *)pool)[off]);

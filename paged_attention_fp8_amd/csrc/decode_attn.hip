@@ -89,10 +89,19 @@ struct TilePages {
     int32_t pid[4];
 };
 
+template <bool ONE_PAGE = false>
 __device__ __forceinline__ TilePages fetch_pages(const int32_t *__restrict__ row, int64_t T0,
                                                  int tpg, int log2_page, int64_t p_last)
 {
     TilePages t;
+    if constexpr (ONE_PAGE) {
+        // the whole tile lies in one page
+        int64_t idx = T0 >> log2_page;
+        if (idx > p_last)
+            idx = p_last;
+        t.pid[0] = t.pid[1] = t.pid[2] = t.pid[3] = row[idx];
+        return t;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         int64_t idx = (T0 + q * tpg) >> log2_page;
@@ -150,7 +159,10 @@ struct Geo {
     static constexpr int NDT = D / 16;              // P.V MFMAs along the head dim
     static constexpr int NPC = TT / 32;             // P.V MFMAs along tokens
     static constexpr int KL = (D / 4) * E / 16;     // 16-byte K loads per lane per token row
+    static constexpr int LOG2_TT = BF16 ? 5 : 6;
+    static constexpr int LOG2_TPG = LOG2_TT - 2;
     static_assert(TPG * E == 16, "a lane group's V run must be one 16-byte load");
+    static_assert((1 << LOG2_TT) == TT, "tile size");
 };
 
 template <bool BF16, int D>
@@ -168,11 +180,11 @@ struct MfmaCtx {
     int lane_r, lane_g;     // lane % 16, lane / 16
 };
 
-// 16-byte KV loads.  e4m3 tiles stream past the caches (each 128-byte line
-// is consumed by one wave's back-to-back loads); bf16 loads stay cacheable:
-// a bf16 tile covers only half of each V line, the other half belonging to
-// the next tile (another wave), and on MI355X streaming bf16 loads (K or V)
-// cost 15-25% of the bandwidth.
+// 16-byte KV loads.  Every K and V line a tile touches is consumed whole by
+// the wave's own load steps, so the loads stream past the caches.
+#ifndef PAFP8_KV_STREAM
+#define PAFP8_KV_STREAM 1
+#endif
 template <bool STREAM>
 __device__ __forceinline__ u32x4 load16_kv(const void *p)
 {
@@ -182,37 +194,68 @@ __device__ __forceinline__ u32x4 load16_kv(const void *p)
         return load16(p);
 }
 
-template <bool BF16, int D>
+// Pool block layout (per page and KV head; see include/pafp8.h): blocks are
+// cut into segments of min(P, TT) tokens -- exactly one wave tile when the
+// page holds one.  K: token TPG*s + 4j + a of a segment keeps its 16-byte
+// chunk q*KL + l at chunk ((j*KL + l)*4 + q)*(4*NS) + 4s + a (NS = segment /
+// TPG), which is precisely the chunk lane 16q + 4s + a loads in step (j, l):
+// every K load step of a tile reads one contiguous run.  V: a segment is
+// [D][segment tokens], so a V load step reads 16 consecutive 64-byte rows.
+//
+// BIG (page >= tile): the tile is one whole segment of one page, so the page
+// base is wave-uniform and each load step is 1 KB at a compile-time offset.
+template <bool BF16, int D, bool BIG>
 __device__ __forceinline__ void mfma_load_k(MfmaTile<BF16, D> &t, const MfmaCtx<BF16, D> &c,
                                             int64_t T0, const TilePages &pg)
 {
     using G_ = Geo<BF16, D>;
-    const int P = 1 << c.log2_page;
-    // this lane supplies token rows of group r/4, head dims [g*D/4, (g+1)*D/4)
-    const int kq = c.lane_r >> 2;
-    const int kslot = static_cast<int>((T0 + kq * G_::TPG) & (P - 1)) + (c.lane_r & 3);
-    const uint8_t *kp = c.k_head + static_cast<int64_t>(select4(kq, pg)) * c.page_bytes +
-                        static_cast<int64_t>(kslot) * (D * G_::E) + c.lane_g * (D / 4) * G_::E;
+    if constexpr (BIG) {
+        const int seg = static_cast<int>(T0 & ((int64_t{1} << c.log2_page) - 1)) >> G_::LOG2_TT;
+        const uint8_t *kp = c.k_head + static_cast<int64_t>(pg.pid[0]) * c.page_bytes +
+                            seg * (G_::TT * D * G_::E) + (c.lane_g * 16 + c.lane_r) * 16;
 #pragma unroll
-    for (int j = 0; j < G_::NJ; ++j)
+        for (int j = 0; j < G_::NJ; ++j)
 #pragma unroll
-        for (int l = 0; l < G_::KL; ++l)
-            t.k[j][l] = load16_kv<!BF16>(kp + j * 4 * (D * G_::E) + 16 * l);
+            for (int l = 0; l < G_::KL; ++l)
+                t.k[j][l] = load16_kv<PAFP8_KV_STREAM != 0>(kp + (j * G_::KL + l) * 1024);
+    } else {
+        // the page is the segment; lane group r/4 reads token group s of its page
+        const int P = 1 << c.log2_page;
+        const int log2_ns = c.log2_page - G_::LOG2_TPG;
+        const int kq = c.lane_r >> 2;
+        const int sub = static_cast<int>((T0 + kq * G_::TPG) & (P - 1)) >> G_::LOG2_TPG;
+        const uint8_t *kp = c.k_head + static_cast<int64_t>(select4(kq, pg)) * c.page_bytes +
+                            ((((c.lane_g << log2_ns) + sub) * 4 + (c.lane_r & 3)) * 16);
+#pragma unroll
+        for (int j = 0; j < G_::NJ; ++j)
+#pragma unroll
+            for (int l = 0; l < G_::KL; ++l)
+                t.k[j][l] = load16_kv<PAFP8_KV_STREAM != 0>(kp + ((j * G_::KL + l) * 256 << log2_ns));
+    }
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool BIG>
 __device__ __forceinline__ void mfma_load_v(MfmaTile<BF16, D> &t, const MfmaCtx<BF16, D> &c,
                                             int64_t T0, const TilePages &pg)
 {
     using G_ = Geo<BF16, D>;
-    const int P = 1 << c.log2_page;
-    // this lane supplies head dim dt*16 + r over the tokens of group g
-    const int vslot = static_cast<int>((T0 + c.lane_g * G_::TPG) & (P - 1));
-    const uint8_t *vp = c.v_head + static_cast<int64_t>(select4(c.lane_g, pg)) * c.page_bytes +
-                        (static_cast<int64_t>(c.lane_r) * P + vslot) * G_::E;
+    // this lane supplies head dim dt*16 + r over the TPG tokens of group g
+    if constexpr (BIG) {
+        const int seg = static_cast<int>(T0 & ((int64_t{1} << c.log2_page) - 1)) >> G_::LOG2_TT;
+        const uint8_t *vp = c.v_head + static_cast<int64_t>(pg.pid[0]) * c.page_bytes +
+                            seg * (G_::TT * D * G_::E) + (c.lane_r * G_::TT + c.lane_g * G_::TPG) * G_::E;
 #pragma unroll
-    for (int dt = 0; dt < G_::NDT; ++dt)
-        t.v[dt] = load16_kv<!BF16>(vp + static_cast<int64_t>(dt) * 16 * P * G_::E);
+        for (int dt = 0; dt < G_::NDT; ++dt)
+            t.v[dt] = load16_kv<PAFP8_KV_STREAM != 0>(vp + dt * 16 * G_::TT * G_::E);
+    } else {
+        const int P = 1 << c.log2_page;
+        const int vslot = static_cast<int>((T0 + c.lane_g * G_::TPG) & (P - 1));
+        const uint8_t *vp = c.v_head + static_cast<int64_t>(select4(c.lane_g, pg)) * c.page_bytes +
+                            ((c.lane_r << c.log2_page) + vslot) * G_::E;
+#pragma unroll
+        for (int dt = 0; dt < G_::NDT; ++dt)
+            t.v[dt] = load16_kv<PAFP8_KV_STREAM != 0>(vp + ((dt * 16 * G_::E) << c.log2_page));
+    }
 }
 
 template <bool BF16, int D>
@@ -387,7 +430,7 @@ __device__ __forceinline__ void merge_and_write(const AttnParams &p, MergeSmem<D
     }
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool BIG>
 __global__ __launch_bounds__(kThreads, 3) void decode_attn_mfma_kernel(AttnParams p)
 {
     using G_ = Geo<BF16, D>;
@@ -450,25 +493,25 @@ __global__ __launch_bounds__(kThreads, 3) void decode_attn_mfma_kernel(AttnParam
         int i = wave;
         int64_t T0 = rng.t0 + static_cast<int64_t>(i) * G_::TT;
         {
-            const TilePages pg = pages_ok(fetch_pages(row, T0, G_::TPG, p.log2_page, rng.p_last),
+            const TilePages pg = pages_ok(fetch_pages<BIG>(row, T0, G_::TPG, p.log2_page, rng.p_last),
                                           p.num_pages, bad);
-            mfma_load_k(t, c, T0, pg);
-            mfma_load_v(t, c, T0, pg);
+            mfma_load_k<BF16, D, BIG>(t, c, T0, pg);
+            mfma_load_v<BF16, D, BIG>(t, c, T0, pg);
         }
-        TilePages pgn = fetch_pages(row, T0 + stride, G_::TPG, p.log2_page, rng.p_last);
+        TilePages pgn = fetch_pages<BIG>(row, T0 + stride, G_::TPG, p.log2_page, rng.p_last);
         while (i + kWaves < ntiles) {
             const TilePages pn = pages_ok(pgn, p.num_pages, bad);
             mfma_qk(t, qop, sacc);
             // keep each load batch where it is: hoisting it above the
             // computation that frees its registers would need a second buffer
             __builtin_amdgcn_sched_barrier(0);
-            mfma_load_k(t, c, T0 + stride, pn);
+            mfma_load_k<BF16, D, BIG>(t, c, T0 + stride, pn);
             __builtin_amdgcn_sched_barrier(0);
             mfma_softmax_pv<BF16, D, false>(t, sacc, st, cs, T0, rng.t1, c.lane_g);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_load_v(t, c, T0 + stride, pn);
+            mfma_load_v<BF16, D, BIG>(t, c, T0 + stride, pn);
             __builtin_amdgcn_sched_barrier(0);
-            pgn = fetch_pages(row, T0 + 2 * stride, G_::TPG, p.log2_page, rng.p_last);
+            pgn = fetch_pages<BIG>(row, T0 + 2 * stride, G_::TPG, p.log2_page, rng.p_last);
             i += kWaves;
             T0 += stride;
         }
@@ -572,21 +615,30 @@ __global__ __launch_bounds__(kThreads) void decode_attn_vec_kernel(AttnParams p)
     const uint8_t *k_head = p.k_pool + g * head_bytes;
     const uint8_t *v_head = p.v_pool + g * head_bytes;
     const int32_t *row = p.page_table + static_cast<int64_t>(b) * p.max_pages;
+    // segment of the block layout: min(page, 64 bytes / element) tokens
+    const int log2_seg = p.log2_page < (BF16 ? 5 : 6) ? p.log2_page : (BF16 ? 5 : 6);
 
     for (int i = wave; i < ntiles; i += kWaves) {
         const int64_t T0 = rng.t0 + static_cast<int64_t>(i) * V_::TT;
         const TilePages pg = pages_ok(fetch_pages(row, T0, 16, p.log2_page, rng.p_last),
                                       p.num_pages, bad);
-        // K row of token T0 + lane
+        // K row of token T0 + lane: token TG*sub + 4j + a of its segment keeps
+        // chunk qc*KLc + l at chunk ((j*KLc + l)*4 + qc)*(4*NS) + 4*sub + a
         const int q = lane >> 4;
         const int kslot = static_cast<int>((T0 + q * 16) & (P - 1)) + (lane & 15);
+        constexpr int LOG2_TG = BF16 ? 3 : 4;     // tokens per K token group: 16 / e
+        constexpr int KLc = V_::KL / 4;           // chunks per quarter row
+        const int log2_ns = log2_seg - LOG2_TG;
+        const int ku = kslot & ((1 << log2_seg) - 1);
+        const int kw = ku & ((1 << LOG2_TG) - 1);
         const uint8_t *kp = k_head + static_cast<int64_t>(select4(q, pg)) * page_bytes +
-                            static_cast<int64_t>(kslot) * D * V_::E;
+                            (kslot >> log2_seg) * ((D * V_::E) << log2_seg) +
+                            ((((kw >> 2) * KLc * 4) << (2 + log2_ns)) + ((ku >> LOG2_TG) << 2) + (kw & 3)) * 16;
         u32x4 kr[V_::KL];
 #pragma unroll
         for (int e = 0; e < V_::KL; ++e)
-            kr[e] = load16_stream(kp + 16 * e);
-        // V: rows lane + 64*r, four 16-token runs
+            kr[e] = load16_stream(kp + ((((e % KLc) * 4 + e / KLc) << (2 + log2_ns)) * 16));
+        // V: rows lane + 64*r, four 16-token runs; a segment is [D][tokens]
         u32x4 vr[V_::ROWS][4][V_::VL];
 #pragma unroll
         for (int r = 0; r < V_::ROWS; ++r)
@@ -594,7 +646,8 @@ __global__ __launch_bounds__(kThreads) void decode_attn_vec_kernel(AttnParams p)
             for (int qq = 0; qq < 4; ++qq) {
                 const int vslot = static_cast<int>((T0 + qq * 16) & (P - 1));
                 const uint8_t *vp = v_head + static_cast<int64_t>(pg.pid[qq]) * page_bytes +
-                                    (static_cast<int64_t>(lane + 64 * r) * P + vslot) * V_::E;
+                                    ((((vslot >> log2_seg) * D + lane + 64 * r) << log2_seg) +
+                                     (vslot & ((1 << log2_seg) - 1))) * V_::E;
 #pragma unroll
                 for (int e = 0; e < V_::VL; ++e)
                     vr[r][qq][e] = load16_stream(vp + 16 * e);
@@ -743,8 +796,11 @@ hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
     if (p.group == 1)
         hipLaunchKernelGGL((decode_attn_vec_kernel<BF16, D>), dim3(static_cast<unsigned>(blocks)),
                            dim3(kThreads), 0, stream, p);
+    else if (p.log2_page >= Geo<BF16, D>::LOG2_TT)
+        hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, true>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D>), dim3(static_cast<unsigned>(blocks)),
+        hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, false>), dim3(static_cast<unsigned>(blocks)),
                            dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

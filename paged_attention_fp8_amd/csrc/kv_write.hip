@@ -11,9 +11,9 @@
 // Work split: one work-group per (request, KV head, 16 consecutive positions).
 // Positions are grouped on 16-aligned boundaries so that a group never spans
 // two pages (pages hold a multiple of 16 tokens).  Thread d owns one head
-// dimension: its K codes go to 16 rows of the token-major K page (a warp-wide
-// contiguous row per token), its V codes form one contiguous 16-slot run of
-// the dim-major V page and leave as a single 16-byte store.
+// dimension: its K codes land in the 16-byte chunks of the block layout
+// (consecutive threads fill a chunk), its V codes form one contiguous run of
+// 16 slots of a V row and leave as a single 16-byte store (two for bf16).
 #include "pafp8_device.hpp"
 #include "pafp8_internal.hpp"
 
@@ -69,8 +69,20 @@ __global__ __launch_bounds__(D) void kv_write_kernel(WriteParams p, int groups_p
     const int slot0 = static_cast<int>(g0 & (P - 1));
     constexpr int E = BF16 ? 2 : 1;
     const int64_t head_block = (static_cast<int64_t>(page) * p.num_kv_heads + g) * P * D;
-    uint8_t *kdst = p.k_pool + (head_block + static_cast<int64_t>(slot0) * D + d) * E;
-    uint8_t *vdst = p.v_pool + (head_block + static_cast<int64_t>(d) * P + slot0) * E;
+    // Block layout (include/pafp8.h): segments of SEG = min(P, 64/E) tokens.
+    // K: token TG*sub + 4j + a of a segment (TG = 16/E) keeps its 16-byte
+    // chunk q*KL + l at chunk ((j*KL + l)*4 + q)*(4*NS) + 4*sub + a, NS =
+    // SEG/TG; thread d's element is byte (d*E) % 16 of chunk d*E/16.  V: a
+    // segment is [D][SEG]; the 16 aligned positions of this work-group lie in
+    // one segment, so thread d's 16 V codes are contiguous.
+    constexpr int LOG2_TG = BF16 ? 3 : 4, KL = D * E / 64;
+    const int log2_seg = p.log2_page < (BF16 ? 5 : 6) ? p.log2_page : (BF16 ? 5 : 6);
+    const int log2_ns = log2_seg - LOG2_TG;
+    const int c = d * E / 16;
+    const int kq = c / KL, kl = c % KL;
+    uint8_t *kblock = p.k_pool + head_block * E + (d * E) % 16;
+    const int seg0 = slot0 >> log2_seg, u0 = slot0 & ((1 << log2_seg) - 1);
+    uint8_t *vdst = p.v_pool + (head_block + ((static_cast<int64_t>(seg0) * D + d) << log2_seg) + u0) * E;
     const float ks = BF16 ? 1.0f : p.k_scale[g];
     const float vs = BF16 ? 1.0f : p.v_scale[g];
     const int64_t src_stride = static_cast<int64_t>(p.num_kv_heads) * D;  // per token
@@ -87,11 +99,16 @@ __global__ __launch_bounds__(D) void kv_write_kernel(WriteParams p, int groups_p
         const int64_t j = pos - start;
         const uint16_t kx = ksrc[j * src_stride];
         const uint16_t vx = vsrc[j * src_stride];
+        // token i of this 16-position group: segment-relative token u
+        const int u = u0 + i;
+        const int w = u & ((1 << LOG2_TG) - 1);
+        uint8_t *kdst = kblock + seg0 * ((D * E) << log2_seg) +
+                        (((((w >> 2) * KL + kl) * 4 + kq) << (2 + log2_ns)) + ((u >> LOG2_TG) << 2) + (w & 3)) * 16;
         if (BF16) {
-            reinterpret_cast<uint16_t *>(kdst)[i * D] = kx;
+            *reinterpret_cast<uint16_t *>(kdst) = kx;
             vword[i >> 1] |= static_cast<uint32_t>(vx) << (16 * (i & 1));
         } else {
-            kdst[i * D] = static_cast<uint8_t>(quantize_bf16(kx, ks));
+            *kdst = static_cast<uint8_t>(quantize_bf16(kx, ks));
             vword[i >> 2] |= quantize_bf16(vx, vs) << (8 * (i & 3));
         }
     }

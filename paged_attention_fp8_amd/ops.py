@@ -24,7 +24,7 @@ KV_BF16 = 1
 REQ_TAG_MISMATCH = 1
 REQ_PAGE_OOB = 2
 REQ_BAD_LEN = 4
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class Pafp8Error(RuntimeError):

@@ -62,14 +62,55 @@ def e4m3_table_torch():
     return _E4M3
 
 
+def block_index_maps(kv_dtype, P, D):
+    """Element offsets, within one head's K block and V block of a page, of
+    element (slot t, dim d): the documented pool layout written out in NumPy
+    (independently of the oracle's C addressing).
+
+    Blocks are cut into segments of SEG = min(P, 64/e) tokens.
+    K: a token row of D*e bytes is R = D*e/16 chunks of 16 bytes, chunk
+    c = q*KL + l with KL = R/4; token u = TG*s + 4j + a of a segment (TG =
+    16/e, a < 4) has chunk c at chunk position ((j*KL + l)*4 + q)*(4*NS) +
+    4s + a of the segment, NS = SEG/TG.
+    V: a segment is [D][SEG].
+    """
+    e = 1 if kv_dtype == oracle.KV_FP8 else 2
+    t = np.arange(P)[:, None]
+    d = np.arange(D)[None, :]
+    SEG = min(P, 64 // e)
+    TG, R = 16 // e, D * e // 16
+    NS, KL = SEG // TG, R // 4
+    seg, u = t // SEG, t % SEG
+    sub, w = u // TG, u % TG
+    j, a = w // 4, w % 4
+    byte = d * e
+    c, inner = byte // 16, byte % 16
+    q, l = c // KL, c % KL
+    k_bytes = seg * SEG * D * e + (((j * KL + l) * 4 + q) * (4 * NS) + 4 * sub + a) * 16 + inner
+    v_off = (seg * D + d) * SEG + u
+    return (k_bytes // e).astype(np.int64), v_off.astype(np.int64)
+
+
+def kv_rows(pool, pages, slots):
+    """K and V of (page, slot) pairs for every head: arrays [n][Hkv][D] of raw
+    codes / bf16 bits, read from the pool by the documented layout."""
+    kmap, vmap = block_index_maps(pool.kv_dtype, pool.P, pool.D)
+    pages = np.asarray(pages, np.int64)[:, None, None]
+    slots = np.asarray(slots, np.int64)
+    heads = np.arange(pool.Hkv, dtype=np.int64)[None, :, None]
+    block = (pages * pool.Hkv + heads) * pool.P * pool.D
+    kidx = block + kmap[slots][:, None, :]
+    vidx = block + vmap[slots][:, None, :]
+    return pool.k.reshape(-1)[kidx], pool.v.reshape(-1)[vidx]
+
+
 def dense_kv(pool, page_row, L, kv_dtype, k_scale=None, v_scale=None):
     """Gather tokens [0, L) of one request from the pool by NumPy indexing of
     the documented layout; returns fp64 K, V [L][Hkv][D]."""
     t = np.arange(L)
     pages = np.asarray(page_row)[t // pool.P]
     slots = t % pool.P
-    kc = pool.k[pages, :, slots, :]
-    vc = pool.v[pages, :, :, slots]
+    kc, vc = kv_rows(pool, pages, slots)
     if kv_dtype == oracle.KV_FP8:
         tab = e4m3_table_torch()
         K = tab[kc] * np.asarray(k_scale, np.float64)[None, :, None]

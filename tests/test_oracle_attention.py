@@ -20,7 +20,7 @@ import oracle
 from paged_attention_fp8_amd import inputs as I
 from helpers import dense_kv, oracle_pool, textbook_attention
 
-SMALL = I.Workload("small_gqa2_ragged", 3, 4, 2, 32, 8, 1, 53, pool_factor=1.5)
+SMALL = I.Workload("small_gqa2_ragged", 3, 4, 2, 64, 16, 1, 70, pool_factor=1.5)
 
 
 def _inputs(w=SMALL, seed=1, **kw):
@@ -119,7 +119,7 @@ def test_physical_page_permutation_invariance():
 def test_split_ranges_combine_to_whole():
     """Attention over page-aligned token ranges, merged by the combine, equals
     attention over the whole context."""
-    inp = _inputs(I.scaled(SMALL, min_len=40, max_len=53), seed=9)
+    inp = _inputs(I.scaled(SMALL, min_len=50, max_len=70), seed=9)
     pool = oracle_pool(inp, oracle.KV_FP8)
     sm = 0.3
     args = (inp.k_scale, inp.v_scale)

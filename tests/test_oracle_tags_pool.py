@@ -117,31 +117,71 @@ def test_tag_check_thousand_requests_one_stale():
 
 # --- pool writes -----------------------------------------------------------------
 
+def test_block_layout_maps_are_permutations():
+    from helpers import block_index_maps
+    for kv in (oracle.KV_FP8, oracle.KV_BF16):
+        for P in (16, 32, 64, 128, 256):
+            for D in (64, 128):
+                kmap, vmap = block_index_maps(kv, P, D)
+                assert np.array_equal(np.sort(kmap.ravel()), np.arange(P * D))
+                assert np.array_equal(np.sort(vmap.ravel()), np.arange(P * D))
+
+
+def test_block_layout_shape_properties():
+    """The properties the layout exists for: a segment is one wave tile (64
+    e4m3 / 32 bf16 tokens) when the page holds it; each 16-byte load step of
+    a tile's K (the 64 lanes' chunks) is one contiguous kilobyte; a V row of
+    the segment is contiguous."""
+    from helpers import block_index_maps
+    for kv, TT, TG in ((oracle.KV_FP8, 64, 16), (oracle.KV_BF16, 32, 8)):
+        kmap, vmap = block_index_maps(kv, 128, 128)
+        e = 1 if kv == oracle.KV_FP8 else 2
+        KL = 128 * e // 64
+        for j in range(TG // 4):
+            for l in range(KL):
+                # lane (q, r) reads chunk q*KL + l of token TG*(r//4) + 4j + r%4
+                pos = sorted(int(kmap[TG * (r // 4) + 4 * j + r % 4, (q * KL + l) * 16 // e]) * e
+                             for q in range(4) for r in range(16))
+                assert pos == list(range(pos[0], pos[0] + 1024, 16))
+        assert np.array_equal(vmap[:TT, 5], vmap[0, 5] + np.arange(TT))
+        assert vmap[TT, 0] == 128 * TT  # the next segment starts after D rows
+
+
+def test_oracle_offsets_match_documented_layout():
+    from helpers import block_index_maps
+    g = np.random.default_rng(9)
+    for kv in (oracle.KV_FP8, oracle.KV_BF16):
+        for P, D, Hkv in ((16, 64, 3), (64, 128, 2), (256, 128, 1), (32, 64, 4)):
+            kmap, vmap = block_index_maps(kv, P, D)
+            for _ in range(200):
+                page, h = int(g.integers(0, 50)), int(g.integers(0, Hkv))
+                t, d = int(g.integers(0, P)), int(g.integers(0, D))
+                base = (page * Hkv + h) * P * D
+                assert oracle.k_offset(kv, page, h, t, d, Hkv, P, D) == base + kmap[t, d]
+                assert oracle.v_offset(kv, page, h, t, d, Hkv, P, D) == base + vmap[t, d]
+
+
 def test_pool_write_layout_and_codes():
-    """Tokens written through the oracle land at the documented offsets, as
+    """Tokens written through the oracle land at the documented positions, as
     torch's e4m3 encoding of f32(x)/scale."""
-    w = I.Workload("w", 2, 4, 2, 16, 8, 19, 30, pool_factor=2.0)
+    from helpers import kv_rows
+    w = I.Workload("w", 2, 4, 2, 64, 16, 19, 40, pool_factor=2.0)
     inp = I.make_decode_inputs(w, 3)
     pool = oracle_pool(inp, oracle.KV_FP8, poison=False)
+    enc = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     for b in range(2):
         L = int(inp.batch.context_lens[b])
-        for t in range(L):
-            page = inp.batch.page_table[b, t // w.page_size]
-            slot = t % w.page_size
-            x_k = I.bf16_bits_to_f32(inp.k_tokens[b][t]) / inp.k_scale[:, None]
-            x_v = I.bf16_bits_to_f32(inp.v_tokens[b][t]) / inp.v_scale[:, None]
-            enc = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-            assert np.array_equal(pool.k[page, :, slot, :], enc(x_k))
-            assert np.array_equal(pool.v[page, :, :, slot], enc(x_v))
-            # flat offsets follow the same formula
-            flat = pool.k.reshape(-1)
-            assert flat[oracle.k_offset(int(page), 1, slot, 3, w.kv_heads, w.page_size, w.head_dim)] == pool.k[page, 1, slot, 3]
-            flatv = pool.v.reshape(-1)
-            assert flatv[oracle.v_offset(int(page), 1, slot, 3, w.kv_heads, w.page_size, w.head_dim)] == pool.v[page, 1, 3, slot]
+        t = np.arange(L)
+        pages = inp.batch.page_table[b][t // w.page_size]
+        kc, vc = kv_rows(pool, pages, t % w.page_size)
+        x_k = I.bf16_bits_to_f32(inp.k_tokens[b]) / inp.k_scale[None, :, None]
+        x_v = I.bf16_bits_to_f32(inp.v_tokens[b]) / inp.v_scale[None, :, None]
+        assert np.array_equal(kc, enc(x_k))
+        assert np.array_equal(vc, enc(x_v))
 
 
 def test_append_equals_bulk_write_of_last_token():
-    w = I.Workload("w", 3, 4, 2, 16, 8, 5, 40, pool_factor=2.0)
+    w = I.Workload("w", 3, 4, 2, 64, 16, 5, 40, pool_factor=2.0)
     inp = I.make_decode_inputs(w, 4)
     a = oracle_pool(inp, oracle.KV_FP8, poison=False, append=True)
     b = oracle_pool(inp, oracle.KV_FP8, poison=False, append=False)
@@ -152,7 +192,7 @@ def test_append_equals_bulk_write_of_last_token():
 
 
 def test_append_skips_aborted_and_invalid():
-    w = I.Workload("w", 3, 4, 2, 16, 8, 20, 20, pool_factor=2.0)
+    w = I.Workload("w", 3, 4, 2, 64, 16, 20, 20, pool_factor=2.0)
     inp = I.make_decode_inputs(w, 5)
     base = oracle_pool(inp, oracle.KV_FP8, poison=False, append=False)
     k0, v0 = base.k.copy(), base.v.copy()
@@ -162,19 +202,21 @@ def test_append_skips_aborted_and_invalid():
                      inp.v_scale, status=np.array([0, 1, 0], np.int32))
     changed = np.argwhere(base.k != k0)
     pages_changed = set(int(p) for p in changed[:, 0])
-    assert pages_changed == {int(inp.batch.page_table[0, 19 // 8])}
+    assert pages_changed == {int(inp.batch.page_table[0, 19 // 16])}
     assert (base.v != v0).any()
 
 
 def test_bf16_append_copies_bits():
-    w = I.Workload("w", 2, 2, 2, 8, 16, 3, 9, pool_factor=2.0)
+    from helpers import kv_rows
+    w = I.Workload("w", 2, 2, 2, 64, 16, 3, 9, pool_factor=2.0)
     inp = I.make_decode_inputs(w, 6)
     pool = oracle_pool(inp, oracle.KV_BF16, poison=False)
     for b in range(2):
         t = int(inp.batch.context_lens[b]) - 1
         page, slot = inp.batch.page_table[b, t // 16], t % 16
-        assert np.array_equal(pool.k[page, :, slot, :], inp.k_new()[b])
-        assert np.array_equal(pool.v[page, :, :, slot], inp.v_new()[b])
+        kc, vc = kv_rows(pool, [page], [slot])
+        assert np.array_equal(kc[0], inp.k_new()[b])
+        assert np.array_equal(vc[0], inp.v_new()[b])
 
 
 # --- capacity invariants ---------------------------------------------------------
