@@ -17,8 +17,12 @@ request through one attention layer per step).  roofline.achieved is the
 algorithmic bytes of one attention launch divided by its mean duration,
 measured with HIP events on the launch stream over the timed steps.  The
 bf16 twin (32 requests: the same KV bytes) and the tag-check overhead against
-the no-op tracker are reported beside it; cpu_baseline times the CPU oracle
-on a bounded sample of the same batch.
+the no-op tracker are reported beside it, and so is the long-context point
+(4 requests of 262,144 tokens in 64 splits: check overhead, and the batch
+with one stale request).  --sweep adds the 1/8/16/32/64 concurrency points,
+each step preceded by a 1 GiB read of other memory so that no point runs
+out of the MALL.  cpu_baseline times the CPU oracle on a bounded sample
+of the same batch.
 """
 from __future__ import annotations
 
@@ -40,6 +44,7 @@ PEAK_HBM_GBS = 8000.0
 COUNTERS_SUMMARY = os.path.join(ROOT, "profiles", "decode_attn_e4m3_gqa8_16k_b64_counters.md")
 ATTN_KERNEL = "decode_attn_mfma_kernel<false, 128"
 COPY_BYTES = 1 << 30
+FLUSH_BYTES = 1 << 30
 SEED = 1003
 METRIC = "decode attention tokens/s and achieved HBM GB/s (% of peak), FP8 vs BF16 KV"
 
@@ -59,7 +64,7 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the bf16 twin and the check-overhead measurement")
+                    help="skip the bf16 twin, the check overhead and the long-context point")
     ap.add_argument("--sweep", action="store_true",
                     help="also run the 1/8/16/32/64 concurrency sweep (both dtypes)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -94,14 +99,14 @@ def algorithmic_bytes(lens, Hq, Hkv, D, P, kv_elem_bytes, checked=True):
 class Point:
     """One decode step's device state for a batch size and pool type."""
 
-    def __init__(self, batch, kv_dtype, device, seed=SEED):
+    def __init__(self, batch, kv_dtype, device, seed=SEED, workload=None):
         from paged_attention_fp8_amd import harness as H
         from paged_attention_fp8_amd import inputs as I
         from paged_attention_fp8_amd import ops
         self.ops, self.H = ops, H
         self.kv_dtype = kv_dtype
         elem = 1 if kv_dtype == ops.KV_FP8_E4M3 else 2
-        self.w = I.sweep_workload(batch, elem)
+        self.w = workload if workload is not None else I.sweep_workload(batch, elem)
         log(f"drawing {self.w.name} ({'e4m3' if kv_dtype == ops.KV_FP8_E4M3 else 'bf16'})")
         self.inp = I.make_device_decode_inputs(self.w, seed, device)
         self.step = H.build_step(self.inp, kv_dtype, device, poison=False)
@@ -109,9 +114,16 @@ class Point:
         self.sm = 1.0 / math.sqrt(self.w.head_dim)
         B, Hq, D = batch, self.w.q_heads, self.w.head_dim
         self.lens = self.inp.batch.context_lens
-        self.bytes = algorithmic_bytes(self.lens, Hq, self.w.kv_heads, D, self.w.page_size, elem)
+        # requests the tag check aborts read no pages: their K/V is not moved
+        live = [0 if b in self.inp.stale else int(L) for b, L in enumerate(self.lens)]
+        self.bytes = algorithmic_bytes(live, Hq, self.w.kv_heads, D, self.w.page_size, elem)
 
-    def run(self, steps, warmup, splits, check=True, events=True):
+    def run(self, steps, warmup, splits, check=True, events=True, flush=False):
+        """Time `steps` decode steps.  flush: before every step, read
+        FLUSH_BYTES of other device memory so that no step finds the previous
+        one's KV bytes in the last-level caches (the 256 MB MALL holds a
+        whole batch of up to 8 requests); step times then come from HIP
+        events around each step instead of the wall clock."""
         import torch
         ops, H, st = self.ops, self.H, self.step
         B, Hq, D = st.batch.batch, self.w.q_heads, self.w.head_dim
@@ -126,8 +138,15 @@ class Point:
         ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        junk = (torch.zeros(FLUSH_BYTES // 8, dtype=torch.int64, device=dev) if flush else None)
 
         def one(i=None):
+            if junk is not None:
+                junk.max()  # reads only: leaves no dirty lines to write back
+            if i is not None and flush:
+                sev[i][0].record()
             stat = None
             if check:
                 stat = ops.page_tag_check(st.batch, self.w.page_size, st.page_tags,
@@ -139,6 +158,8 @@ class Point:
             ops.paged_decode_attn(st.cache, b, st.q, self.sm, S, ws, out, lse)
             if i is not None and events:
                 ev[i][1].record()
+            if i is not None and flush:
+                sev[i][1].record()
 
         for _ in range(warmup):
             one()
@@ -149,7 +170,9 @@ class Point:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         attn_ms = [a.elapsed_time(b) for a, b in ev] if events else []
-        return {"splits": S, "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
+        ms = (statistics.mean(a.elapsed_time(b) for a, b in sev) if flush
+              else 1e3 * wall / steps)
+        return {"splits": S, "wall_s": wall, "ms_per_step": ms,
                 "attn_ms": attn_ms, "out": out, "lse": lse, "status": status}
 
 
@@ -194,6 +217,49 @@ def cpu_baseline(point, target_s):
     return {"value": n / t, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"first {n} of {len(lens)} requests of the same batch (all 64 heads, "
                       f"16384 tokens each), fp64 oracle, one call, {t:.1f} s"}
+
+
+def long_context(args, dev):
+    """4 requests of 262,144 tokens in 64 splits: the tag check's overhead on
+    the clean batch (against the no-op tracker), and the batch with one
+    stale request, which the check must abort while the others run."""
+    import torch
+    from paged_attention_fp8_amd import inputs as I
+    from paged_attention_fp8_amd import ops
+    w = I.WORKLOADS["gqa8_256k_b4"]
+    pc = Point(w.batch, ops.KV_FP8_E4M3, dev, workload=I.scaled(w, stale_requests=0))
+    rc = pc.run(args.steps, args.warmup, w.num_splits, check=True, flush=True)
+    rn = pc.run(args.steps, args.warmup, w.num_splits, check=False, flush=True)
+    clean_ms = statistics.mean(rc["attn_ms"])
+    rd = pc.run(args.steps, args.warmup, 0, check=True, flush=True)
+    dms = statistics.mean(rd["attn_ms"])
+    res = {
+        "workload": "gqa8_256k_b4: 4 requests x 262144 tokens, 64 query / 8 KV heads, head_dim 128, "
+                    "64-token pages, 64 splits",
+        "ms_per_step_checked": rc["ms_per_step"],
+        "ms_per_step_no_tracker": rn["ms_per_step"],
+        "check_overhead_pct": 100.0 * (rc["ms_per_step"] - rn["ms_per_step"]) / rn["ms_per_step"],
+        "attn_us": 1e3 * clean_ms,
+        "attn_GBps": pc.bytes / (clean_ms * 1e-3) / 1e9,
+        "attn_frac": pc.bytes / (clean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "default_splits": rd["splits"],
+        "default_splits_attn_us": 1e3 * dms,
+        "default_splits_attn_frac": pc.bytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+    del pc, rc, rn, rd
+    torch.cuda.empty_cache()
+    ps = Point(w.batch, ops.KV_FP8_E4M3, dev, workload=w)
+    rs = ps.run(args.steps, args.warmup, w.num_splits, check=True, flush=True)
+    flagged = [int(b) for b in torch.nonzero(rs["status"]).flatten().tolist()]
+    if flagged != sorted(ps.inp.stale):
+        raise SystemExit(f"long context: tag check flagged {flagged}, stale {ps.inp.stale}")
+    ms = statistics.mean(rs["attn_ms"])
+    res["stale_requests"] = flagged
+    res["stale_ms_per_step"] = rs["ms_per_step"]
+    res["stale_attn_GBps_live"] = ps.bytes / (ms * 1e-3) / 1e9
+    del ps, rs
+    torch.cuda.empty_cache()
+    return res
 
 
 def _pmc_values(directory, counter, kernel_substr):
@@ -366,6 +432,7 @@ def main():
         }
         del q
         torch.cuda.empty_cache()
+        result["long_context"] = long_context(args, dev)
     if args.sweep:
         sweep = []
         for kv_dtype, name in ((ops.KV_FP8_E4M3, "fp8"), (ops.KV_BF16, "bf16")):
@@ -374,10 +441,13 @@ def main():
                     sweep.append({"dtype": name, "batch": b, "result": "out of pool memory"})
                     continue
                 pt = Point(b, kv_dtype, dev)
-                rr = pt.run(args.steps, args.warmup, 0)
+                rr = pt.run(args.steps, args.warmup, 0, flush=True)
                 ms = statistics.mean(rr["attn_ms"])
                 sweep.append({"dtype": name, "batch": b, "tokens_per_s": b / (rr["ms_per_step"] * 1e-3),
-                              "attn_GBps": pt.bytes / (ms * 1e-3) / 1e9, "splits": rr["splits"]})
+                              "ms_per_step": rr["ms_per_step"], "attn_us": 1e3 * ms,
+                              "attn_GBps": pt.bytes / (ms * 1e-3) / 1e9,
+                              "attn_frac": pt.bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                              "splits": rr["splits"]})
                 del pt
                 torch.cuda.empty_cache()
         result["sweep"] = sweep

@@ -177,7 +177,7 @@ pafp8_status kv_quant_fill(const pafp8_cache *cache, const pafp8_batch *batch,
  * splitk_combine merges them.  pafp8_decode_workspace_bytes gives the
  * workspace size (0 when S == 1); pafp8_default_num_splits picks S so that
  * batch * num_kv_heads * S is about one work-group per CU, with splits of at
- * least 512 tokens (num_cus <= 0: query the current device).  Pure host
+ * least 1024 tokens (num_cus <= 0: query the current device).  Pure host
  * functions.
  * ------------------------------------------------------------------------- */
 size_t pafp8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,

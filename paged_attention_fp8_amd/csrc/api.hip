@@ -311,13 +311,14 @@ int32_t pafp8_default_num_splits(int32_t batch, int32_t num_kv_heads, int32_t ma
         return 1;
     if (num_cus <= 0)
         num_cus = device_cu_count();
-    // about one work-group per CU (measured best from 1 to 64 requests of 16k
-    // tokens on MI355X: more, shorter splits add combine traffic and per-split
-    // start-up), without splits shorter than 512 tokens
+    // about one work-group per CU (measured best from 4 to 64 requests of
+    // 16k-256k tokens on MI355X: more, shorter splits add combine traffic and
+    // per-split start-up), without splits shorter than 1024 tokens (one
+    // request of 16k tokens: 16 splits took 16 us, 32 splits 20 us)
     const int64_t units = static_cast<int64_t>(batch) * num_kv_heads;
     int64_t S = (num_cus + units - 1) / units;
     const int64_t tokens = static_cast<int64_t>(max_pages_per_req) * page_size;
-    int64_t s_max = tokens / 512;
+    int64_t s_max = tokens / 1024;
     if (s_max < 1)
         s_max = 1;
     if (S > s_max)

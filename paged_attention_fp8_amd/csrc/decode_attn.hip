@@ -709,9 +709,9 @@ __global__ __launch_bounds__(kThreads) void decode_attn_vec_kernel(AttnParams p)
 }
 
 // ===========================================================================
-// split-K combine: one work-group per (request, query head).  Threads split
-// the head dims four at a time and the splits among themselves; partial
-// sums meet in LDS.
+// split-K combine, any head dim (a multiple of 4 up to 1024): one work-group
+// per (request, query head).  Threads split the head dims four at a time and
+// the splits among themselves; partial sums meet in LDS.
 // ===========================================================================
 __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max)
 {
@@ -787,6 +787,86 @@ __global__ __launch_bounds__(kThreads) void splitk_combine_kernel(
         lse_out[bh] = LSE;
 }
 
+// Wave-per-head combine for the attention's own head dims: one wave owns a
+// (request, query head); lane (g, c) handles float4 column c of the splits
+// k = g (mod 64 / (D/4)).  The first PF partial rows of every lane are
+// loaded together with the split LSEs, so the whole reduction costs one
+// memory round trip when S * D <= 64 * 4 * PF.
+template <int D>
+__global__ __launch_bounds__(kThreads) void splitk_combine_wave_kernel(
+    const float *__restrict__ part_o, const float *__restrict__ part_lse, int BH, int Hq, int S,
+    const int32_t *__restrict__ req_status, float *__restrict__ out, float *__restrict__ lse_out)
+{
+    constexpr int NC = D / 4;    // float4 columns of a row
+    constexpr int NG = 64 / NC;  // split groups in a wave
+    constexpr int PF = 8;        // partial rows per lane loaded up front
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * kWaves + uniform(threadIdx.x >> 6);
+    if (bh >= BH)
+        return;
+    const int col = lane % NC, grp = lane / NC;
+    const float *pl = part_lse + static_cast<int64_t>(bh) * S;
+    const float *po = part_o + static_cast<int64_t>(bh) * S * D + col * 4;
+    f32x4 pre[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        const int k = grp + i * NG;
+        pre[i] = k < S ? *reinterpret_cast<const f32x4 *>(po + static_cast<int64_t>(k) * D)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float l0 = lane < S ? pl[lane] : kNegInf;
+    const bool aborted = req_status != nullptr && req_status[bh / Hq] != 0;
+    float M = l0;
+    bool nan = l0 != l0;
+    for (int k = lane + 64; k < S; k += 64) {
+        const float v = pl[k];
+        nan |= v != v;
+        M = __builtin_fmaxf(M, v);
+    }
+    M = wave_max(M);
+    const bool has_nan = __builtin_amdgcn_ballot_w64(nan) != 0;
+    float *o = out + static_cast<int64_t>(bh) * D;
+    if (aborted || has_nan || M == kNegInf) {
+        const float fill = (has_nan && !aborted) ? __builtin_nanf("") : 0.f;
+        if (grp == 0)
+            *reinterpret_cast<f32x4 *>(o + col * 4) = f32x4{fill, fill, fill, fill};
+        if (lane == 0 && lse_out != nullptr)
+            lse_out[bh] = (has_nan && !aborted) ? fill : kNegInf;
+        return;
+    }
+    float sum = lane < S ? __expf(l0 - M) : 0.f;
+    for (int k = lane + 64; k < S; k += 64)
+        sum += __expf(pl[k] - M);
+    sum = wave_sum(sum);
+    const float LSE = M + __logf(sum);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        const int k = grp + i * NG;
+        const float from_lane = __shfl(l0, k & 63, 64);  // every lane takes part
+        if (k < S) {
+            const float lk = S <= 64 ? from_lane : pl[k];
+            if (lk != kNegInf)  // empty split: contributes nothing
+                acc += __expf(lk - LSE) * pre[i];
+        }
+    }
+    for (int k = grp + PF * NG; k < S; k += NG) {
+        const float lk = pl[k];
+        if (lk != kNegInf)
+            acc += __expf(lk - LSE) * *reinterpret_cast<const f32x4 *>(po + static_cast<int64_t>(k) * D);
+    }
+#pragma unroll
+    for (int m = NC; m < 64; m <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc[e] += shfl_xor_f(acc[e], m);
+    }
+    if (grp == 0)
+        *reinterpret_cast<f32x4 *>(o + col * 4) = acc;
+    if (lane == 0 && lse_out != nullptr)
+        lse_out[bh] = LSE;
+}
+
 template <bool BF16, int D>
 hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
 {
@@ -823,6 +903,18 @@ hipError_t launch_splitk_combine(const float *part_o, const float *part_lse, int
     const int64_t bh = static_cast<int64_t>(batch) * num_q_heads;
     if (bh > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
+    if (head_dim == 64 || head_dim == 128) {
+        const unsigned blocks = static_cast<unsigned>((bh + kWaves - 1) / kWaves);
+        if (head_dim == 64)
+            hipLaunchKernelGGL(splitk_combine_wave_kernel<64>, dim3(blocks), dim3(kThreads), 0, stream,
+                               part_o, part_lse, static_cast<int>(bh), num_q_heads, num_splits,
+                               req_status, out, lse);
+        else
+            hipLaunchKernelGGL(splitk_combine_wave_kernel<128>, dim3(blocks), dim3(kThreads), 0, stream,
+                               part_o, part_lse, static_cast<int>(bh), num_q_heads, num_splits,
+                               req_status, out, lse);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(splitk_combine_kernel, dim3(static_cast<unsigned>(bh)), dim3(kThreads), 0,
                        stream, part_o, part_lse, num_q_heads, num_splits, head_dim, req_status, out,
                        lse);

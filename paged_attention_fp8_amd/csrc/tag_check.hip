@@ -19,6 +19,7 @@ constexpr int kTagMismatch = 1;
 constexpr int kPageOob = 2;
 constexpr int kBadLen = 4;
 constexpr int kThreads = 256;
+constexpr int kChunk = 16;  // page-table entries per thread per pass
 
 __global__ __launch_bounds__(kThreads) void tag_check_kernel(
     int max_pages, int page_size, const int32_t *__restrict__ page_table,
@@ -33,12 +34,33 @@ __global__ __launch_bounds__(kThreads) void tag_check_kernel(
         const int n = static_cast<int>((static_cast<int64_t>(L) + page_size - 1) / page_size);
         const int32_t *row = page_table + static_cast<int64_t>(b) * max_pages;
         const uint32_t *exp_row = expected_tags + static_cast<int64_t>(b) * max_pages;
-        for (int i = threadIdx.x; i < n; i += kThreads) {
-            const int32_t page = row[i];
-            if (page < 0 || page >= num_pages)
-                flags |= kPageOob;
-            else if (page_tags[page] != exp_row[i])
-                flags |= kTagMismatch;
+        // kChunk entries per thread per pass, every load issued before any
+        // compare: a long request costs two memory round trips per pass
+        // instead of two per 256 entries.  Indices past n read entry n - 1
+        // again (n >= 1) and are not judged.
+        for (int base = 0; base < n; base += kThreads * kChunk) {
+            int32_t page[kChunk];
+            uint32_t want[kChunk], have[kChunk];
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) {
+                const int i = min(base + j * kThreads + static_cast<int>(threadIdx.x), n - 1);
+                page[j] = row[i];
+                want[j] = exp_row[i];
+            }
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) {
+                const bool in_pool = page[j] >= 0 && page[j] < num_pages;
+                have[j] = in_pool ? page_tags[page[j]] : 0u;  // the pool may be empty
+            }
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) {
+                if (base + j * kThreads + static_cast<int>(threadIdx.x) >= n)
+                    continue;
+                if (page[j] < 0 || page[j] >= num_pages)
+                    flags |= kPageOob;
+                else if (have[j] != want[j])
+                    flags |= kTagMismatch;
+            }
         }
     }
     const int any_tag = __syncthreads_or(flags & kTagMismatch);

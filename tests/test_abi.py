@@ -79,10 +79,11 @@ def test_default_split_choice(L):
     assert L.pafp8_default_num_splits(16, 8, 256, 64, 256) == 2
     assert L.pafp8_default_num_splits(8, 8, 256, 64, 256) == 4
     assert L.pafp8_default_num_splits(4, 8, 4096, 64, 256) == 8
-    # no split shorter than 512 tokens
-    assert L.pafp8_default_num_splits(1, 8, 256, 64, 256) == 32
+    # no split shorter than 1024 tokens
+    assert L.pafp8_default_num_splits(1, 8, 256, 64, 256) == 16
     assert L.pafp8_default_num_splits(1, 4, 16, 16, 256) == 1
-    assert L.pafp8_default_num_splits(2, 8, 64, 16, 256) == 2
+    assert L.pafp8_default_num_splits(2, 8, 64, 16, 256) == 1
+    assert L.pafp8_default_num_splits(2, 8, 128, 16, 256) == 2
 
 
 def _cache(**kw):

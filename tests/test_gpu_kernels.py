@@ -203,7 +203,7 @@ def test_append_skips_aborted_and_invalid_lengths():
 
 # --- combine --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("S,D", [(1, 128), (7, 64), (64, 128), (130, 128)])
+@pytest.mark.parametrize("S,D", [(1, 128), (7, 64), (17, 64), (64, 128), (130, 128), (5, 96), (70, 256)])
 def test_combine_matches_oracle(S, D):
     say(f"combine: S={S} D={D}")
     g = np.random.default_rng(S * 1000 + D)
