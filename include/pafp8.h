@@ -159,7 +159,8 @@ pafp8_status kv_quant_append(const pafp8_cache *cache, const pafp8_batch *batch,
  * position token_start[b] + j, encoded as in kv_quant_append.
  *   token_start, token_count  device int32 [B]
  *   src_tokens                T, the row count of the source arrays (>= 1)
- *   k_src, v_src              device bf16 [B][T][num_kv_heads][head_dim]
+ *   k_src, v_src              device bf16 [B][T][num_kv_heads][head_dim],
+ *                             16-byte aligned
  * Requires token_count[b] <= T (larger counts are clipped to T).  Positions
  * outside [0, max_pages_per_req * page_size), page ids outside the pool and
  * requests with a non-zero batch->req_status are skipped.  context_lens is

@@ -228,6 +228,8 @@ pafp8_status write_impl(const pafp8_cache *cache, const pafp8_batch *batch, bool
             return fail(PAFP8_EINVAL, "token_start or token_count is NULL");
         if (T < 1)
             return fail(PAFP8_EINVAL, "src_tokens = %d < 1", T);
+        if (!aligned16(k_src) || !aligned16(v_src))
+            return fail(PAFP8_EINVAL, "k_src and v_src must be 16-byte aligned");
     }
     pafp8::WriteParams p{};
     p.k_pool = static_cast<uint8_t *>(cache->k_pool);

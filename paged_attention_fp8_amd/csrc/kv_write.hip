@@ -8,12 +8,14 @@
 // context_lens[b] - 1) and the prefill-to-decode hand-off (a block of tokens
 // per request).
 //
-// Work split: one work-group per (request, KV head, 16 consecutive positions).
-// Positions are grouped on 16-aligned boundaries so that a group never spans
-// two pages (pages hold a multiple of 16 tokens).  Thread d owns one head
-// dimension: its K codes land in the 16-byte chunks of the block layout
-// (consecutive threads fill a chunk), its V codes form one contiguous run of
-// 16 slots of a V row and leave as a single 16-byte store (two for bf16).
+// Append (one token per request): one work-group per (request, KV head),
+// thread d owning head dimension d.
+//
+// Fill (a block of tokens per request): one work-group per (request, KV head,
+// aligned segment of the block layout).  The segment's K and V source rows
+// are staged in LDS by coalesced 16-byte loads; K then leaves in the order of
+// the block layout (a wave stores 1 KiB of consecutive chunks) and V as
+// 16-byte runs of one head dim, read down an LDS column.
 #include "pafp8_device.hpp"
 #include "pafp8_internal.hpp"
 
@@ -21,107 +23,200 @@ namespace pafp8 {
 namespace {
 
 template <bool BF16, int D>
-__global__ __launch_bounds__(D) void kv_write_kernel(WriteParams p, int groups_per_req)
+__global__ __launch_bounds__(D) void kv_append_kernel(WriteParams p)
 {
-    const int k = blockIdx.x % groups_per_req;
-    const int bg = blockIdx.x / groups_per_req;
-    const int g = bg % p.num_kv_heads;
-    const int b = bg / p.num_kv_heads;
+    const int g = blockIdx.x % p.num_kv_heads;
+    const int b = blockIdx.x / p.num_kv_heads;
     const int d = threadIdx.x;
-    const int P = 1 << p.log2_page;
     const int64_t cap = static_cast<int64_t>(p.max_pages) << p.log2_page;
 
     if (p.req_status != nullptr && p.req_status[b] != 0)
         return;
-    int64_t start, count;
-    int T;
-    if (p.context_lens != nullptr) {
-        const int32_t L = p.context_lens[b];
-        if (L < 1 || L > cap)
-            return;
-        start = L - 1;
-        count = 1;
-        T = 1;
+    const int32_t L = p.context_lens[b];
+    if (L < 1 || L > cap)
+        return;
+    const int64_t pos = L - 1;
+    const int32_t page = p.page_table[static_cast<int64_t>(b) * p.max_pages + (pos >> p.log2_page)];
+    if (page < 0 || page >= p.num_pages)
+        return;
+    constexpr int E = BF16 ? 2 : 1;
+    constexpr int LOG2_TG = BF16 ? 3 : 4, KL = D * E / 64;
+    const int slot = static_cast<int>(pos & ((int64_t{1} << p.log2_page) - 1));
+    const int64_t head_block = (static_cast<int64_t>(page) * p.num_kv_heads + g) << p.log2_page;
+    // Block layout (include/pafp8.h): segments of SEG = min(P, 64/E) slots.
+    // K: slot TG*sub + 4j + a of a segment (TG = 16/E) keeps its 16-byte
+    // chunk q*KL + l at chunk ((j*KL + l)*4 + q)*(4*NS) + 4*sub + a, NS =
+    // SEG/TG; thread d's element is byte (d*E) % 16 of chunk d*E/16.  V: a
+    // segment is [D][SEG].
+    const int log2_seg = p.log2_page < (BF16 ? 5 : 6) ? p.log2_page : (BF16 ? 5 : 6);
+    const int log2_ns = log2_seg - LOG2_TG;
+    const int seg = slot >> log2_seg, u = slot & ((1 << log2_seg) - 1);
+    const int w = u & ((1 << LOG2_TG) - 1);
+    const int c = d * E / 16;
+    const int kq = c / KL, kl = c % KL;
+    uint8_t *kdst = p.k_pool + (head_block * D + (static_cast<int64_t>(seg) * D << log2_seg)) * E +
+                    (((((w >> 2) * KL + kl) * 4 + kq) << (2 + log2_ns)) + ((u >> LOG2_TG) << 2) + (w & 3)) * 16 +
+                    (d * E) % 16;
+    uint8_t *vdst = p.v_pool + (head_block * D + ((static_cast<int64_t>(seg) * D + d) << log2_seg) + u) * E;
+    const int64_t src = (static_cast<int64_t>(b) * p.num_kv_heads + g) * D + d;
+    const uint16_t kx = p.k_src[src];
+    const uint16_t vx = p.v_src[src];
+    if (BF16) {
+        *reinterpret_cast<uint16_t *>(kdst) = kx;
+        *reinterpret_cast<uint16_t *>(vdst) = vx;
     } else {
-        T = p.src_tokens;
-        start = p.token_start[b];
-        count = p.token_count[b];
-        if (count > T)
-            count = T;
-        if (count <= 0)
-            return;
+        *kdst = static_cast<uint8_t>(quantize_bf16(kx, p.k_scale[g]));
+        *vdst = static_cast<uint8_t>(quantize_bf16(vx, p.v_scale[g]));
     }
-    const int64_t g0 = ((start >> 4) + k) << 4;
-    int64_t lo = g0 > start ? g0 : start;
+}
+
+constexpr int kFillThreads = 256;
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(kFillThreads) void kv_fill_kernel(WriteParams p, int segs_per_req)
+{
+    constexpr int E = BF16 ? 2 : 1;
+    constexpr int LOG2_MAXSEG = BF16 ? 5 : 6;   // 64 bytes per element column
+    constexpr int MAXSEG = 1 << LOG2_MAXSEG;
+    constexpr int LOG2_TG = BF16 ? 3 : 4;       // tokens per K token group (16 / E)
+    constexpr int R = D * E / 16;               // 16-byte chunks per K row
+    constexpr int KL = R / 4;
+    constexpr int TR = 16 / E;                  // tokens per 16-byte V run
+    constexpr int RS = D + 8;                   // LDS row stride (bf16), 16 bytes of padding
+    __shared__ __align__(16) uint16_t kt[MAXSEG * RS];
+    __shared__ __align__(16) uint16_t vt[MAXSEG * RS];
+
+    const int k = blockIdx.x % segs_per_req;
+    const int bg = blockIdx.x / segs_per_req;
+    const int g = bg % p.num_kv_heads;
+    const int b = bg / p.num_kv_heads;
+    const int tid = threadIdx.x;
+    if (p.req_status != nullptr && p.req_status[b] != 0)
+        return;
+    const int T = p.src_tokens;
+    const int64_t start = p.token_start[b];
+    int64_t count = p.token_count[b];
+    if (count > T)
+        count = T;
+    if (count <= 0)
+        return;
+    const int log2_seg = p.log2_page < LOG2_MAXSEG ? p.log2_page : LOG2_MAXSEG;
+    const int SEG = 1 << log2_seg;
+    const int64_t cap = static_cast<int64_t>(p.max_pages) << p.log2_page;
+    const int64_t pos0 = ((start >> log2_seg) + k) << log2_seg;  // first position of the segment
+    int64_t lo = pos0 > start ? pos0 : start;
     if (lo < 0)
         lo = 0;
-    int64_t hi = g0 + 16;
+    int64_t hi = pos0 + SEG;
     if (hi > start + count)
         hi = start + count;
     if (hi > cap)
         hi = cap;
     if (lo >= hi)
         return;
-
-    const int32_t page = p.page_table[static_cast<int64_t>(b) * p.max_pages + (g0 >> p.log2_page)];
+    const int32_t page = p.page_table[static_cast<int64_t>(b) * p.max_pages + (pos0 >> p.log2_page)];
     if (page < 0 || page >= p.num_pages)
         return;
-    const int slot0 = static_cast<int>(g0 & (P - 1));
-    constexpr int E = BF16 ? 2 : 1;
-    const int64_t head_block = (static_cast<int64_t>(page) * p.num_kv_heads + g) * P * D;
-    // Block layout (include/pafp8.h): segments of SEG = min(P, 64/E) tokens.
-    // K: token TG*sub + 4j + a of a segment (TG = 16/E) keeps its 16-byte
-    // chunk q*KL + l at chunk ((j*KL + l)*4 + q)*(4*NS) + 4*sub + a, NS =
-    // SEG/TG; thread d's element is byte (d*E) % 16 of chunk d*E/16.  V: a
-    // segment is [D][SEG]; the 16 aligned positions of this work-group lie in
-    // one segment, so thread d's 16 V codes are contiguous.
-    constexpr int LOG2_TG = BF16 ? 3 : 4, KL = D * E / 64;
-    const int log2_seg = p.log2_page < (BF16 ? 5 : 6) ? p.log2_page : (BF16 ? 5 : 6);
-    const int log2_ns = log2_seg - LOG2_TG;
-    const int c = d * E / 16;
-    const int kq = c / KL, kl = c % KL;
-    uint8_t *kblock = p.k_pool + head_block * E + (d * E) % 16;
-    const int seg0 = slot0 >> log2_seg, u0 = slot0 & ((1 << log2_seg) - 1);
-    uint8_t *vdst = p.v_pool + (head_block + ((static_cast<int64_t>(seg0) * D + d) << log2_seg) + u0) * E;
-    const float ks = BF16 ? 1.0f : p.k_scale[g];
-    const float vs = BF16 ? 1.0f : p.v_scale[g];
-    const int64_t src_stride = static_cast<int64_t>(p.num_kv_heads) * D;  // per token
-    const uint16_t *ksrc = p.k_src + (static_cast<int64_t>(b) * T * p.num_kv_heads + g) * D + d;
-    const uint16_t *vsrc = p.v_src + (static_cast<int64_t>(b) * T * p.num_kv_heads + g) * D + d;
+    const int u_lo = static_cast<int>(lo - pos0), u_hi = static_cast<int>(hi - pos0);
+    const int seg = static_cast<int>(pos0 & ((int64_t{1} << p.log2_page) - 1)) >> log2_seg;
+    const int64_t seg_elem = (((static_cast<int64_t>(page) * p.num_kv_heads + g) << p.log2_page) +
+                              (static_cast<int64_t>(seg) << log2_seg)) * D;
+    uint8_t *kseg = p.k_pool + seg_elem * E;
+    uint8_t *vseg = p.v_pool + seg_elem * E;
 
-    constexpr int NV = BF16 ? 8 : 4;  // dwords holding the 16 V slots
-    uint32_t vword[NV] = {};
+    // stage the segment's source rows (zeros outside [lo, hi)); every load
+    // of a thread is issued before the first LDS store
+    const int64_t row_stride = static_cast<int64_t>(p.num_kv_heads) * D;
+    const int64_t src0 = (static_cast<int64_t>(b) * T * p.num_kv_heads + g) * D;
+    constexpr int NLD = (MAXSEG * D / 8 + kFillThreads - 1) / kFillThreads;
+    u32x4 kx[NLD], vx[NLD];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int64_t pos = g0 + i;
-        if (pos < lo || pos >= hi)
-            continue;
-        const int64_t j = pos - start;
-        const uint16_t kx = ksrc[j * src_stride];
-        const uint16_t vx = vsrc[j * src_stride];
-        // token i of this 16-position group: segment-relative token u
-        const int u = u0 + i;
-        const int w = u & ((1 << LOG2_TG) - 1);
-        uint8_t *kdst = kblock + seg0 * ((D * E) << log2_seg) +
-                        (((((w >> 2) * KL + kl) * 4 + kq) << (2 + log2_ns)) + ((u >> LOG2_TG) << 2) + (w & 3)) * 16;
-        if (BF16) {
-            *reinterpret_cast<uint16_t *>(kdst) = kx;
-            vword[i >> 1] |= static_cast<uint32_t>(vx) << (16 * (i & 1));
-        } else {
-            *kdst = static_cast<uint8_t>(quantize_bf16(kx, ks));
-            vword[i >> 2] |= quantize_bf16(vx, vs) << (8 * (i & 3));
+    for (int i = 0; i < NLD; ++i) {
+        const int idx = tid + i * kFillThreads;
+        const int u = idx / (D / 8), c8 = idx % (D / 8);
+        kx[i] = vx[i] = u32x4{0u, 0u, 0u, 0u};
+        if (u >= u_lo && u < u_hi) {
+            const int64_t off = src0 + (pos0 + u - start) * row_stride + c8 * 8;
+            kx[i] = load16(p.k_src + off);
+            vx[i] = load16(p.v_src + off);
         }
     }
-    if (lo == g0 && hi == g0 + 16) {
 #pragma unroll
-        for (int w = 0; w < NV; w += 4)
-            store16(vdst + 4 * w, u32x4{vword[w], vword[w + 1], vword[w + 2], vword[w + 3]});
-    } else {
-        for (int i = static_cast<int>(lo - g0); i < static_cast<int>(hi - g0); ++i) {
-            if (BF16)
-                reinterpret_cast<uint16_t *>(vdst)[i] = static_cast<uint16_t>(vword[i >> 1] >> (16 * (i & 1)));
-            else
-                vdst[i] = static_cast<uint8_t>(vword[i >> 2] >> (8 * (i & 3)));
+    for (int i = 0; i < NLD; ++i) {
+        const int idx = tid + i * kFillThreads;
+        const int u = idx / (D / 8), c8 = idx % (D / 8);
+        if (u < SEG) {
+            *reinterpret_cast<u32x4 *>(&kt[u * RS + c8 * 8]) = kx[i];
+            *reinterpret_cast<u32x4 *>(&vt[u * RS + c8 * 8]) = vx[i];
+        }
+    }
+    __syncthreads();
+
+    const float ks = BF16 ? 1.0f : p.k_scale[g];
+    const float vs = BF16 ? 1.0f : p.v_scale[g];
+    // K: this thread's chunk positions cp, in storage order; chunk cp holds
+    // chunk c = q*KL + l of slot u = TG*s + 4j + a
+    const int log2_ns = log2_seg - LOG2_TG;
+    constexpr int NK = (MAXSEG * R + kFillThreads - 1) / kFillThreads;
+#pragma unroll
+    for (int it = 0; it < NK; ++it) {
+        const int cp = tid + it * kFillThreads;
+        if (cp >= SEG * R)
+            break;
+        const int a = cp & 3;
+        const int s_ = (cp >> 2) & ((1 << log2_ns) - 1);
+        const int rest = cp >> (2 + log2_ns);
+        const int q = rest & 3, jl = rest >> 2;
+        const int j = jl / KL, l = jl % KL;
+        const int u = (s_ << LOG2_TG) + 4 * j + a;
+        if (u < u_lo || u >= u_hi)
+            continue;
+        const uint16_t *row = &kt[u * RS + (q * KL + l) * (16 / E)];
+        u32x4 out;
+        if (BF16) {
+            out = *reinterpret_cast<const u32x4 *>(row);
+        } else {
+            const u32x4 x0 = *reinterpret_cast<const u32x4 *>(row);
+            const u32x4 x1 = *reinterpret_cast<const u32x4 *>(row + 8);
+            out = u32x4{quantize_bf16x4(x0[0], x0[1], ks), quantize_bf16x4(x0[2], x0[3], ks),
+                        quantize_bf16x4(x1[0], x1[1], ks), quantize_bf16x4(x1[2], x1[3], ks)};
+        }
+        store16(kseg + cp * 16, out);
+    }
+    // V: runs of TR slots of one head dim, the dim fastest across lanes
+    constexpr int NV = (MAXSEG / TR * D + kFillThreads - 1) / kFillThreads;
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+        const int idx = tid + it * kFillThreads;
+        if (idx >= (SEG / TR) * D)
+            break;
+        const int d = idx % D, r = idx / D;
+        const int u0 = r * TR;
+        uint32_t word[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int u = u0 + e * (TR / 4);
+            if (BF16) {
+                word[e] = static_cast<uint32_t>(vt[u * RS + d]) | static_cast<uint32_t>(vt[(u + 1) * RS + d]) << 16;
+            } else {
+                word[e] = quantize_bf16x4(static_cast<uint32_t>(vt[u * RS + d]) | static_cast<uint32_t>(vt[(u + 1) * RS + d]) << 16,
+                                    static_cast<uint32_t>(vt[(u + 2) * RS + d]) | static_cast<uint32_t>(vt[(u + 3) * RS + d]) << 16,
+                                    vs);
+            }
+        }
+        uint8_t *dst = vseg + (static_cast<int64_t>(d) * SEG + u0) * E;
+        if (u0 >= u_lo && u0 + TR <= u_hi) {
+            store16(dst, u32x4{word[0], word[1], word[2], word[3]});
+        } else {
+            for (int t = 0; t < TR; ++t) {
+                const int u = u0 + t;
+                if (u < u_lo || u >= u_hi)
+                    continue;
+                if (BF16)
+                    reinterpret_cast<uint16_t *>(dst)[t] = static_cast<uint16_t>(word[t >> 1] >> (16 * (t & 1)));
+                else
+                    dst[t] = static_cast<uint8_t>(word[t >> 2] >> (8 * (t & 3)));
+            }
         }
     }
 }
@@ -129,23 +224,47 @@ __global__ __launch_bounds__(D) void kv_write_kernel(WriteParams p, int groups_p
 template <bool BF16, int D>
 hipError_t launch_write_t(const WriteParams &p, hipStream_t stream)
 {
-    const int groups = p.context_lens != nullptr ? 1 : (p.src_tokens + 15) / 16 + 1;
-    const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * groups;
+    if (p.context_lens != nullptr) {
+        const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads;
+        if (blocks > 0x7FFFFFFF)
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((kv_append_kernel<BF16, D>), dim3(static_cast<unsigned>(blocks)), dim3(D), 0,
+                           stream, p);
+        return hipGetLastError();
+    }
+    const int log2_maxseg = BF16 ? 5 : 6;
+    const int log2_seg = p.log2_page < log2_maxseg ? p.log2_page : log2_maxseg;
+    // segments one request's span can touch: ceil(T / SEG) + 1 (an unaligned start)
+    const int segs = ((p.src_tokens + (1 << log2_seg) - 1) >> log2_seg) + 1;
+    const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * segs;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((kv_write_kernel<BF16, D>), dim3(static_cast<unsigned>(blocks)), dim3(D), 0,
-                       stream, p, groups);
+    hipLaunchKernelGGL((kv_fill_kernel<BF16, D>), dim3(static_cast<unsigned>(blocks)), dim3(kFillThreads),
+                       0, stream, p, segs);
     return hipGetLastError();
 }
 
 // --- codec conformance kernels -------------------------------------------------
 
+// four values per thread through the packed encoder the fill kernel uses, so
+// the exhaustive sweep covers every byte position of it
 __global__ __launch_bounds__(256) void e4m3_encode_kernel(const float *__restrict__ x,
                                                           uint8_t *__restrict__ codes, int64_t n)
 {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
-        codes[i] = static_cast<uint8_t>(e4m3_encode(x[i]));
+    const int64_t n4 = (n + 3) / 4;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const int64_t e = 4 * i;
+        if (e + 4 <= n) {
+            const uint32_t w = e4m3_encode4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                codes[e + k] = static_cast<uint8_t>(w >> (8 * k));
+        } else {
+            for (int64_t k = e; k < n; ++k)
+                codes[k] = static_cast<uint8_t>(e4m3_encode(x[k]));
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void e4m3_decode_kernel(const uint8_t *__restrict__ codes,
@@ -170,7 +289,7 @@ __global__ __launch_bounds__(256) void e4m3_decode_kernel(const uint8_t *__restr
 
 unsigned grid_for(int64_t n)
 {
-    int64_t blocks = (n + 255) / 256;
+    int64_t blocks = (n + 1023) / 1024;
     if (blocks > 65536)
         blocks = 65536;
     return static_cast<unsigned>(blocks < 1 ? 1 : blocks);

@@ -14,7 +14,7 @@ import oracle
 from paged_attention_fp8_amd import harness as H
 from paged_attention_fp8_amd import inputs as I
 from paged_attention_fp8_amd import ops
-from helpers import allclose_report, oracle_pool
+from helpers import allclose_report, oracle_pool, poison_value
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -158,28 +158,42 @@ def test_fill_and_append_pools_bit_exact(w, kv_dtype):
     assert np.array_equal(v, ref.v)
 
 
-def test_fill_arbitrary_offsets_and_status():
-    """Blocks starting at unaligned positions, clipped counts, aborted and
-    invalid requests."""
-    say("kv write: offsets / status")
-    w = I.Workload("w", 5, 4, 2, 64, 16, 80, 80, pool_factor=1.0)
+@pytest.mark.parametrize("kv_dtype,P,D", [(ops.KV_FP8_E4M3, 16, 64), (ops.KV_FP8_E4M3, 64, 128),
+                                          (ops.KV_FP8_E4M3, 128, 128), (ops.KV_BF16, 16, 64),
+                                          (ops.KV_BF16, 32, 128), (ops.KV_BF16, 256, 128)])
+def test_fill_arbitrary_offsets_and_status(kv_dtype, P, D):
+    """Blocks starting at unaligned positions, partial and whole segments,
+    clipped counts, aborted and invalid requests."""
+    say(f"kv write: offsets / status dtype={kv_dtype} P={P} D={D}")
+    L = 300
+    w = I.Workload("w", 5, 4, 2, D, P, L, L, pool_factor=1.0)
     inp = I.make_decode_inputs(w, 3)
-    cache = H.new_cache(w, inp.num_pages, ops.KV_FP8_E4M3, DEV, inp.k_scale, inp.v_scale)
+    fp8 = kv_dtype == ops.KV_FP8_E4M3
+    cache = H.new_cache(w, inp.num_pages, kv_dtype, DEV, inp.k_scale if fp8 else None,
+                        inp.v_scale if fp8 else None)
     dbatch, _, _ = H.upload_batch(inp.batch, inp.pool, DEV)
+    cap = inp.batch.max_pages * P
     status = np.array([0, 1, 0, 0, 0], np.int32)
-    start = np.array([3, 0, 70, -5, 33], np.int32)
-    count = np.array([20, 10, 40, 9, 0], np.int32)      # 70+40 runs past the table; -5 starts before it
-    T = 12
+    start = np.array([3, 0, cap - 10, -5, 33], np.int32)   # cap - 10 runs past the table
+    count = np.array([150, 10, 40, 90, 0], np.int32)       # -5 starts before it; 150 is clipped
+    T = 130
     k_src = np.stack([inp.k_tokens[b][:T] for b in range(5)])
     v_src = np.stack([inp.v_tokens[b][:T] for b in range(5)])
     db = dbatch.with_status(torch.from_numpy(status).to(DEV))
     ops.kv_quant_fill(cache, db, torch.from_numpy(start).to(DEV), torch.from_numpy(count).to(DEV),
                       H.bf16_tensor(k_src, DEV), H.bf16_tensor(v_src, DEV))
-    ref = oracle.Pool(oracle.KV_FP8, inp.num_pages, 2, 16, 64, fill=H.FP8_NAN_CODE)
+    okv = oracle.KV_FP8 if fp8 else oracle.KV_BF16
+    ref = oracle.Pool(okv, inp.num_pages, 2, P, D, fill=poison_value(okv))
     oracle.kv_write(ref, inp.batch.page_table, start, np.minimum(count, T), k_src, v_src,
-                    inp.k_scale, inp.v_scale, status=status)
-    assert np.array_equal(cache.k_pool.cpu().numpy(), ref.k)
-    assert np.array_equal(cache.v_pool.cpu().numpy(), ref.v)
+                    inp.k_scale if fp8 else None, inp.v_scale if fp8 else None, status=status)
+    k, v = cache.k_pool.cpu(), cache.v_pool.cpu()
+    if not fp8:
+        k, v = k.view(torch.int16), v.view(torch.int16)
+    k, v = k.numpy(), v.numpy()
+    if not fp8:
+        k, v = k.view(np.uint16), v.view(np.uint16)
+    assert np.array_equal(k, ref.k)
+    assert np.array_equal(v, ref.v)
 
 
 def test_append_skips_aborted_and_invalid_lengths():
