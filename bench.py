@@ -19,7 +19,8 @@ measured with HIP events on the launch stream over the timed steps.  The
 bf16 twin (32 requests: the same KV bytes) and the tag-check overhead against
 the no-op tracker are reported beside it, and so is the long-context point
 (4 requests of 262,144 tokens in 64 splits: check overhead, and the batch
-with one stale request).  --sweep adds the 1/8/16/32/64 concurrency points,
+with one stale request) and the prefill-to-decode hand-off (kv_quant_fill of
+8 prompts of 8,192 tokens).  --sweep adds the 1/8/16/32/64 concurrency points,
 each step preceded by a 1 GiB read of other memory so that no point runs
 out of the MALL.  cpu_baseline times the CPU oracle on a bounded sample
 of the same batch.
@@ -118,7 +119,7 @@ class Point:
         live = [0 if b in self.inp.stale else int(L) for b, L in enumerate(self.lens)]
         self.bytes = algorithmic_bytes(live, Hq, self.w.kv_heads, D, self.w.page_size, elem)
 
-    def run(self, steps, warmup, splits, check=True, events=True, flush=False):
+    def run(self, steps, warmup, splits, check=True, events=True, flush=False, fused=False):
         """Time `steps` decode steps.  flush: before every step, read
         FLUSH_BYTES of other device memory so that no step finds the previous
         one's KV bytes in the last-level caches (the 256 MB MALL holds a
@@ -148,11 +149,16 @@ class Point:
             if i is not None and flush:
                 sev[i][0].record()
             stat = None
-            if check:
-                stat = ops.page_tag_check(st.batch, self.w.page_size, st.page_tags,
-                                          st.expected_tags, out=status)
-            b = st.batch.with_status(stat)
-            ops.kv_quant_append(st.cache, b, st.k_new, st.v_new)
+            if fused:   # check and append in one launch
+                stat = ops.kv_quant_append_checked(st.cache, st.batch, st.page_tags,
+                                                   st.expected_tags, st.k_new, st.v_new, out=status)
+                b = st.batch.with_status(stat)
+            else:
+                if check:
+                    stat = ops.page_tag_check(st.batch, self.w.page_size, st.page_tags,
+                                              st.expected_tags, out=status)
+                b = st.batch.with_status(stat)
+                ops.kv_quant_append(st.cache, b, st.k_new, st.v_new)
             if i is not None and events:
                 ev[i][0].record()
             ops.paged_decode_attn(st.cache, b, st.q, self.sm, S, ws, out, lse)
@@ -260,6 +266,41 @@ def long_context(args, dev):
     del ps, rs
     torch.cuda.empty_cache()
     return res
+
+
+def handoff(args, dev):
+    """The prefill-to-decode hand-off: kv_quant_fill of 8 prompts of 8,192
+    bf16 tokens (8 KV heads, head_dim 128) into e4m3 pages.  Per element it
+    must read 2 bytes and write 1, for K and for V."""
+    import torch
+    from paged_attention_fp8_amd import harness as H
+    from paged_attention_fp8_amd import inputs as I
+    from paged_attention_fp8_amd import ops
+    w = I.Workload("handoff_8k_b8", 8, 64, 8, 128, 64, 8192, 8192, pool_factor=1.0)
+    inp = I.make_device_decode_inputs(w, SEED, dev)
+    cache = H.new_cache(w, inp.num_pages, ops.KV_FP8_E4M3, dev, inp.k_scale, inp.v_scale, poison=False)
+    batch, _, _ = H.upload_batch(inp.batch, inp.pool, dev)
+    B, T = w.batch, w.max_len
+    start = torch.zeros(B, dtype=torch.int32, device=dev)
+    count = torch.full((B,), T, dtype=torch.int32, device=dev)
+    k, v = inp.k_tokens[:, :T].contiguous(), inp.v_tokens[:, :T].contiguous()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        ops.kv_quant_fill(cache, batch, start, count, k, v)
+    for a, b in ev:
+        a.record()
+        ops.kv_quant_fill(cache, batch, start, count, k, v)
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.mean(a.elapsed_time(b) for a, b in ev)
+    elems = B * T * w.kv_heads * w.head_dim
+    nbytes = 2 * elems * (2 + 1) + B * (T // w.page_size) * 4 + 2 * B * 4 + 2 * w.kv_heads * 4
+    del cache, inp, k, v
+    torch.cuda.empty_cache()
+    return {"workload": "8 prompts x 8192 bf16 tokens, 8 KV heads, head_dim 128, 64-token pages -> e4m3",
+            "kernel": "kv_fill_kernel<e4m3, 128>", "us": 1e3 * ms, "algorithmic_bytes": nbytes,
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
 def _pmc_values(directory, counter, kernel_substr):
@@ -417,7 +458,14 @@ def main():
         r0 = p.run(args.steps, args.warmup, args.splits, check=False)
         result["check_overhead_pct"] = 100.0 * (r["ms_per_step"] - r0["ms_per_step"]) / r0["ms_per_step"]
         result["no_tracker_ms_per_step"] = r0["ms_per_step"]
-        del r0
+        rf = p.run(args.steps, args.warmup, args.splits, fused=True)
+        if not torch.all(rf["status"] == 0):
+            raise SystemExit("fused check flagged requests in a clean batch")
+        result["fused_check"] = {
+            "ms_per_step": rf["ms_per_step"],
+            "check_overhead_pct": 100.0 * (rf["ms_per_step"] - r0["ms_per_step"]) / r0["ms_per_step"],
+        }
+        del r0, rf
         q = Point(32, ops.KV_BF16, dev)
         rb = q.run(args.steps, args.warmup, args.splits)
         bms = statistics.mean(rb["attn_ms"])
@@ -433,6 +481,7 @@ def main():
         del q
         torch.cuda.empty_cache()
         result["long_context"] = long_context(args, dev)
+        result["prefill_handoff"] = handoff(args, dev)
     if args.sweep:
         sweep = []
         for kv_dtype, name in ((ops.KV_FP8_E4M3, "fp8"), (ops.KV_BF16, "bf16")):

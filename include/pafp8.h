@@ -153,6 +153,49 @@ pafp8_status kv_quant_append(const pafp8_cache *cache, const pafp8_batch *batch,
                              hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * kv_quant_append_checked -- page_tag_check and kv_quant_append in one launch
+ * (section "共享 KV 缓存保护": the check runs before decode reads or writes
+ * the cache, at a cost the post wants negligible).  Computes exactly the
+ * verdict page_tag_check would (with page_size = cache->page_size and
+ * num_pages = cache->num_pages), writes it to req_status_out[b], and appends
+ * the token of every request whose verdict is 0, exactly as kv_quant_append.
+ * batch->req_status is ignored.  Pass req_status_out to the attention call of
+ * the same step (and of every other layer that shares these pages).
+ *   page_tags      device uint32 [num_pages]
+ *   expected_tags  device uint32 [B][max_pages_per_req]
+ *   req_status_out device int32 [B]
+ * Bit-exact.
+ * ------------------------------------------------------------------------- */
+pafp8_status kv_quant_append_checked(const pafp8_cache *cache, const pafp8_batch *batch,
+                                     const uint32_t *page_tags, const uint32_t *expected_tags,
+                                     const uint16_t *k_new, const uint16_t *v_new,
+                                     int32_t *req_status_out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * page_tag_realloc -- give pages to new owners on the device (section
+ * "共享 KV 缓存保护": a page's tag changes whenever the page is reallocated,
+ * so a request still holding it under the old tag fails its next check).
+ * For every k < n with p = page_ids[k] inside [0, num_pages):
+ *   page_tags[p] += 1 (wrapping modulo 2^32);
+ *   if owner_req is given and (b, i) = (owner_req[k], owner_slot[k]) lies in
+ *   [0, batch) x [0, max_pages_per_req): expected_tags[b][i] = the new tag
+ *   and, if page_table is given, page_table[b][i] = p.
+ * Entries with p outside the pool change nothing.
+ *   page_ids, owner_req, owner_slot  device int32 [n]; owner_* may both be NULL
+ *   page_tags      device uint32 [num_pages], updated in place
+ *   page_table     device int32 [batch][max_pages_per_req] or NULL
+ *   expected_tags  device uint32 [batch][max_pages_per_req] (may be NULL
+ *                  only without owners)
+ * The pages of one call should be distinct: then the result is bit-exact.
+ * A page listed m times is bumped by exactly m, but which of its owners
+ * records which of the intermediate tags is unspecified.
+ * ------------------------------------------------------------------------- */
+pafp8_status page_tag_realloc(int32_t n, const int32_t *page_ids, const int32_t *owner_req,
+                              const int32_t *owner_slot, uint32_t *page_tags, int32_t num_pages,
+                              int32_t *page_table, uint32_t *expected_tags, int32_t batch,
+                              int32_t max_pages_per_req, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * kv_quant_fill -- write a block of tokens per request (the prefill-to-decode
  * hand-off: prefill keeps a BF16 cache, decode stores e4m3; section
  * "KV 缓存量化").  Source token j < token_count[b] of request b goes to

@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_kv_append.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
                                        _P, _P, _P, _P, _P, _P]
         L.oracle_page_tag_check.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I, _P]
+        L.oracle_page_tag_realloc.argtypes = [_I, _P, _P, _P, _P, _I, _P, _P, _I, _I]
         L.oracle_paged_attention.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
                                              _P, _P, _P, _P, _P, _D, _P, _P]
         L.oracle_attention_range.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _I, _I,
@@ -219,6 +220,23 @@ def page_tag_check(page_table, context_lens, expected_tags, page_tags, page_size
                                 _ptr(_c(expected_tags, np.uint32)), _ptr(page_tags),
                                 page_tags.size, _ptr(out))
     return out
+
+
+def page_tag_realloc(page_ids, page_tags, owner_req=None, owner_slot=None, page_table=None,
+                     expected_tags=None):
+    """Reallocation in list order; returns updated copies (page_tags,
+    page_table or None, expected_tags or None)."""
+    ids = _c(page_ids, np.int32)
+    tags = np.array(page_tags, np.uint32, copy=True)
+    table = None if page_table is None else np.array(page_table, np.int32, copy=True)
+    exp = None if expected_tags is None else np.array(expected_tags, np.uint32, copy=True)
+    shape = table.shape if table is not None else (exp.shape if exp is not None else (0, 0))
+    B, maxP = shape
+    req = None if owner_req is None else _c(owner_req, np.int32)
+    slot = None if owner_slot is None else _c(owner_slot, np.int32)
+    lib().oracle_page_tag_realloc(ids.size, _ptr(ids), _ptr(req), _ptr(slot), _ptr(tags), tags.size,
+                                  _ptr(table), _ptr(exp), B, maxP)
+    return tags, table, exp
 
 
 # --- O7 / O8: attention and combine ---------------------------------------------

@@ -332,6 +332,33 @@ void oracle_page_tag_check(int B, int maxP, int P, const int32_t *page_table,
     }
 }
 
+/* O6b: giving pages to new owners (Cloudflare, "Smaller, faster, safer",
+ * section "共享 KV 缓存保护": a page's tag changes every time the page is
+ * reallocated).  Entries are applied in list order: the page's tag moves on
+ * by one (modulo 2^32) and an owner inside the table records the page and
+ * the new tag.  Entries naming a page outside the pool change nothing. */
+void oracle_page_tag_realloc(int n, const int32_t *page_ids, const int32_t *owner_req,
+                             const int32_t *owner_slot, uint32_t *page_tags, int num_pages,
+                             int32_t *page_table, uint32_t *expected_tags, int B, int maxP)
+{
+    int k;
+    for (k = 0; k < n; ++k) {
+        int32_t page = page_ids[k], b, i;
+        if (page < 0 || page >= num_pages)
+            continue;
+        page_tags[page] = page_tags[page] + 1u;
+        if (owner_req == NULL)
+            continue;
+        b = owner_req[k];
+        i = owner_slot[k];
+        if (b < 0 || b >= B || i < 0 || i >= maxP)
+            continue;
+        expected_tags[(int64_t)b * maxP + i] = page_tags[page];
+        if (page_table != NULL)
+            page_table[(int64_t)b * maxP + i] = page;
+    }
+}
+
 /* exact value of element (token t, head g, dim d) of K or V, or NaN when the
  * token's page is not a valid page of the pool */
 static double kv_value(int kv_dtype, int is_v, const void *pool, const float *scale,

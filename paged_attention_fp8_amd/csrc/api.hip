@@ -212,7 +212,9 @@ pafp8_status attn_impl(const pafp8_cache *cache, const pafp8_batch *batch, const
 
 pafp8_status write_impl(const pafp8_cache *cache, const pafp8_batch *batch, bool append,
                         const int32_t *start, const int32_t *count, int32_t T,
-                        const uint16_t *k_src, const uint16_t *v_src, hipStream_t stream)
+                        const uint16_t *k_src, const uint16_t *v_src, hipStream_t stream,
+                        const uint32_t *page_tags = nullptr, const uint32_t *expected_tags = nullptr,
+                        int32_t *status_out = nullptr, bool checked = false)
 {
     pafp8_status st = check_cache(cache, -1);
     if (st != PAFP8_OK)
@@ -223,6 +225,8 @@ pafp8_status write_impl(const pafp8_cache *cache, const pafp8_batch *batch, bool
         return ok();
     if (k_src == nullptr || v_src == nullptr)
         return fail(PAFP8_EINVAL, "source K/V is NULL");
+    if (checked && (page_tags == nullptr || expected_tags == nullptr || status_out == nullptr))
+        return fail(PAFP8_EINVAL, "page_tags, expected_tags or req_status_out is NULL");
     if (!append) {
         if (start == nullptr || count == nullptr)
             return fail(PAFP8_EINVAL, "token_start or token_count is NULL");
@@ -249,9 +253,16 @@ pafp8_status write_impl(const pafp8_cache *cache, const pafp8_batch *batch, bool
     p.num_kv_heads = cache->num_kv_heads;
     p.batch = batch->batch;
     p.max_pages = batch->max_pages_per_req;
+    if (checked) {
+        p.req_status = nullptr;
+        p.page_tags = page_tags;
+        p.expected_tags = expected_tags;
+        p.status_out = status_out;
+    }
     return hip_status(pafp8::launch_kv_write(cache->kv_dtype == PAFP8_KV_BF16, cache->head_dim, p,
                                              stream),
-                      append ? "kv_quant_append launch" : "kv_quant_fill launch");
+                      checked ? "kv_quant_append_checked launch"
+                              : append ? "kv_quant_append launch" : "kv_quant_fill launch");
 }
 
 }  // namespace
@@ -286,6 +297,36 @@ pafp8_status kv_quant_append(const pafp8_cache *cache, const pafp8_batch *batch,
                              const uint16_t *k_new, const uint16_t *v_new, hipStream_t stream)
 {
     return write_impl(cache, batch, true, nullptr, nullptr, 1, k_new, v_new, stream);
+}
+
+pafp8_status kv_quant_append_checked(const pafp8_cache *cache, const pafp8_batch *batch,
+                                     const uint32_t *page_tags, const uint32_t *expected_tags,
+                                     const uint16_t *k_new, const uint16_t *v_new,
+                                     int32_t *req_status_out, hipStream_t stream)
+{
+    return write_impl(cache, batch, true, nullptr, nullptr, 1, k_new, v_new, stream, page_tags,
+                      expected_tags, req_status_out, true);
+}
+
+pafp8_status page_tag_realloc(int32_t n, const int32_t *page_ids, const int32_t *owner_req,
+                              const int32_t *owner_slot, uint32_t *page_tags, int32_t num_pages,
+                              int32_t *page_table, uint32_t *expected_tags, int32_t batch,
+                              int32_t max_pages_per_req, hipStream_t stream)
+{
+    if (n < 0 || num_pages < 0 || batch < 0 || max_pages_per_req < 0)
+        return fail(PAFP8_EINVAL, "n, num_pages, batch and max_pages_per_req must be >= 0");
+    if (n == 0)
+        return ok();
+    if (page_ids == nullptr || (num_pages > 0 && page_tags == nullptr))
+        return fail(PAFP8_EINVAL, "page_ids or page_tags is NULL");
+    if ((owner_req == nullptr) != (owner_slot == nullptr))
+        return fail(PAFP8_EINVAL, "owner_req and owner_slot must both be given or both be NULL");
+    if (owner_req != nullptr && expected_tags == nullptr)
+        return fail(PAFP8_EINVAL, "expected_tags is NULL while owners are given");
+    return hip_status(pafp8::launch_tag_realloc(n, page_ids, owner_req, owner_slot, page_tags,
+                                                num_pages, page_table, expected_tags, batch,
+                                                max_pages_per_req, stream),
+                      "page_tag_realloc launch");
 }
 
 pafp8_status kv_quant_fill(const pafp8_cache *cache, const pafp8_batch *batch,

@@ -9,7 +9,9 @@
 // per request).
 //
 // Append (one token per request): one work-group per (request, KV head),
-// thread d owning head dimension d.
+// thread d owning head dimension d.  The checked variant first derives the
+// request's page-tag verdict (every work-group of the request computes the
+// same value) and writes nothing for a request that fails it.
 //
 // Fill (a block of tokens per request): one work-group per (request, KV head,
 // aligned segment of the block layout).  The segment's K and V source rows
@@ -18,11 +20,12 @@
 // 16-byte runs of one head dim, read down an LDS column.
 #include "pafp8_device.hpp"
 #include "pafp8_internal.hpp"
+#include "tag_verify.hpp"
 
 namespace pafp8 {
 namespace {
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool CHECKED>
 __global__ __launch_bounds__(D) void kv_append_kernel(WriteParams p)
 {
     const int g = blockIdx.x % p.num_kv_heads;
@@ -30,8 +33,17 @@ __global__ __launch_bounds__(D) void kv_append_kernel(WriteParams p)
     const int d = threadIdx.x;
     const int64_t cap = static_cast<int64_t>(p.max_pages) << p.log2_page;
 
-    if (p.req_status != nullptr && p.req_status[b] != 0)
-        return;
+    if constexpr (CHECKED) {
+        const int flags = request_flags<D>(b, p.max_pages, 1 << p.log2_page, p.page_table,
+                                           p.context_lens, p.expected_tags, p.page_tags, p.num_pages);
+        if (g == 0 && d == 0)
+            p.status_out[b] = flags;
+        if (flags != 0)
+            return;
+    } else {
+        if (p.req_status != nullptr && p.req_status[b] != 0)
+            return;
+    }
     const int32_t L = p.context_lens[b];
     if (L < 1 || L > cap)
         return;
@@ -228,8 +240,12 @@ hipError_t launch_write_t(const WriteParams &p, hipStream_t stream)
         const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads;
         if (blocks > 0x7FFFFFFF)
             return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((kv_append_kernel<BF16, D>), dim3(static_cast<unsigned>(blocks)), dim3(D), 0,
-                           stream, p);
+        if (p.status_out != nullptr)
+            hipLaunchKernelGGL((kv_append_kernel<BF16, D, true>), dim3(static_cast<unsigned>(blocks)),
+                               dim3(D), 0, stream, p);
+        else
+            hipLaunchKernelGGL((kv_append_kernel<BF16, D, false>), dim3(static_cast<unsigned>(blocks)),
+                               dim3(D), 0, stream, p);
         return hipGetLastError();
     }
     const int log2_maxseg = BF16 ? 5 : 6;

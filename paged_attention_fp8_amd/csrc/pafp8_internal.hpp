@@ -43,6 +43,11 @@ hipError_t launch_splitk_combine(const float *part_o, const float *part_lse, int
                                  const int32_t *req_status, float *out, float *lse,
                                  hipStream_t stream);
 
+hipError_t launch_tag_realloc(int n, const int32_t *page_ids, const int32_t *owner_req,
+                              const int32_t *owner_slot, uint32_t *page_tags, int num_pages,
+                              int32_t *page_table, uint32_t *expected_tags, int batch,
+                              int max_pages, hipStream_t stream);
+
 hipError_t launch_tag_check(int batch, int max_pages, int page_size, const int32_t *page_table,
                             const int32_t *context_lens, const uint32_t *expected_tags,
                             const uint32_t *page_tags, int num_pages, int32_t *status,
@@ -70,6 +75,12 @@ struct WriteParams {
     int32_t num_kv_heads;
     int32_t batch;
     int32_t max_pages;
+    // append with the tag check fused (status_out != nullptr): the verdict of
+    // page_tag_check is computed per request, written to status_out, and a
+    // non-zero verdict skips the write; req_status is then not read
+    const uint32_t *page_tags;
+    const uint32_t *expected_tags;
+    int32_t *status_out;
 };
 
 hipError_t launch_kv_write(bool bf16_pool, int head_dim, const WriteParams &p,

@@ -6,20 +6,22 @@
 // per request, the pages and tags it expects, and verifies them before decode
 // reads the cache; a mismatch terminates that request.  The post runs the
 // verification as its own batched pass rather than inside the attention
-// kernel (fusing it would race between GPU thread groups); this kernel is
-// that pass: one work-group per request, stream-ordered before append and
-// attention, which read its per-request verdict.
-#include "pafp8_device.hpp"
+// kernel (fusing it would race between GPU thread groups); tag_check_kernel
+// is that pass: one work-group per request, stream-ordered before append and
+// attention, which read its per-request verdict.  (The append kernel can
+// also compute the verdict itself: each of its work-groups derives the same
+// value from read-only inputs, so nothing races.)
+//
+// tag_realloc_kernel is the device side of giving a page to a new owner: the
+// page's tag moves on, so a request still holding the page with its old tag
+// fails the next check.
 #include "pafp8_internal.hpp"
+#include "tag_verify.hpp"
 
 namespace pafp8 {
 namespace {
 
-constexpr int kTagMismatch = 1;
-constexpr int kPageOob = 2;
-constexpr int kBadLen = 4;
 constexpr int kThreads = 256;
-constexpr int kChunk = 16;  // page-table entries per thread per pass
 
 __global__ __launch_bounds__(kThreads) void tag_check_kernel(
     int max_pages, int page_size, const int32_t *__restrict__ page_table,
@@ -27,46 +29,35 @@ __global__ __launch_bounds__(kThreads) void tag_check_kernel(
     const uint32_t *__restrict__ page_tags, int num_pages, int32_t *__restrict__ status)
 {
     const int b = blockIdx.x;
-    const int32_t L = context_lens[b];
-    const bool bad_len = L < 1 || static_cast<int64_t>(L) > static_cast<int64_t>(max_pages) * page_size;
-    int flags = 0;
-    if (!bad_len) {
-        const int n = static_cast<int>((static_cast<int64_t>(L) + page_size - 1) / page_size);
-        const int32_t *row = page_table + static_cast<int64_t>(b) * max_pages;
-        const uint32_t *exp_row = expected_tags + static_cast<int64_t>(b) * max_pages;
-        // kChunk entries per thread per pass, every load issued before any
-        // compare: a long request costs two memory round trips per pass
-        // instead of two per 256 entries.  Indices past n read entry n - 1
-        // again (n >= 1) and are not judged.
-        for (int base = 0; base < n; base += kThreads * kChunk) {
-            int32_t page[kChunk];
-            uint32_t want[kChunk], have[kChunk];
-#pragma unroll
-            for (int j = 0; j < kChunk; ++j) {
-                const int i = min(base + j * kThreads + static_cast<int>(threadIdx.x), n - 1);
-                page[j] = row[i];
-                want[j] = exp_row[i];
-            }
-#pragma unroll
-            for (int j = 0; j < kChunk; ++j) {
-                const bool in_pool = page[j] >= 0 && page[j] < num_pages;
-                have[j] = in_pool ? page_tags[page[j]] : 0u;  // the pool may be empty
-            }
-#pragma unroll
-            for (int j = 0; j < kChunk; ++j) {
-                if (base + j * kThreads + static_cast<int>(threadIdx.x) >= n)
-                    continue;
-                if (page[j] < 0 || page[j] >= num_pages)
-                    flags |= kPageOob;
-                else if (have[j] != want[j])
-                    flags |= kTagMismatch;
-            }
-        }
-    }
-    const int any_tag = __syncthreads_or(flags & kTagMismatch);
-    const int any_oob = __syncthreads_or(flags & kPageOob);
+    const int flags = request_flags<kThreads>(b, max_pages, page_size, page_table, context_lens,
+                                              expected_tags, page_tags, num_pages);
     if (threadIdx.x == 0)
-        status[b] = bad_len ? kBadLen : ((any_tag ? kTagMismatch : 0) | (any_oob ? kPageOob : 0));
+        status[b] = flags;
+}
+
+// Device-side reallocation: entry k gives page page_ids[k] a new tag and, if
+// its owner lies in the table, records the page and the new tag there.
+__global__ __launch_bounds__(kThreads) void tag_realloc_kernel(
+    int n, const int32_t *__restrict__ page_ids, const int32_t *__restrict__ owner_req,
+    const int32_t *__restrict__ owner_slot, uint32_t *page_tags, int num_pages, int32_t *page_table,
+    uint32_t *expected_tags, int batch, int max_pages)
+{
+    const int k = blockIdx.x * kThreads + threadIdx.x;
+    if (k >= n)
+        return;
+    const int32_t page = page_ids[k];
+    if (page < 0 || page >= num_pages)
+        return;
+    const uint32_t tag = atomicAdd(&page_tags[page], 1u) + 1u;
+    if (owner_req == nullptr)
+        return;
+    const int32_t b = owner_req[k], i = owner_slot[k];
+    if (b < 0 || b >= batch || i < 0 || i >= max_pages)
+        return;
+    const int64_t at = static_cast<int64_t>(b) * max_pages + i;
+    expected_tags[at] = tag;
+    if (page_table != nullptr)
+        page_table[at] = page;
 }
 
 }  // namespace
@@ -79,6 +70,17 @@ hipError_t launch_tag_check(int batch, int max_pages, int page_size, const int32
     hipLaunchKernelGGL(tag_check_kernel, dim3(batch), dim3(kThreads), 0, stream, max_pages,
                        page_size, page_table, context_lens, expected_tags, page_tags, num_pages,
                        status);
+    return hipGetLastError();
+}
+
+hipError_t launch_tag_realloc(int n, const int32_t *page_ids, const int32_t *owner_req,
+                              const int32_t *owner_slot, uint32_t *page_tags, int num_pages,
+                              int32_t *page_table, uint32_t *expected_tags, int batch,
+                              int max_pages, hipStream_t stream)
+{
+    hipLaunchKernelGGL(tag_realloc_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                       stream, n, page_ids, owner_req, owner_slot, page_tags, num_pages, page_table,
+                       expected_tags, batch, max_pages);
     return hipGetLastError();
 }
 

@@ -51,6 +51,8 @@ _CP, _BP = ctypes.POINTER(_Cache), ctypes.POINTER(_Batch)
 _SIGNATURES = {
     "page_tag_check": (_I32, [_BP, _I32, _V, _I32, _V, _V, _V]),
     "kv_quant_append": (_I32, [_CP, _BP, _V, _V, _V]),
+    "kv_quant_append_checked": (_I32, [_CP, _BP, _V, _V, _V, _V, _V, _V]),
+    "page_tag_realloc": (_I32, [_I32, _V, _V, _V, _V, _I32, _V, _V, _I32, _I32, _V]),
     "kv_quant_fill": (_I32, [_CP, _BP, _V, _V, _I32, _V, _V, _V]),
     "pafp8_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "pafp8_default_num_splits": (_I32, [_I32, _I32, _I32, _I32, _I32]),
@@ -246,6 +248,57 @@ def kv_quant_append(cache: PagedKVCache, batch: DecodeBatch, k_new: torch.Tensor
     _kv_src(v_new, "v_new", shape, dev)
     _check(lib().kv_quant_append(ctypes.byref(cs), ctypes.byref(bs), k_new.data_ptr(),
                                  v_new.data_ptr(), _stream(dev)), "kv_quant_append")
+
+
+def kv_quant_append_checked(cache: PagedKVCache, batch: DecodeBatch, page_tags: torch.Tensor,
+                            expected_tags: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """page_tag_check and kv_quant_append in one launch; returns the per-request
+    status (batch.req_status is ignored)."""
+    dev = cache.device
+    cs, bs = cache._struct(), batch._struct(dev)
+    shape = (batch.batch, cache.num_kv_heads, cache.head_dim)
+    _kv_src(k_new, "k_new", shape, dev)
+    _kv_src(v_new, "v_new", shape, dev)
+    tag_dtype = page_tags.dtype if page_tags.dtype in (torch.int32, torch.uint32) else torch.int32
+    _need(page_tags, "page_tags", tag_dtype, (cache.num_pages,), dev)
+    _need(expected_tags, "expected_tags", tag_dtype, tuple(batch.page_table.shape), dev)
+    if out is None:
+        out = torch.empty(batch.batch, dtype=torch.int32, device=dev)
+    _need(out, "req_status_out", torch.int32, (batch.batch,), dev)
+    _check(lib().kv_quant_append_checked(ctypes.byref(cs), ctypes.byref(bs), page_tags.data_ptr(),
+                                         expected_tags.data_ptr(), k_new.data_ptr(),
+                                         v_new.data_ptr(), out.data_ptr(), _stream(dev)),
+           "kv_quant_append_checked")
+    return out
+
+
+def page_tag_realloc(page_ids: torch.Tensor, page_tags: torch.Tensor,
+                     owner_req: Optional[torch.Tensor] = None,
+                     owner_slot: Optional[torch.Tensor] = None,
+                     page_table: Optional[torch.Tensor] = None,
+                     expected_tags: Optional[torch.Tensor] = None) -> None:
+    """Bump the tag of every listed page (in place) and record new owners."""
+    dev = page_tags.device
+    n = int(page_ids.numel())
+    _need(page_ids, "page_ids", torch.int32, (n,), dev)
+    tag_dtype = page_tags.dtype if page_tags.dtype in (torch.int32, torch.uint32) else torch.int32
+    _need(page_tags, "page_tags", tag_dtype, device=dev)
+    if (owner_req is None) != (owner_slot is None):
+        raise ValueError("owner_req and owner_slot go together")
+    B = maxP = 0
+    if owner_req is not None:
+        _need(owner_req, "owner_req", torch.int32, (n,), dev)
+        _need(owner_slot, "owner_slot", torch.int32, (n,), dev)
+        if expected_tags is None or expected_tags.dim() != 2:
+            raise ValueError("expected_tags [B][max_pages] is needed with owners")
+        _need(expected_tags, "expected_tags", tag_dtype, device=dev)
+        B, maxP = (int(x) for x in expected_tags.shape)
+        if page_table is not None:
+            _need(page_table, "page_table", torch.int32, (B, maxP), dev)
+    _check(lib().page_tag_realloc(n, page_ids.data_ptr(), _ptr(owner_req), _ptr(owner_slot),
+                                  page_tags.data_ptr(), page_tags.numel(), _ptr(page_table),
+                                  _ptr(expected_tags), B, maxP, _stream(dev)), "page_tag_realloc")
 
 
 def kv_quant_fill(cache: PagedKVCache, batch: DecodeBatch, token_start: torch.Tensor,

@@ -31,7 +31,8 @@ def L():
 
 def test_header_declares_the_path():
     names = set(declared_functions())
-    for n in ["page_tag_check", "kv_quant_append", "kv_quant_fill", "paged_decode_attn_fp8",
+    for n in ["page_tag_check", "kv_quant_append", "kv_quant_fill", "kv_quant_append_checked",
+              "page_tag_realloc", "paged_decode_attn_fp8",
               "paged_decode_attn_bf16", "splitk_combine", "pafp8_decode_workspace_bytes",
               "pafp8_default_num_splits", "pafp8_status_string", "pafp8_last_error",
               "pafp8_abi_version", "pafp8_e4m3_encode", "pafp8_e4m3_decode"]:
@@ -148,6 +149,16 @@ def test_other_entry_points_validate_without_gpu(L):
     assert L.page_tag_check(ctypes.byref(b), 64, 64, 10, None, 64, None) == 1
     assert L.splitk_combine(64, 64, 1, 8, 2, 6, None, 64, None, None) == 2
     assert L.splitk_combine(None, 64, 1, 8, 2, 128, None, 64, None, None) == 1
+    assert L.kv_quant_append_checked(ctypes.byref(c), ctypes.byref(b), None, 64, 64, 64, 64, None) == 1
+    assert b"page_tags" in L.pafp8_last_error()
+    assert L.kv_quant_append_checked(ctypes.byref(c), ctypes.byref(b), 64, 64, 64, 64, None, None) == 1
+    assert L.page_tag_realloc(-1, 64, None, None, 64, 10, None, None, 0, 0, None) == 1
+    assert L.page_tag_realloc(4, None, None, None, 64, 10, None, None, 0, 0, None) == 1
+    assert L.page_tag_realloc(4, 64, 64, None, 64, 10, None, 64, 4, 16, None) == 1
+    assert b"both" in L.pafp8_last_error()
+    assert L.page_tag_realloc(4, 64, 64, 64, 64, 10, None, None, 4, 16, None) == 1
+    assert b"expected_tags" in L.pafp8_last_error()
+    assert L.page_tag_realloc(0, None, None, None, None, 0, None, None, 0, 0, None) == 0
     assert L.pafp8_e4m3_encode(None, None, -1, None) == 1
     # empty work is OK and launches nothing
     assert L.pafp8_e4m3_encode(None, None, 0, None) == 0

@@ -25,8 +25,8 @@ def say(*a):
     print(*a, flush=True)
 
 
-def run_gpu(step, sm, num_splits, check=True):
-    out, lse, status = H.decode_step(step, sm, num_splits, check=check)
+def run_gpu(step, sm, num_splits, check=True, fused=False):
+    out, lse, status = H.decode_step(step, sm, num_splits, check=check, fused=fused)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy(), (None if status is None else status.cpu().numpy())
 
@@ -151,11 +151,13 @@ def test_physical_page_permutation_is_bitwise_invariant():
     assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["check_then_append", "append_checked"])
 @pytest.mark.parametrize("kv_dtype", [ops.KV_FP8_E4M3, ops.KV_BF16], ids=["fp8", "bf16"])
-def test_stale_request_aborted_and_excluded(kv_dtype):
+def test_stale_request_aborted_and_excluded(kv_dtype, fused):
     """A request with a stale tag is flagged, not appended, outputs 0 / -inf,
     and the other requests are bitwise what they are without it; its pages
-    may hold anything (NaN codes here) without effect."""
+    may hold anything (NaN codes here) without effect.  Same with the check
+    fused into the append launch."""
     w = I.scaled(CASES[4], stale_requests=1)
     inp = I.make_decode_inputs(w, 16)
     assert len(inp.stale) == 1
@@ -172,7 +174,7 @@ def test_stale_request_aborted_and_excluded(kv_dtype):
     else:
         step.cache.k_pool.view(torch.int16)[idx] = nan
         step.cache.v_pool.view(torch.int16)[idx] = nan
-    out, lse, status = run_gpu(step, 0.088, 3)
+    out, lse, status = run_gpu(step, 0.088, 3, fused=fused)
     want = np.zeros(inp.batch.batch, np.int32)
     want[bad] = oracle.REQ_TAG_MISMATCH
     assert np.array_equal(status, want)

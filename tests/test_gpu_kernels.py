@@ -215,6 +215,89 @@ def test_append_skips_aborted_and_invalid_lengths():
     assert np.array_equal(step.cache.v_pool.cpu().numpy(), ref.v)
 
 
+# --- fused check + append, device-side reallocation ------------------------------------
+
+def _dev(a, dtype=np.int32):
+    return torch.from_numpy(np.ascontiguousarray(a).view(dtype)).to(DEV)
+
+
+@pytest.mark.parametrize("kv_dtype", [ops.KV_FP8_E4M3, ops.KV_BF16])
+@pytest.mark.parametrize("D,P", [(64, 16), (128, 64)])
+def test_append_checked_equals_check_then_append(kv_dtype, D, P):
+    say(f"append checked: dtype={kv_dtype} D={D} P={P}")
+    w = I.Workload("chk", 8, 16, 4, D, P, 1, 40 * P, pool_factor=1.5)
+    inp = I.make_decode_inputs(w, 11)
+    step = H.build_step(inp, kv_dtype, DEV, poison=True)
+    table = inp.batch.page_table.copy()
+    lens = inp.batch.context_lens.copy()
+    tags = inp.pool.tags.copy()
+    tags[table[1, 0]] += np.uint32(1)      # request 1: page 0 reallocated behind its back
+    table[3, 0] = inp.num_pages + 5        # request 3: a page id outside the pool
+    lens[5] = 0                            # request 5: invalid length
+    dbatch = ops.DecodeBatch(_dev(table), _dev(lens))
+    got = ops.kv_quant_append_checked(step.cache, dbatch, _dev(tags), step.expected_tags,
+                                      step.k_new, step.v_new).cpu().numpy()
+    want = oracle.page_tag_check(table, lens, inp.batch.expected_tags, tags, P)
+    assert np.array_equal(got, want), (got, want)
+    assert want[1] == 1 and want[3] == 2 and want[5] == 4 and np.count_nonzero(want) == 3
+    fp8 = kv_dtype == ops.KV_FP8_E4M3
+    okv = oracle.KV_FP8 if fp8 else oracle.KV_BF16
+    ref = oracle_pool(inp, okv, poison=True, append=False)
+    oracle.kv_append(ref, table, lens, inp.k_new(), inp.v_new(), inp.k_scale if fp8 else None,
+                     inp.v_scale if fp8 else None, status=want)
+    k, v = step.cache.k_pool.cpu(), step.cache.v_pool.cpu()
+    if not fp8:
+        k, v = k.view(torch.int16), v.view(torch.int16)
+    k, v = k.numpy(), v.numpy()
+    if not fp8:
+        k, v = k.view(np.uint16), v.view(np.uint16)
+    assert np.array_equal(k, ref.k)
+    assert np.array_equal(v, ref.v)
+
+
+def test_tag_realloc_matches_oracle():
+    say("tag realloc: distinct pages vs oracle")
+    g = np.random.default_rng(21)
+    num_pages, B, maxP = 5000, 20, 64
+    tags0 = g.integers(0, 2**32, num_pages, dtype=np.uint64).astype(np.uint32)
+    tags0[:50] = 0xFFFFFFFF
+    table0 = g.integers(-1, num_pages, (B, maxP)).astype(np.int32)
+    exp0 = g.integers(0, 2**32, (B, maxP), dtype=np.uint64).astype(np.uint32)
+    n = 3000
+    ids = g.permutation(num_pages)[:n].astype(np.int32)
+    ids[::97] = -3                                   # outside the pool
+    ids[5::101] = num_pages + 1
+    req = np.full(n, -1, np.int32)
+    slot = np.full(n, 0, np.int32)
+    k = min(n, B * maxP)
+    perm = g.permutation(B * maxP)[:k]               # distinct owner slots
+    req[:k], slot[:k] = perm // maxP, perm % maxP
+    req[g.random(n) < 0.1] = B + 3                   # owners outside the table
+    t_d, pt_d, ex_d = _dev(tags0), _dev(table0), _dev(exp0)
+    ops.page_tag_realloc(_dev(ids), t_d, _dev(req), _dev(slot), pt_d, ex_d)
+    rt, rp, re_ = oracle.page_tag_realloc(ids, tags0, req, slot, table0, exp0)
+    assert np.array_equal(t_d.cpu().numpy().view(np.uint32), rt)
+    assert np.array_equal(pt_d.cpu().numpy(), rp)
+    assert np.array_equal(ex_d.cpu().numpy().view(np.uint32), re_)
+
+
+def test_tag_realloc_repeated_pages():
+    """A page listed m times moves on by m; its owners record m distinct
+    tags, one per listing."""
+    say("tag realloc: repeated pages")
+    tags0 = np.array([10, 0xFFFFFFFE, 3], np.uint32)
+    ids = np.array([1, 1, 1, 0, 1], np.int32)
+    B, maxP = 1, 5
+    req = np.zeros(5, np.int32)
+    slot = np.arange(5, dtype=np.int32)
+    t_d, ex_d = _dev(tags0), _dev(np.zeros((B, maxP), np.uint32))
+    ops.page_tag_realloc(_dev(ids), t_d, _dev(req), _dev(slot), None, ex_d)
+    tags = t_d.cpu().numpy().view(np.uint32)
+    ex = ex_d.cpu().numpy().view(np.uint32)[0]
+    assert list(tags) == [11, 2, 3]
+    assert sorted(ex[[0, 1, 2, 4]].tolist()) == [0, 1, 2, 0xFFFFFFFF] and ex[3] == 11
+
+
 # --- combine --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("S,D", [(1, 128), (7, 64), (17, 64), (64, 128), (130, 128), (5, 96), (70, 256)])

@@ -115,6 +115,58 @@ def test_tag_check_thousand_requests_one_stale():
     assert np.flatnonzero(st).tolist() == [437] and st[437] == oracle.REQ_TAG_MISMATCH
 
 
+# --- O6b: reallocation ---------------------------------------------------------------
+
+def test_realloc_reproduces_the_host_allocator():
+    """Replaying the host allocator's allocations as reallocation entries gives
+    its tags, page table and recorded tags (two independent implementations
+    of 'every allocation moves the page's tag on')."""
+    pool = I.PagePool(300, seed=5, first_tag=7)
+    tags0 = pool.tags.copy()
+    batch = I.allocate_batch(pool, [40, 900, 1, 513, 64], 16)
+    ids, reqs, slots = [], [], []
+    for b in range(batch.batch):
+        n = I.pages_needed(batch.context_lens[b], 16)
+        ids += list(batch.page_table[b, :n])
+        reqs += [b] * n
+        slots += list(range(n))
+    table0 = np.full_like(batch.page_table, -1)
+    exp0 = np.zeros_like(batch.expected_tags)
+    tags, table, exp = oracle.page_tag_realloc(ids, tags0, reqs, slots, table0, exp0)
+    assert np.array_equal(tags, pool.tags)
+    assert np.array_equal(table, batch.page_table)
+    assert np.array_equal(exp, batch.expected_tags)
+
+
+def test_realloc_makes_the_old_owner_stale_and_the_new_one_valid():
+    """A page given to another request: the old holder fails the check with a
+    tag mismatch, the new holder passes, everyone else is unchanged."""
+    pool = I.PagePool(64, seed=1)
+    batch = I.allocate_batch(pool, [48, 48, 48], 16)   # 3 pages each
+    check = lambda t, tb, e: oracle.page_tag_check(tb, batch.context_lens, e, t, 16)
+    assert np.all(check(pool.tags, batch.page_table, batch.expected_tags) == 0)
+    victim = int(batch.page_table[0, 1])
+    # request 2 takes over the page as its logical page 2
+    tags, table, exp = oracle.page_tag_realloc([victim], pool.tags, [2], [2], batch.page_table,
+                                               batch.expected_tags)
+    st = check(tags, table, exp)
+    assert list(st) == [oracle.REQ_TAG_MISMATCH, 0, 0]
+    assert table[2, 2] == victim and exp[2, 2] == pool.tags[victim] + 1
+
+
+def test_realloc_edges():
+    tags0 = np.array([0xFFFFFFFF, 5, 9], np.uint32)
+    # wrap-around, out-of-pool entries, owners outside the table
+    tags, table, exp = oracle.page_tag_realloc([0, 3, -1, 1], tags0, [0, 0, 0, 7], [1, 0, 0, 0],
+                                               np.full((2, 2), -1, np.int32), np.zeros((2, 2), np.uint32))
+    assert list(tags) == [0, 6, 9]
+    assert table[0, 1] == 0 and exp[0, 1] == 0          # the wrapped tag is recorded
+    assert np.count_nonzero(table != -1) == 1             # page 3 and -1 are outside; owner 7 too
+    # without owners only the tags move; a page listed twice moves twice
+    tags, table, exp = oracle.page_tag_realloc([2, 2, 1], tags0)
+    assert list(tags) == [0xFFFFFFFF, 6, 11] and table is None and exp is None
+
+
 # --- pool writes -----------------------------------------------------------------
 
 def test_block_layout_maps_are_permutations():
