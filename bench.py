@@ -20,7 +20,8 @@ bf16 twin (32 requests: the same KV bytes) and the tag-check overhead against
 the no-op tracker are reported beside it, and so is the long-context point
 (4 requests of 262,144 tokens in 64 splits: check overhead, and the batch
 with one stale request) and the prefill-to-decode hand-off (kv_quant_fill of
-8 prompts of 8,192 tokens).  --sweep adds the 1/8/16/32/64 concurrency points,
+8 prompts of 8,192 tokens) and a continuous decode loop with admission
+under the same 2 GiB budget (e4m3 vs bf16).  --sweep adds the 1/8/16/32/64 concurrency points,
 each step preceded by a 1 GiB read of other memory so that no point runs
 out of the MALL.  cpu_baseline times the CPU oracle on a bounded sample
 of the same batch.
@@ -303,6 +304,54 @@ def handoff(args, dev):
             "GBps": nbytes / (ms * 1e-3) / 1e9, "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+def decode_loop(args, dev):
+    """Continuous decode under the 2 GiB pool budget: 128 requests of 16,384
+    tokens in total (prompt handed over by kv_quant_fill, then 64-192 decode
+    steps each), admitted first come first served while pages are free; each
+    step is kv_quant_append_checked + attention over 64 slots.  Run once with
+    an e4m3 pool and once with a bf16 pool of the same bytes."""
+    import numpy as np
+    import torch
+    from paged_attention_fp8_amd import decode_loop as DL
+    from paged_attention_fp8_amd import inputs as I
+    from paged_attention_fp8_amd import ops
+    g = np.random.default_rng(SEED + 7)
+    dec = g.integers(64, 193, 128)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(SEED + 8)
+    sample = torch.randn(1 << 22, generator=gen, device=dev).to(torch.bfloat16).float()
+    scale = I.fp8_scale_from_amax(np.full(8, float(sample.abs().max()), np.float32))
+    res = {}
+    for kv_dtype, name in ((ops.KV_FP8_E4M3, "e4m3"), (ops.KV_BF16, "bf16")):
+        loop = DL.DecodeLoop(kv_dtype, I.SWEEP_BUDGET_BYTES, 64, 8, 128, 64, 64, 16384, dev,
+                             SEED, scale, scale)
+        for rid, d in enumerate(dec):
+            loop.submit(DL.Request(rid, 16384 - int(d), int(d)))
+        stats = []
+        t0 = time.perf_counter()
+        while (loop.queue or any(r is not None for r in loop.slots)) and len(stats) < 4000:
+            stats.append(loop.step())
+        wall = time.perf_counter() - t0
+        tokens = sum(st.active for st in stats)
+        gpu_s = sum(st.gpu_ms for st in stats) * 1e-3
+        res[name] = {
+            "pool_pages": loop.num_pages,
+            "max_concurrent": loop.max_active,
+            "waiting_after_first_step": stats[0].waiting,
+            "steps": len(stats),
+            "finished": sum(1 for r in loop.finished if not r.terminated),
+            "terminated": sum(1 for r in loop.finished if r.terminated),
+            "decode_tokens": tokens,
+            "decode_tokens_per_gpu_s": tokens / gpu_s,
+            "mean_step_gpu_ms": 1e3 * gpu_s / len(stats),
+            "wall_s": wall,
+        }
+        del loop
+        torch.cuda.empty_cache()
+    return {"workload": "128 requests x 16384 tokens (prompt + 64..192 decode steps), GQA 64/8, "
+                        "head_dim 128, 64-token pages, 2 GiB pool, 64 slots", **res}
+
+
 def _pmc_values(directory, counter, kernel_substr):
     """Per-dispatch values of one counter for kernels whose name contains
     kernel_substr, from a rocprofv3 --pmc csv run directory."""
@@ -482,6 +531,7 @@ def main():
         torch.cuda.empty_cache()
         result["long_context"] = long_context(args, dev)
         result["prefill_handoff"] = handoff(args, dev)
+        result["decode_loop"] = decode_loop(args, dev)
     if args.sweep:
         sweep = []
         for kv_dtype, name in ((ops.KV_FP8_E4M3, "fp8"), (ops.KV_BF16, "bf16")):

@@ -125,7 +125,10 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
 
 @dataclasses.dataclass
 class PagedKVCache:
-    """The shared physical page pool: K [pages][Hkv][P][D], V [pages][Hkv][D][P]."""
+    """The shared physical page pool.  The tensors are shaped [pages][Hkv][P][D]
+    (K) and [pages][Hkv][D][P] (V) as containers only: the P*D elements of a
+    (page, KV head) block are ordered by the segmented block layout of
+    include/pafp8.h, and only the library's calls write them."""
     k_pool: torch.Tensor           # uint8 (e4m3 codes) or bfloat16
     v_pool: torch.Tensor
     k_scale: Optional[torch.Tensor] = None   # float32 [Hkv], e4m3 only
