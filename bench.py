@@ -21,7 +21,8 @@ the no-op tracker are reported beside it, and so is the long-context point
 (4 requests of 262,144 tokens in 64 splits: check overhead, and the batch
 with one stale request) and the prefill-to-decode hand-off (kv_quant_fill of
 8 prompts of 8,192 tokens) and a continuous decode loop with admission
-under the same 2 GiB budget (e4m3 vs bf16).  --sweep adds the 1/8/16/32/64 concurrency points,
+under the same 2 GiB budget (e4m3 vs bf16), and INT4 weight streaming
+(int4_gemv over 940 MB of int4 weights at 1-64 rows).  --sweep adds the 1/8/16/32/64 concurrency points,
 each step preceded by a 1 GiB read of other memory so that no point runs
 out of the MALL.  cpu_baseline times the CPU oracle on a bounded sample
 of the same batch.
@@ -352,6 +353,46 @@ def decode_loop(args, dev):
                         "head_dim 128, 64-token pages, 2 GiB pool, 64 slots", **res}
 
 
+def int4_decode(args, dev):
+    """Decode-time weight streaming with INT4 weights: y = x . W^T for 8
+    distinct 28672 x 8192 weight matrices in turn (940 MB of int4 weights, far
+    beyond the MALL), at 1, 8, 16, 32 and 64 rows of x (concurrent requests)."""
+    import torch
+    from paged_attention_fp8_amd import ops
+    N, K, layers = 28672, 8192, 8
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(SEED + 11)
+    ws = [torch.randint(0, 256, (N * K // 2,), generator=gen, device=dev, dtype=torch.uint8)
+          for _ in range(layers)]
+    ss = [(torch.rand((K // 128, N), generator=gen, device=dev) * 0.05 + 1e-3).to(torch.bfloat16)
+          for _ in range(layers)]
+    res = []
+    for M in (1, 8, 16, 32, 64):
+        x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            for i in range(layers):
+                ops.int4_gemv(x, ws[i], ss[i], N, K, out=y)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            for i in range(layers):
+                ops.int4_gemv(x, ws[i], ss[i], N, K, out=y)
+            b.record()
+        torch.cuda.synchronize()
+        ms = statistics.mean(a.elapsed_time(b) for a, b in ev) / layers
+        nbytes = N * K // 2 + (K // 128) * N * 2 + M * K * 2 + M * N * 4
+        res.append({"rows": M, "us_per_matrix": 1e3 * ms,
+                    "GBps": nbytes / (ms * 1e-3) / 1e9,
+                    "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                    "TFLOPs": 2.0 * M * N * K / (ms * 1e-3) / 1e12})
+    del ws, ss
+    torch.cuda.empty_cache()
+    return {"workload": "8 int4 weight matrices 28672 x 8192 (bf16 scale per 128 inputs), "
+                        "bf16 activations, fp32 output", "kernel": "int4_gemv_kernel", "points": res}
+
+
 def _pmc_values(directory, counter, kernel_substr):
     """Per-dispatch values of one counter for kernels whose name contains
     kernel_substr, from a rocprofv3 --pmc csv run directory."""
@@ -532,6 +573,7 @@ def main():
         result["long_context"] = long_context(args, dev)
         result["prefill_handoff"] = handoff(args, dev)
         result["decode_loop"] = decode_loop(args, dev)
+        result["int4_decode_gemv"] = int4_decode(args, dev)
     if args.sweep:
         sweep = []
         for kv_dtype, name in ((ops.KV_FP8_E4M3, "fp8"), (ops.KV_BF16, "bf16")):

@@ -215,6 +215,43 @@ pafp8_status kv_quant_fill(const pafp8_cache *cache, const pafp8_batch *batch,
                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * INT4 weight streaming for decode (the post's section "模型权重压缩", model
+ * weight compression: GLM weights go from FP8 to INT4 because decode streams the
+ * weights from GPU memory for every token, and fewer bytes stream faster;
+ * the weights are expanded before the multiplication).  The pages give no
+ * grouping or zero point; the reading here: weights are signed 4-bit
+ * integers q in [-8, 7] (two's complement nibbles) with one bf16 scale per
+ * output row and group of 128 consecutive input features:
+ *     y[m][n] = sum_k x[m][k] * q[n][k] * scales[k / 128][n].
+ *
+ * Packed weight layout (what int4_gemv reads): blocks of 1024 bytes, one per
+ * (row tile nt of 16 output rows, group g of 128 features), ordered
+ * [N / 16][K / 128].  Byte 16 * L + 4 * j + b of a block (L < 64, j < 4,
+ * b < 4), with L = 16 * kq + c, holds row n = 16 * nt + c, features
+ * k = 128 * g + 32 * j + 8 * kq + 2 * b (low nibble) and k + 1 (high nibble).
+ * ------------------------------------------------------------------------- */
+
+/* int4_pack_weights -- row-major weights to the packed layout.
+ *   w_rowmajor  device [N][K / 2] bytes: byte k / 2 of row n holds feature k
+ *               (low nibble for even k); 4-byte aligned
+ *   w_packed    device [N * K / 2] bytes, 16-byte aligned (output)
+ * Requires N % 16 == 0 and K % 512 == 0.  A byte permutation: bit-exact. */
+pafp8_status int4_pack_weights(const uint8_t *w_rowmajor, int32_t N, int32_t K, uint8_t *w_packed,
+                               hipStream_t stream);
+
+/* int4_gemv -- y = x . W^T with W expanded on read (q * scale).
+ *   x         device bf16 bit patterns [M][K], 16-byte aligned
+ *   w_packed  device, the packed layout above, 16-byte aligned
+ *   scales    device bf16 bit patterns [K / 128][N]
+ *   y         device fp32 [M][N] (output)
+ * Requires N % 16 == 0 and K % 512 == 0; any M >= 0 (64 rows of x per
+ * launch).  Products are exact (q / 16 is exact in bf16) and summed in fp32,
+ * 128 per group and then over the K / 128 groups, so to first order
+ *     |y[m][n] - exact| <= (K / 128 + 129) * 2^-24 * sum_k |x[m][k] * q[n][k] * s|. */
+pafp8_status int4_gemv(const uint16_t *x, int32_t M, const uint8_t *w_packed, const uint16_t *scales,
+                       int32_t N, int32_t K, float *y, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Split-K (flash-decoding) sizing.  With num_splits = S > 1 each request's
  * pages are cut into S consecutive chunks of ceil(max_pages_per_req / S)
  * pages; each chunk produces a partial (o, lse) in the workspace and

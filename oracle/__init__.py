@@ -13,6 +13,8 @@ lists the sources and the readings taken where the pages are silent:
   (KV cache quantization) -- FP8 e4m3 storage, conversion on read;
 * same post, section "共享 KV 缓存保护" (shared KV cache protection) -- per-page
   tags, per-request expected tags, check before decode reads, abort on mismatch;
+* same post, section "模型权重压缩" (model weight compression) -- INT4 weights
+  streamed and expanded on read during decode;
 * remio.ai analysis of the post, section on shared KV cache safety -- paged
   attention maps each logical sequence onto physical pages.
 
@@ -88,6 +90,8 @@ def lib() -> ctypes.CDLL:
                                        _P, _P, _P, _P, _P, _P]
         L.oracle_page_tag_check.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I, _P]
         L.oracle_page_tag_realloc.argtypes = [_I, _P, _P, _P, _P, _I, _P, _P, _I, _I]
+        L.oracle_int4_unpack.argtypes = [_P, _I, _I, _P]
+        L.oracle_int4_gemv.argtypes = [_I, _I, _I, _P, _P, _P, _P]
         L.oracle_paged_attention.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
                                              _P, _P, _P, _P, _P, _D, _P, _P]
         L.oracle_attention_range.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _I, _I,
@@ -288,3 +292,25 @@ def splitk_combine(part_o, part_lse, status=None):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+# --- INT4 weight streaming --------------------------------------------------------
+
+def int4_unpack(w_packed, N, K) -> np.ndarray:
+    """q [N][K] int8 from the packed layout (the oracle's own addressing)."""
+    w = _c(w_packed, np.uint8)
+    q = np.empty((N, K), np.int8)
+    lib().oracle_int4_unpack(_ptr(w), N, K, _ptr(q))
+    return q
+
+
+def int4_gemv(x_bf16, w_packed, scales_bf16, N, K) -> np.ndarray:
+    """y[m][n] = sum_k x[m][k] q[n][k] s[k/128][n] in fp64; x [M][K] and
+    scales [K/128][N] as bf16 bit patterns."""
+    x = _c(x_bf16, np.uint16)
+    M = x.shape[0]
+    y = np.empty((M, N), np.float64)
+    lib().oracle_int4_gemv(M, N, K, _ptr(x), _ptr(_c(w_packed, np.uint8)),
+                           _ptr(_c(scales_bf16, np.uint16)), _ptr(y))
+    return y
+

@@ -24,6 +24,10 @@
  *          attention splits the cache into reusable blocks and maps each
  *          logical sequence onto physical pages; tags act like generation
  *          counters.
+ *   [WQ]   same post, section "模型权重压缩" (model weight compression): GLM
+ *          weights go from FP8 to INT4; decode reads the weights for every
+ *          token, so fewer bytes decode faster; the weights are expanded
+ *          before multiplying.
  *   [OFP8] The e4m3 format itself is not defined on the pages, which only name
  *          it.  The reading used here is the OCP 8-bit floating point "E4M3"
  *          encoding: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
@@ -548,3 +552,55 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------
+ * INT4 weight streaming (Cloudflare, "Smaller, faster, safer", section
+ * "模型权重压缩" (model weight compression): GLM weights go from FP8 to INT4; decode reads
+ * the weights for every token and expands them before multiplying).  The
+ * pages give no grouping or zero point; the reading taken: symmetric signed
+ * 4-bit integers, one bf16 scale per output row and 128 input features.
+ * ------------------------------------------------------------------------ */
+
+/* weight q[n][k] from the packed layout: 1024-byte blocks per (16 rows,
+ * 128 features), ordered by row tile then group; inside a block, byte
+ * 16*(16*kq + c) + 4*j + b holds row 16*nt + c, features
+ * 128*g + 32*j + 8*kq + 2*b (low nibble) and the next one (high nibble) */
+static int int4_weight(const uint8_t *packed, int K, int n, int k)
+{
+    int nt = n / 16, c = n % 16, g = k / 128, r = k % 128;
+    int j = r / 32, kq = (r % 32) / 8, b = (r % 8) / 2, high = r % 2;
+    int64_t byte = ((int64_t)nt * (K / 128) + g) * 1024 + (16 * kq + c) * 16 + 4 * j + b;
+    int nib = high ? (packed[byte] >> 4) & 15 : packed[byte] & 15;
+    return nib >= 8 ? nib - 16 : nib;
+}
+
+void oracle_int4_unpack(const uint8_t *packed, int N, int K, int8_t *q_out)
+{
+    int n, k;
+    for (n = 0; n < N; ++n)
+        for (k = 0; k < K; ++k)
+            q_out[(int64_t)n * K + k] = (int8_t)int4_weight(packed, K, n, k);
+}
+
+/* y[m][n] = sum_k x[m][k] * q[n][k] * s[k / 128][n], in fp64 (exact inputs) */
+void oracle_int4_gemv(int M, int N, int K, const uint16_t *x, const uint8_t *packed,
+                      const uint16_t *scales, double *y)
+{
+    int64_t mn;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 64)
+#endif
+    for (mn = 0; mn < (int64_t)M * N; ++mn) {
+        int m = (int)(mn / N), n = (int)(mn % N), k;
+        {
+            double acc = 0.0;
+            for (k = 0; k < K; ++k) {
+                double xv = (double)bf16_value(x[(int64_t)m * K + k]);
+                double sv = (double)bf16_value(scales[(int64_t)(k / 128) * N + n]);
+                acc += xv * (double)int4_weight(packed, K, n, k) * sv;
+            }
+            y[(int64_t)m * N + n] = acc;
+        }
+    }
+}
+

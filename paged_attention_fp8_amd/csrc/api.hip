@@ -410,6 +410,48 @@ pafp8_status splitk_combine(const float *part_o, const float *part_lse, int32_t 
                       "splitk_combine launch");
 }
 
+pafp8_status int4_pack_weights(const uint8_t *w_rowmajor, int32_t N, int32_t K, uint8_t *w_packed,
+                               hipStream_t stream)
+{
+    if (N < 0 || K < 0 || N % 16 != 0 || K % 512 != 0)
+        return fail(PAFP8_EUNSUPPORTED, "N = %d, K = %d (need N a multiple of 16, K of 512)", N, K);
+    if (N == 0 || K == 0)
+        return ok();
+    if (w_rowmajor == nullptr || w_packed == nullptr)
+        return fail(PAFP8_EINVAL, "w_rowmajor or w_packed is NULL");
+    if ((reinterpret_cast<uintptr_t>(w_rowmajor) & 3u) != 0 || !aligned16(w_packed))
+        return fail(PAFP8_EINVAL, "w_rowmajor must be 4-byte and w_packed 16-byte aligned");
+    return hip_status(pafp8::launch_int4_pack(w_rowmajor, w_packed, N, K, stream),
+                      "int4_pack_weights launch");
+}
+
+pafp8_status int4_gemv(const uint16_t *x, int32_t M, const uint8_t *w_packed, const uint16_t *scales,
+                       int32_t N, int32_t K, float *y, hipStream_t stream)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return fail(PAFP8_EINVAL, "M, N and K must be >= 0");
+    if (N % 16 != 0 || K % 512 != 0)
+        return fail(PAFP8_EUNSUPPORTED, "N = %d, K = %d (need N a multiple of 16, K of 512)", N, K);
+    if (M == 0 || N == 0)
+        return ok();
+    if (K == 0)
+        return fail(PAFP8_EUNSUPPORTED, "K = 0");
+    if (x == nullptr || w_packed == nullptr || scales == nullptr || y == nullptr)
+        return fail(PAFP8_EINVAL, "x, w_packed, scales or y is NULL");
+    if (!aligned16(x) || !aligned16(w_packed))
+        return fail(PAFP8_EINVAL, "x and w_packed must be 16-byte aligned");
+    // 64 rows of x per launch
+    for (int32_t m0 = 0; m0 < M; m0 += 64) {
+        const int32_t m = M - m0 < 64 ? M - m0 : 64;
+        const hipError_t e = pafp8::launch_int4_gemv(x + static_cast<int64_t>(m0) * K, m, w_packed,
+                                                     scales, N, K, y + static_cast<int64_t>(m0) * N,
+                                                     stream);
+        if (e != hipSuccess)
+            return hip_status(e, "int4_gemv launch");
+    }
+    return ok();
+}
+
 pafp8_status pafp8_e4m3_encode(const float *x, uint8_t *codes, int64_t n, hipStream_t stream)
 {
     if (n < 0)

@@ -1,0 +1,216 @@
+// int4_gemv.hip -- decode-time weight streaming with INT4 weights,
+// dequantized on read.
+//
+// Cloudflare, "Smaller, faster, safer: running Kimi and GLM at scale",
+// section "模型权重压缩" (model weight compression: GLM weights FP8 -> INT4): decode
+// streams the weights from GPU memory for every generated token, so 4-bit
+// weights move fewer bytes and decode runs faster; the weights are expanded
+// before the multiplication.  The pages give no grouping or zero point; the
+// reading here is symmetric signed 4-bit integers q in [-8, 7] with one bf16
+// scale per 128 consecutive input features of an output row:
+//     y[m][n] = sum_k x[m][k] * q[n][k] * s[k / 128][n].
+//
+// Packed weight layout (include/pafp8.h): 1 KiB blocks of 16 output rows x
+// 128 input features, ordered [N / 16][K / 128].  Lane L = 16*kq + c of a
+// wave loads the 16 bytes at L*16 of a block; their dword j holds the 8
+// weights of row c at features 32j + 8kq .. +8 (feature order = nibble
+// order, low nibble first), which is exactly lane L's B operand of the j-th
+// v_mfma_f32_16x16x32_bf16 over the block.
+//
+// Work split: a work-group of 4 waves owns 64 output rows (one 16-row tile
+// per wave) over all of K.  Per group of 128 features the work-group stages
+// x[0:16*MT][group] in LDS; each wave expands its 1 KiB block to bf16
+// (v_cvt_off_f32_i4 gives q/16 exactly; the factor 16 goes into the scale),
+// runs 4 MFMAs per 16-row tile of x and adds 16*s times the group's partial
+// sums into its fp32 accumulators.
+#include "pafp8_device.hpp"
+#include "pafp8_internal.hpp"
+
+namespace pafp8 {
+namespace {
+
+constexpr int kGemvWaves = 4;
+constexpr int kGemvThreads = 64 * kGemvWaves;
+constexpr int kGroup = 128;        // input features per scale
+
+// 8 int4 weights (one dword, low nibble first) -> 8 bf16 of q/16, exact
+__device__ __forceinline__ bf16x8 int4x8_to_bf16_div16(uint32_t w)
+{
+    f32x2 f[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i][0] = __builtin_amdgcn_cvt_off_f32_i4(w >> (8 * i));
+        f[i][1] = __builtin_amdgcn_cvt_off_f32_i4(w >> (8 * i + 4));
+    }
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2 p = __builtin_convertvector(f[i], bf16x2);
+        r[2 * i] = p[0];
+        r[2 * i + 1] = p[1];
+    }
+    return r;
+}
+
+template <int MT>
+__global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
+    const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ w,
+    const uint16_t *__restrict__ scales, int N, int K, float *__restrict__ y)
+{
+    constexpr int PF = 4;                                // weight blocks in flight per wave
+    constexpr int XC = MT == 1 ? 4 : (MT == 2 ? 2 : 1);  // groups per staged x chunk
+    constexpr int XS = XC * kGroup + 8;                  // LDS row stride (bf16), 16 bytes of padding
+    constexpr int XP = MT * XC;                          // 16-byte x pieces per thread per chunk
+    __shared__ __align__(16) uint16_t xs[2][MT * 16 * XS];
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int tid = threadIdx.x;
+    const int n_tiles = N / 16;
+    const int nt = blockIdx.x * kGemvWaves + wave;  // this wave's 16-row tile
+    const bool live = nt < n_tiles;
+    const int G = K / kGroup;
+    const int c = lane & 15, kq = lane >> 4;
+
+    // x chunk ch: rows [0, 16*MT) x features [ch*XC*128, (ch+1)*XC*128); rows >= M are zero
+    u32x4 xr[XP];
+    auto load_x = [&](int ch) {
+#pragma unroll
+        for (int it = 0; it < XP; ++it) {
+            const int idx = tid + it * kGemvThreads;
+            const int m = idx / (XC * kGroup / 8), c8 = idx % (XC * kGroup / 8);
+            xr[it] = u32x4{0u, 0u, 0u, 0u};
+            if (m < M)
+                xr[it] = load16(x + static_cast<int64_t>(m) * K + static_cast<int64_t>(ch) * XC * kGroup + c8 * 8);
+        }
+    };
+    auto store_x = [&](int buf) {
+#pragma unroll
+        for (int it = 0; it < XP; ++it) {
+            const int idx = tid + it * kGemvThreads;
+            const int m = idx / (XC * kGroup / 8), c8 = idx % (XC * kGroup / 8);
+            *reinterpret_cast<u32x4 *>(&xs[buf][m * XS + c8 * 8]) = xr[it];
+        }
+    };
+
+    const uint8_t *wb = w + (static_cast<int64_t>(live ? nt : 0) * G) * 1024 + lane * 16;
+    const uint16_t *sp = scales + (live ? nt : 0) * 16 + c;
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 wr[PF];
+    uint16_t sr[PF];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+        if (u < G) {
+            wr[u] = load16_stream(wb + static_cast<int64_t>(u) * 1024);
+            sr[u] = sp[static_cast<int64_t>(u) * N];
+        }
+    }
+    load_x(0);
+    store_x(0);
+    __syncthreads();
+
+    // G is a multiple of XC (K % 512 == 0 when XC = 4 is checked on the host),
+    // and XC divides PF, so chunk boundaries fall on fixed u
+    for (int g0 = 0; g0 < G; g0 += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int g = g0 + u;
+            if (g >= G)
+                break;
+            const int ch = g / XC;
+            if (u % XC == 0 && (ch + 1) * XC < G)
+                load_x(ch + 1);
+            bf16x8 bop[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bop[j] = int4x8_to_bf16_div16(wr[u][j]);
+            const float s16 = 16.0f * __uint_as_float(static_cast<uint32_t>(sr[u]) << 16);
+            if (g + PF < G) {
+                wr[u] = load16_stream(wb + static_cast<int64_t>(g + PF) * 1024);
+                sr[u] = sp[static_cast<int64_t>(g + PF) * N];
+            }
+            const uint16_t *xa = &xs[ch & 1][c * XS + (u % XC) * kGroup + 8 * kq];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xa + mt * 16 * XS + 32 * j);
+                    part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[j], part, 0, 0, 0);
+                }
+                acc[mt] += s16 * part;
+            }
+            if (u % XC == XC - 1 && (ch + 1) * XC < G) {
+                // every wave is done with buffer (ch + 1) & 1 since the last barrier
+                store_x((ch + 1) & 1);
+                __syncthreads();
+            }
+        }
+    }
+    if (!live)
+        return;
+    // acc[mt][i] = y[16*mt + 4*kq + i][16*nt + c]
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = mt * 16 + 4 * kq + i;
+            if (m < M)
+                y[static_cast<int64_t>(m) * N + nt * 16 + c] = acc[mt][i];
+        }
+}
+
+// row-major int4 [N][K/2] -> packed blocks: a permutation of 4-byte words
+__global__ __launch_bounds__(256) void int4_pack_kernel(const uint32_t *__restrict__ src,
+                                                        uint32_t *__restrict__ dst, int N, int K)
+{
+    const int64_t words = static_cast<int64_t>(N) * K / 8;
+    const int G = K / kGroup;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        // destination word i: block (nt, g), lane L = 16*kq + c, dword j
+        const int j = static_cast<int>(i & 3);
+        const int L = static_cast<int>((i >> 2) & 63);
+        const int64_t blk = i >> 8;
+        const int g = static_cast<int>(blk % G);
+        const int64_t nt = blk / G;
+        const int c = L & 15, kq = L >> 4;
+        const int64_t n = nt * 16 + c;
+        const int64_t k = static_cast<int64_t>(g) * kGroup + 32 * j + 8 * kq;
+        dst[i] = src[(n * K + k) / 8];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const uint16_t *scales,
+                            int N, int K, float *y, hipStream_t stream)
+{
+    const int n_tiles = N / 16;
+    const dim3 grid((n_tiles + kGemvWaves - 1) / kGemvWaves);
+    const int mt = (M + 15) / 16;
+    if (mt == 1)
+        hipLaunchKernelGGL(int4_gemv_kernel<1>, grid, dim3(kGemvThreads), 0, stream, x, M, w, scales, N, K, y);
+    else if (mt == 2)
+        hipLaunchKernelGGL(int4_gemv_kernel<2>, grid, dim3(kGemvThreads), 0, stream, x, M, w, scales, N, K, y);
+    else if (mt == 3)
+        hipLaunchKernelGGL(int4_gemv_kernel<3>, grid, dim3(kGemvThreads), 0, stream, x, M, w, scales, N, K, y);
+    else
+        hipLaunchKernelGGL(int4_gemv_kernel<4>, grid, dim3(kGemvThreads), 0, stream, x, M, w, scales, N, K, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_int4_pack(const uint8_t *src, uint8_t *dst, int N, int K, hipStream_t stream)
+{
+    const int64_t words = static_cast<int64_t>(N) * K / 8;
+    int64_t blocks = (words + 255) / 256;
+    if (blocks > 65536)
+        blocks = 65536;
+    hipLaunchKernelGGL(int4_pack_kernel, dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks)), dim3(256), 0,
+                       stream, reinterpret_cast<const uint32_t *>(src), reinterpret_cast<uint32_t *>(dst), N, K);
+    return hipGetLastError();
+}
+
+}  // namespace pafp8

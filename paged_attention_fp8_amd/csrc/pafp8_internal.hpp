@@ -86,6 +86,11 @@ struct WriteParams {
 hipError_t launch_kv_write(bool bf16_pool, int head_dim, const WriteParams &p,
                            hipStream_t stream);
 
+// INT4 weight streaming: y[M][N] = x[M][K] . (q * s)^T, w in packed blocks.
+hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const uint16_t *scales,
+                            int N, int K, float *y, hipStream_t stream);
+hipError_t launch_int4_pack(const uint8_t *src, uint8_t *dst, int N, int K, hipStream_t stream);
+
 hipError_t launch_e4m3_encode(const float *x, uint8_t *codes, int64_t n, hipStream_t stream);
 hipError_t launch_e4m3_decode(const uint8_t *codes, float *f32, float *via_f16, float *via_bf16,
                               int64_t n, hipStream_t stream);

@@ -54,6 +54,8 @@ _SIGNATURES = {
     "kv_quant_append_checked": (_I32, [_CP, _BP, _V, _V, _V, _V, _V, _V]),
     "page_tag_realloc": (_I32, [_I32, _V, _V, _V, _V, _I32, _V, _V, _I32, _I32, _V]),
     "kv_quant_fill": (_I32, [_CP, _BP, _V, _V, _I32, _V, _V, _V]),
+    "int4_pack_weights": (_I32, [_V, _I32, _I32, _V, _V]),
+    "int4_gemv": (_I32, [_V, _I32, _V, _V, _I32, _I32, _V, _V]),
     "pafp8_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "pafp8_default_num_splits": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "paged_decode_attn_fp8": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V]),
@@ -412,3 +414,41 @@ def e4m3_decode(codes: torch.Tensor):
                                    outs[2].data_ptr(), codes.numel(), _stream(codes.device)),
            "pafp8_e4m3_decode")
     return tuple(outs)
+
+
+# ----------------------------------------------------------------------------
+# INT4 weight streaming
+# ----------------------------------------------------------------------------
+
+def int4_pack_weights(w_rowmajor: torch.Tensor, N: int, K: int,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Row-major int4 weights (uint8 [N][K/2], low nibble = even feature) to
+    the packed layout int4_gemv reads (uint8 [N*K/2])."""
+    dev = w_rowmajor.device
+    _need(w_rowmajor, "w_rowmajor", torch.uint8, (N, K // 2), dev)
+    if out is None:
+        out = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+    _need(out, "w_packed", torch.uint8, (N * K // 2,), dev)
+    _check(lib().int4_pack_weights(w_rowmajor.data_ptr(), N, K, out.data_ptr(), _stream(dev)),
+           "int4_pack_weights")
+    return out
+
+
+def int4_gemv(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor, N: int, K: int,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[M][N] = x[M][K] . (q * scale)^T with packed int4 weights and bf16
+    scales [K/128][N]; fp32 output."""
+    dev = x.device
+    if x.dim() != 2:
+        raise ValueError("x must be [M][K]")
+    M = int(x.shape[0])
+    _need(x, "x", torch.bfloat16, (M, K), dev)
+    _need(w_packed, "w_packed", torch.uint8, (N * K // 2,), dev)
+    _need(scales, "scales", torch.bfloat16, (K // 128, N), dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _need(out, "y", torch.float32, (M, N), dev)
+    _check(lib().int4_gemv(x.data_ptr(), M, w_packed.data_ptr(), scales.data_ptr(), N, K,
+                           out.data_ptr(), _stream(dev)), "int4_gemv")
+    return out
+

@@ -145,3 +145,25 @@ def allclose_report(got, ref, atol=2e-3, rtol=1e-2):
     ok = bool(np.all(err <= atol + rtol * np.abs(ref)))
     rel = err / np.maximum(np.abs(ref), 1e-30)
     return ok, float(err.max()) if err.size else 0.0, float(rel.max()) if rel.size else 0.0
+
+
+# --- INT4 weights -------------------------------------------------------------------
+
+def int4_rowmajor(q: np.ndarray) -> np.ndarray:
+    """int8 q [N][K] in [-8, 7] -> bytes [N][K/2], feature k in the low nibble
+    of byte k/2 when k is even."""
+    u = (np.asarray(q, np.int16) & 15).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def int4_blocks(q: np.ndarray) -> np.ndarray:
+    """The packed layout written out in NumPy (independently of the oracle's
+    C addressing): 1024-byte blocks per (16 rows, 128 features), ordered
+    [N/16][K/128]; byte 16*(16*kq + c) + 4*j + b of a block holds row c of
+    the tile, features 32*j + 8*kq + 2*b and +1 of the group."""
+    N, K = q.shape
+    rm = int4_rowmajor(q)                                  # [N][K/2]
+    # [nt][c][g][j][kq][b] bytes of the row-major array
+    t = rm.reshape(N // 16, 16, K // 128, 4, 4, 4)
+    # -> [nt][g][kq][c][j][b]
+    return np.ascontiguousarray(t.transpose(0, 2, 4, 1, 3, 5)).reshape(-1)
