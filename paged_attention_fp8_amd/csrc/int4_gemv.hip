@@ -52,12 +52,14 @@ __device__ __forceinline__ bf16x8 int4x8_to_bf16_div16(uint32_t w)
     return r;
 }
 
-template <int MT>
+// MT: 16-row tiles of x; PF: weight blocks in flight per wave, a divisor of
+// K / 128 (so the unrolled group loop needs no early exit, which would let
+// the compiler sink the x loads to their use)
+template <int MT, int PF>
 __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ w,
     const uint16_t *__restrict__ scales, int N, int K, float *__restrict__ y)
 {
-    constexpr int PF = 4;                                // weight blocks in flight per wave
     constexpr int XC = MT == 1 ? 4 : (MT == 2 ? 2 : 1);  // groups per staged x chunk
     constexpr int XS = XC * kGroup + 8;                  // LDS row stride (bf16), 16 bytes of padding
     constexpr int XP = MT * XC;                          // 16-byte x pieces per thread per chunk
@@ -71,16 +73,19 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
     const int G = K / kGroup;
     const int c = lane & 15, kq = lane >> 4;
 
-    // x chunk ch: rows [0, 16*MT) x features [ch*XC*128, (ch+1)*XC*128); rows >= M are zero
+    // x chunk ch: rows [0, 16*MT) x features [ch*XC*128, (ch+1)*XC*128); rows
+    // >= M are zero.  Loads in the main loop are unconditional (rows and
+    // blocks clamped into range, unwanted values dropped by a select): a
+    // conditional load would make the compiler wait for it where the
+    // branches join.
     u32x4 xr[XP];
     auto load_x = [&](int ch) {
 #pragma unroll
         for (int it = 0; it < XP; ++it) {
             const int idx = tid + it * kGemvThreads;
             const int m = idx / (XC * kGroup / 8), c8 = idx % (XC * kGroup / 8);
-            xr[it] = u32x4{0u, 0u, 0u, 0u};
-            if (m < M)
-                xr[it] = load16(x + static_cast<int64_t>(m) * K + static_cast<int64_t>(ch) * XC * kGroup + c8 * 8);
+            const int mr = m < M ? m : M - 1;
+            xr[it] = load16(x + static_cast<int64_t>(mr) * K + static_cast<int64_t>(ch) * XC * kGroup + c8 * 8);
         }
     };
     auto store_x = [&](int buf) {
@@ -88,7 +93,8 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
         for (int it = 0; it < XP; ++it) {
             const int idx = tid + it * kGemvThreads;
             const int m = idx / (XC * kGroup / 8), c8 = idx % (XC * kGroup / 8);
-            *reinterpret_cast<u32x4 *>(&xs[buf][m * XS + c8 * 8]) = xr[it];
+            const u32x4 v = m < M ? xr[it] : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4 *>(&xs[buf][m * XS + c8 * 8]) = v;
         }
     };
 
@@ -98,38 +104,42 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // scales kept one per 32-bit register: packing two 16-bit values per
+    // register would make the compiler wait for each scale load at once
     u32x4 wr[PF];
-    uint16_t sr[PF];
+    uint32_t sr[PF];
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-        if (u < G) {
-            wr[u] = load16_stream(wb + static_cast<int64_t>(u) * 1024);
-            sr[u] = sp[static_cast<int64_t>(u) * N];
-        }
+        const int gl = u < G ? u : G - 1;
+        wr[u] = load16_stream(wb + static_cast<int64_t>(gl) * 1024);
+        sr[u] = static_cast<uint32_t>(sp[static_cast<int64_t>(gl) * N]);
     }
     load_x(0);
     store_x(0);
     __syncthreads();
 
-    // G is a multiple of XC (K % 512 == 0 when XC = 4 is checked on the host),
-    // and XC divides PF, so chunk boundaries fall on fixed u
+    // PF divides G and XC divides PF, so chunk boundaries fall on fixed u
     for (int g0 = 0; g0 < G; g0 += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
             const int g = g0 + u;
-            if (g >= G)
-                break;
             const int ch = g / XC;
-            if (u % XC == 0 && (ch + 1) * XC < G)
-                load_x(ch + 1);
+            const int last_ch = G / XC - 1;
+            if (u % XC == 0) {
+                load_x(ch + 1 <= last_ch ? ch + 1 : last_ch);
+                // keep these loads ahead of the chunk's weight loads: the
+                // LDS store at the chunk's end then waits for them alone
+                __builtin_amdgcn_sched_barrier(0);
+            }
             bf16x8 bop[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 bop[j] = int4x8_to_bf16_div16(wr[u][j]);
-            const float s16 = 16.0f * __uint_as_float(static_cast<uint32_t>(sr[u]) << 16);
-            if (g + PF < G) {
-                wr[u] = load16_stream(wb + static_cast<int64_t>(g + PF) * 1024);
-                sr[u] = sp[static_cast<int64_t>(g + PF) * N];
+            const float s16 = 16.0f * __uint_as_float(sr[u] << 16);
+            {
+                const int gl = g + PF < G ? g + PF : G - 1;
+                wr[u] = load16_stream(wb + static_cast<int64_t>(gl) * 1024);
+                sr[u] = static_cast<uint32_t>(sp[static_cast<int64_t>(gl) * N]);
             }
             const uint16_t *xa = &xs[ch & 1][c * XS + (u % XC) * kGroup + 8 * kq];
 #pragma unroll
@@ -142,8 +152,10 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
                 }
                 acc[mt] += s16 * part;
             }
-            if (u % XC == XC - 1 && (ch + 1) * XC < G) {
-                // every wave is done with buffer (ch + 1) & 1 since the last barrier
+            if (u % XC == XC - 1) {
+                // every wave is done with buffer (ch + 1) & 1 since the last
+                // barrier; after the last chunk this store is dead but keeps
+                // the x loads unconditional (and so issued early)
                 store_x((ch + 1) & 1);
                 __syncthreads();
             }
@@ -191,14 +203,24 @@ hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const ui
     const int n_tiles = N / 16;
     const dim3 grid((n_tiles + kGemvWaves - 1) / kGemvWaves);
     const int mt = (M + 15) / 16;
-    if (mt == 1)
-        hipLaunchKernelGGL(int4_gemv_kernel<1>, grid, dim3(kGemvThreads), 0, stream, x, M, w, scales, N, K, y);
-    else if (mt == 2)
-        hipLaunchKernelGGL(int4_gemv_kernel<2>, grid, dim3(kGemvThreads), 0, stream, x, M, w, scales, N, K, y);
-    else if (mt == 3)
-        hipLaunchKernelGGL(int4_gemv_kernel<3>, grid, dim3(kGemvThreads), 0, stream, x, M, w, scales, N, K, y);
-    else
-        hipLaunchKernelGGL(int4_gemv_kernel<4>, grid, dim3(kGemvThreads), 0, stream, x, M, w, scales, N, K, y);
+    const bool pf8 = (K / kGroup) % 8 == 0;   // K % 512 == 0 gives a multiple of 4
+#define PAFP8_GEMV(MT_)                                                                            \
+    if (pf8)                                                                                       \
+        hipLaunchKernelGGL((int4_gemv_kernel<MT_, 8>), grid, dim3(kGemvThreads), 0, stream, x, M, w, \
+                           scales, N, K, y);                                                       \
+    else                                                                                           \
+        hipLaunchKernelGGL((int4_gemv_kernel<MT_, 4>), grid, dim3(kGemvThreads), 0, stream, x, M, w, \
+                           scales, N, K, y);
+    if (mt == 1) {
+        PAFP8_GEMV(1)
+    } else if (mt == 2) {
+        PAFP8_GEMV(2)
+    } else if (mt == 3) {
+        PAFP8_GEMV(3)
+    } else {
+        PAFP8_GEMV(4)
+    }
+#undef PAFP8_GEMV
     return hipGetLastError();
 }
 
