@@ -80,11 +80,16 @@ def parse_args():
     return ap.parse_args()
 
 
+# the sources the counted attention launch is built and configured from
+ATTN_SOURCES = ("decode_attn.hip", "pafp8_device.hpp", "pafp8_internal.hpp", "api.hip")
+
+
 def source_hash() -> str:
-    """Hash of the kernel sources: counter figures taken on other sources are stale."""
+    """Hash of the attention kernel's sources: counter figures taken on other
+    sources are stale."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "paged_attention_fp8_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "paged_attention_fp8_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
