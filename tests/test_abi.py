@@ -32,7 +32,7 @@ def L():
 def test_header_declares_the_path():
     names = set(declared_functions())
     for n in ["page_tag_check", "kv_quant_append", "kv_quant_fill", "kv_quant_append_checked",
-              "page_tag_realloc", "paged_decode_attn_fp8",
+              "page_tag_realloc", "int4_pack_weights", "int4_gemv", "paged_decode_attn_fp8",
               "paged_decode_attn_bf16", "splitk_combine", "pafp8_decode_workspace_bytes",
               "pafp8_default_num_splits", "pafp8_status_string", "pafp8_last_error",
               "pafp8_abi_version", "pafp8_e4m3_encode", "pafp8_e4m3_decode"]:
@@ -159,6 +159,15 @@ def test_other_entry_points_validate_without_gpu(L):
     assert L.page_tag_realloc(4, 64, 64, 64, 64, 10, None, None, 4, 16, None) == 1
     assert b"expected_tags" in L.pafp8_last_error()
     assert L.page_tag_realloc(0, None, None, None, None, 0, None, None, 0, 0, None) == 0
+    # INT4 weight streaming: shapes, NULLs, alignment
+    assert L.int4_gemv(64, 1, 64, 64, 24, 512, 64, None) == 2           # N % 16
+    assert L.int4_gemv(64, 1, 64, 64, 16, 384, 64, None) == 2           # K % 512
+    assert L.int4_gemv(None, 1, 64, 64, 16, 512, 64, None) == 1
+    assert L.int4_gemv(72, 1, 64, 64, 16, 512, 64, None) == 1           # x not 16-byte aligned
+    assert L.int4_gemv(None, 0, None, None, 16, 512, None, None) == 0   # M = 0: nothing to do
+    assert L.int4_pack_weights(64, 16, 500, 64, None) == 2
+    assert L.int4_pack_weights(None, 16, 512, 64, None) == 1
+    assert L.int4_pack_weights(66, 16, 512, 64, None) == 1              # source not 4-byte aligned
     assert L.pafp8_e4m3_encode(None, None, -1, None) == 1
     # empty work is OK and launches nothing
     assert L.pafp8_e4m3_encode(None, None, 0, None) == 0
