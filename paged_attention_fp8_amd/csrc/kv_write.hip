@@ -20,6 +20,7 @@
 // 16-byte runs of one head dim, read down an LDS column.
 #include "pafp8_device.hpp"
 #include "pafp8_internal.hpp"
+#include "pafp8_quant.hpp"
 #include "tag_verify.hpp"
 
 namespace pafp8 {
@@ -77,8 +78,8 @@ __global__ __launch_bounds__(D) void kv_append_kernel(WriteParams p)
         *reinterpret_cast<uint16_t *>(kdst) = kx;
         *reinterpret_cast<uint16_t *>(vdst) = vx;
     } else {
-        *kdst = static_cast<uint8_t>(quantize_bf16(kx, p.k_scale[g]));
-        *vdst = static_cast<uint8_t>(quantize_bf16(vx, p.v_scale[g]));
+        *kdst = static_cast<uint8_t>(quantize_bf16(kx, make_quantizer(p.k_scale[g])));
+        *vdst = static_cast<uint8_t>(quantize_bf16(vx, make_quantizer(p.v_scale[g])));
     }
 }
 
@@ -164,8 +165,8 @@ __global__ __launch_bounds__(kFillThreads) void kv_fill_kernel(WriteParams p, in
     }
     __syncthreads();
 
-    const float ks = BF16 ? 1.0f : p.k_scale[g];
-    const float vs = BF16 ? 1.0f : p.v_scale[g];
+    const E4m3Quantizer ks = make_quantizer(BF16 ? 1.0f : p.k_scale[g]);
+    const E4m3Quantizer vs = make_quantizer(BF16 ? 1.0f : p.v_scale[g]);
     // K: this thread's chunk positions cp, in storage order; chunk cp holds
     // chunk c = q*KL + l of slot u = TG*s + 4j + a
     const int log2_ns = log2_seg - LOG2_TG;

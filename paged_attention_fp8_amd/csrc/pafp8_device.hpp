@@ -1,7 +1,8 @@
 // pafp8_device.hpp -- device-side building blocks for gfx950 (CDNA4).
 //
-// The e4m3 codec the kernels share, the MFMA operand types, 16-byte global
-// loads, and small wave helpers.  The cache format is the pages' "FP8 (e4m3)"
+// The e4m3 decode routes the attention kernels use, the MFMA operand types,
+// 16-byte global loads, and small wave helpers (the encoder and quantiser are
+// in pafp8_quant.hpp).  The cache format is the pages' "FP8 (e4m3)"
 // (Cloudflare, "Smaller, faster, safer: running Kimi and GLM at scale",
 // section "KV 缓存量化" / KV cache quantization), read as the OCP E4M3 encoding
 // (bias 7, no infinities, +-448 largest finite value), which gfx950's
@@ -24,62 +25,6 @@ typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-
-// ---------------------------------------------------------------------------
-// e4m3 encode: round to nearest even, saturate to +-448, NaN -> 0x7F|sign.
-// The hardware conversion rounds to nearest even on the OCP grid; clamping to
-// +-448 first turns overflow (and +-inf) into saturation instead of NaN.
-// ---------------------------------------------------------------------------
-// Branch-free: the NaN substitution is a per-byte select, so a wave never
-// splits over a NaN.
-__device__ __forceinline__ float e4m3_clamp(float x)
-{
-    return __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f);  // NaN -> -448, fixed below
-}
-
-__device__ __forceinline__ uint32_t e4m3_nan_byte(float x)
-{
-    return x != x ? (0x7Fu | ((__float_as_uint(x) >> 24) & 0x80u)) : 0x100u;  // 0x100: not NaN
-}
-
-// Four values -> four codes packed little-endian (a in the low byte).
-__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d)
-{
-    uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false));
-    w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d),
-                                                               static_cast<int>(w), true));
-    const float v[4] = {a, b, c, d};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t n = e4m3_nan_byte(v[i]);
-        const uint32_t mask = 0xFFu << (8 * i);
-        w = n < 0x100u ? (w & ~mask) | (n << (8 * i)) : w;
-    }
-    return w;
-}
-
-__device__ __forceinline__ uint32_t e4m3_encode(float x)
-{
-    const uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(x), 0.0f, 0, false)) & 0xFFu;
-    const uint32_t n = e4m3_nan_byte(x);
-    return n < 0x100u ? n : w;
-}
-
-// Quantise one bf16 element with a per-head scale: e4m3(f32(x) / scale).
-// '/' is IEEE-correctly-rounded here (no fast-math flags are used).
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t x) { return __uint_as_float(x << 16); }
-
-__device__ __forceinline__ uint32_t quantize_bf16(uint16_t x, float scale)
-{
-    return e4m3_encode(bf16_bits_to_f32(x) / scale);
-}
-
-// Four bf16 (two dwords, element 0 in the low half of w0) -> four codes.
-__device__ __forceinline__ uint32_t quantize_bf16x4(uint32_t w0, uint32_t w1, float scale)
-{
-    return e4m3_encode4(bf16_bits_to_f32(w0 & 0xFFFFu) / scale, bf16_bits_to_f32(w0 >> 16) / scale,
-                        bf16_bits_to_f32(w1 & 0xFFFFu) / scale, bf16_bits_to_f32(w1 >> 16) / scale);
-}
 
 // ---------------------------------------------------------------------------
 // e4m3 decode routes.  Every e4m3 value is exact in fp16, bf16 and fp32.

@@ -215,6 +215,40 @@ def test_append_skips_aborted_and_invalid_lengths():
     assert np.array_equal(step.cache.v_pool.cpu().numpy(), ref.v)
 
 
+SCALE_ROUNDS = [
+    # fast-path scales, its boundaries, and scales outside it (exact division)
+    [1.0, 3.7e-3, 0.0137, 2.0 ** -64, 2.0 ** 64, 2.0 ** -70, 5e30, 1.5e-20],
+    [0.5, 1.0 / 448, 7.77, 2.0 ** -63.5, 2.0 ** 63.9, 1e-30, 2.0 ** 70, 0.1],
+]
+
+
+@pytest.mark.parametrize("rnd", range(len(SCALE_ROUNDS)))
+def test_fill_quantises_every_bf16_pattern(rnd):
+    """All 65536 bf16 bit patterns (NaN, infinities, subnormals, zeros
+    included) under 16 scales each, through kv_quant_fill: pools byte-exact
+    against the oracle, which divides."""
+    say(f"kv write: every bf16 pattern, scale round {rnd}")
+    Hkv, D, P, T = 8, 128, 64, 512
+    w = I.Workload("allbf16", 1, Hkv, Hkv, D, P, T + 1, T + 1, pool_factor=1.0)
+    inp = I.make_decode_inputs(w, 5)
+    pats = np.arange(65536, dtype=np.uint16).reshape(T, D)
+    g = np.random.default_rng(rnd)
+    k = np.stack([pats[:, g.permutation(D)] for _ in range(Hkv)], axis=1)[None]   # [1][T][Hkv][D]
+    v = np.stack([pats[g.permutation(T)] for _ in range(Hkv)], axis=1)[None]
+    ks = np.asarray(SCALE_ROUNDS[rnd], np.float32)
+    vs = ks[::-1].copy()
+    cache = H.new_cache(w, inp.num_pages, ops.KV_FP8_E4M3, DEV, ks, vs)
+    dbatch, _, _ = H.upload_batch(inp.batch, inp.pool, DEV)
+    zero = np.zeros(1, np.int32)
+    count = np.array([T], np.int32)
+    ops.kv_quant_fill(cache, dbatch, torch.from_numpy(zero).to(DEV), torch.from_numpy(count).to(DEV),
+                      H.bf16_tensor(k, DEV), H.bf16_tensor(v, DEV))
+    ref = oracle.Pool(oracle.KV_FP8, inp.num_pages, Hkv, P, D, fill=H.FP8_NAN_CODE)
+    oracle.kv_write(ref, inp.batch.page_table, zero, count, k, v, ks, vs)
+    assert np.array_equal(cache.k_pool.cpu().numpy(), ref.k)
+    assert np.array_equal(cache.v_pool.cpu().numpy(), ref.v)
+
+
 # --- fused check + append, device-side reallocation ------------------------------------
 
 def _dev(a, dtype=np.int32):
