@@ -81,7 +81,7 @@ def parse_args():
 
 
 # the sources the counted attention launch is built and configured from
-ATTN_SOURCES = ("decode_attn.hip", "pafp8_device.hpp", "pafp8_internal.hpp", "api.hip")
+ATTN_SOURCES = ("decode_attn.hip", "pafp8_device.hpp", "attn_params.hpp")
 
 
 def source_hash() -> str:

@@ -35,8 +35,8 @@
 //    dot products with FMAs (lane = token for Q.K, lane = head dim for P.V).
 // Arithmetic: scores and outputs accumulate in fp32, softmax in the exp2
 // domain; the result is exact up to fp32 rounding.
+#include "attn_params.hpp"
 #include "pafp8_device.hpp"
-#include "pafp8_internal.hpp"
 
 namespace pafp8 {
 namespace {
