@@ -1,7 +1,9 @@
 """INT4 weight streaming on the GPU (int4_pack_weights, int4_gemv) against
-the oracle.  Tolerance: products are exact and summed in fp32, 128 per
-group and then over the groups, so
-    |y - exact| <= (K/128 + 129) * 2^-24 * sum_k |x q s|,
+the oracle.  Tolerance (the bound include/pafp8.h states): products are
+exact and summed in fp32, 128 per group and then over the groups, so
+    |y - exact| <= (K/128 + 160) * 2^-24 * sum_k |x| (|q| + c) s,
+with c = 0 from 2 rows of x up (MFMA path) and c = 272 for one row (the
+dot-product path sums x (136 + q) and takes 136 sum x back out),
 checked with a factor 2 of slack."""
 import numpy as np
 import pytest
@@ -42,13 +44,15 @@ def _case(M, N, K, seed):
 
 def _bound(q, x, s):
     N, K = q.shape
+    M = x.shape[0]
+    off = 272.0 if M % 64 == 1 else 0.0   # the launch that gets one row
     xa = np.abs(I.bf16_bits_to_f32(x).astype(np.float64))
     sf = I.bf16_bits_to_f32(s).astype(np.float64)
-    out = np.empty((x.shape[0], N))
+    out = np.empty((M, N))
     for n0 in range(0, N, 1024):                 # rows in chunks: bounded memory
-        wa = np.abs(q[n0:n0 + 1024].astype(np.float64)) * np.repeat(sf[:, n0:n0 + 1024], 128, axis=0).T
+        wa = (np.abs(q[n0:n0 + 1024].astype(np.float64)) + off) * np.repeat(sf[:, n0:n0 + 1024], 128, axis=0).T
         out[:, n0:n0 + 1024] = xa @ wa.T
-    return 2.0 * (K / 128 + 129) * 2.0 ** -24 * out
+    return 2.0 * (K / 128 + 160) * 2.0 ** -24 * out
 
 
 def test_pack_matches_documented_layout():
@@ -59,8 +63,9 @@ def test_pack_matches_documented_layout():
         assert np.array_equal(packed, int4_blocks(q)), (N, K)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 512), (5, 48, 512), (16, 64, 1024), (17, 80, 1536),
-                                   (33, 128, 512), (64, 256, 2048), (100, 32, 512), (3, 1008, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 16, 512), (2, 48, 1536), (1, 1008, 2048), (5, 48, 512),
+                                   (16, 64, 1024), (17, 80, 1536), (33, 128, 512), (64, 256, 2048),
+                                   (100, 32, 512), (66, 32, 512), (3, 1008, 1024)])
 def test_gemv_matches_oracle(M, N, K):
     say(f"int4 gemv: M={M} N={N} K={K}")
     q, x, s = _case(M, N, K, M * 1000 + N + K)
@@ -76,12 +81,12 @@ def test_gemv_full_size_decode_shape():
     """The measured shape (28672 x 8192): at one row every output against the
     oracle; at 64 rows, 16 sampled 16-row tiles of the output."""
     N, K = 28672, 8192
-    for M in (1, 64):
+    for M in (1, 2, 64):
         say(f"int4 gemv full size: M={M}")
         q, x, s = _case(M, N, K, 99 + M)
         packed = ops.int4_pack_weights(_dev_u8(int4_rowmajor(q)), N, K)
         y = ops.int4_gemv(_dev_bf16(x), packed, _dev_bf16(s), N, K).cpu().numpy()
-        if M == 1:
+        if M <= 2:
             rows = np.arange(N)
         else:
             tiles = np.random.default_rng(5).choice(N // 16, 16, replace=False)
