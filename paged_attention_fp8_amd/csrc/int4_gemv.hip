@@ -178,125 +178,110 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
 // run on v_dot2_f32_bf16 instead.  The weights are expanded with a shift and
 // one logic op per pair: ((w >> 4i) & 0x000F000F) ^ 0x43084308 is the bf16
 // pair (136 + q_i, 136 + q_{i+4}) of features i and i + 4 of the dword (the
-// nibble's top bit flipped turns q into q + 8 < 16, and 0x4300 is 128).  x is staged in LDS
-// with the same pairing, and each lane subtracts 136 times the sum of its own
-// x features per group (staged alongside) before applying the group's scale.
-// Lanes c, c+16, c+32, c+48 hold row c's four feature quarters and are summed
-// at the end.
-template <int M, int PF>
-__global__ __launch_bounds__(kGemvThreads) void int4_gemv_dot_kernel(
+// nibble's top bit flipped turns q into q + 8 < 16, and 0x4300 is 128).  x
+// is staged in LDS with the same pairing, and each lane subtracts 136 times
+// the sum of its own x features per group (staged alongside) before applying
+// the group's scale.
+//
+// A work-group owns one 16-row tile; its four waves take consecutive quarters
+// of K (in chunks of 4 groups), each with its own prefetch ring and its own
+// x staging, so no wave waits for another until the final sum.  Lanes c,
+// c+16, c+32, c+48 of every wave hold row c's four feature quarters of each
+// group.
+__global__ __launch_bounds__(kGemvThreads) void int4_gemv_row_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w, const uint16_t *__restrict__ scales,
     int N, int K, float *__restrict__ y)
 {
-    constexpr int XC = 4;                      // groups per staged x chunk
-    constexpr int PIECES = XC * kGroup / 8;    // 16-byte pieces of one row per chunk (64: one wave)
-    __shared__ __align__(16) uint32_t xs[2][M][XC * kGroup / 2];  // bf16 pairs (x_i, x_{i+4})
-    __shared__ float xsum[2][M][XC][4];                           // per (group, quarter kq)
+    constexpr int PF = 4;   // weight blocks in flight per wave (one chunk)
+    constexpr int XC = 4;   // groups per staged x chunk: one 16-byte piece per lane
+    __shared__ __align__(16) uint32_t xs[kGemvWaves][2][XC * kGroup / 2];  // bf16 pairs (x_i, x_{i+4})
+    __shared__ float xsum[kGemvWaves][2][XC][4];                           // per (group, quarter kq)
+    __shared__ float red[kGemvWaves][64];
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
-    const int n_tiles = N / 16;
-    const int nt = blockIdx.x * kGemvWaves + wave;
-    const bool live = nt < n_tiles;
+    const int nt = blockIdx.x;
     const int G = K / kGroup;
+    const int C = G / XC;                                   // chunks of K
+    const int c0 = wave * C / kGemvWaves, c1 = (wave + 1) * C / kGemvWaves;
     const int c = lane & 15, kq = lane >> 4;
+    const int g_first = c0 * XC, g_last = c1 * XC - 1;      // this wave's groups (none if c0 == c1)
 
-    // wave m < M stages row m: lane = piece c8 + 16 * group; unconditional loads
-    u32x4 xr = {0u, 0u, 0u, 0u};
+    u32x4 xr;
     auto load_x = [&](int ch) {
-        if (wave < M)
-            xr = load16(x + static_cast<int64_t>(wave) * K + static_cast<int64_t>(ch) * XC * kGroup + lane * 8);
+        xr = load16(x + static_cast<int64_t>(ch) * XC * kGroup + lane * 8);
     };
     auto store_x = [&](int buf) {
-        if (wave < M) {
-            // pairs (x_i, x_{i+4}) of the piece's 8 features
-            u32x4 v;
-            v[0] = __builtin_amdgcn_perm(xr[2], xr[0], 0x05040100u);
-            v[1] = __builtin_amdgcn_perm(xr[2], xr[0], 0x07060302u);
-            v[2] = __builtin_amdgcn_perm(xr[3], xr[1], 0x05040100u);
-            v[3] = __builtin_amdgcn_perm(xr[3], xr[1], 0x07060302u);
-            *reinterpret_cast<u32x4 *>(&xs[buf][wave][lane * 4]) = v;
-            // sum of the piece, then over the four pieces j of one quarter kq
-            float sum = 0.f;
+        u32x4 v;
+        v[0] = __builtin_amdgcn_perm(xr[2], xr[0], 0x05040100u);
+        v[1] = __builtin_amdgcn_perm(xr[2], xr[0], 0x07060302u);
+        v[2] = __builtin_amdgcn_perm(xr[3], xr[1], 0x05040100u);
+        v[3] = __builtin_amdgcn_perm(xr[3], xr[1], 0x07060302u);
+        *reinterpret_cast<u32x4 *>(&xs[wave][buf][lane * 4]) = v;
+        // sum of the piece, then over the four pieces j of one quarter kq
+        float sum = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sum += __uint_as_float(xr[i] << 16) + __uint_as_float(xr[i] & 0xFFFF0000u);
-            sum += shfl_xor_f(sum, 4);
-            sum += shfl_xor_f(sum, 8);
-            const int c8 = lane & 15;
-            if (c8 < 4)
-                xsum[buf][wave][lane >> 4][c8] = sum;
-        }
+        for (int i = 0; i < 4; ++i)
+            sum += __uint_as_float(xr[i] << 16) + __uint_as_float(xr[i] & 0xFFFF0000u);
+        sum += shfl_xor_f(sum, 4);
+        sum += shfl_xor_f(sum, 8);
+        const int c8 = lane & 15;
+        if (c8 < 4)
+            xsum[wave][buf][lane >> 4][c8] = sum;
     };
 
-    const uint8_t *wb = w + (static_cast<int64_t>(live ? nt : 0) * G) * 1024 + lane * 16;
-    const uint16_t *sp = scales + (live ? nt : 0) * 16 + c;
-    float tot[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-        tot[m] = 0.f;
-    u32x4 wr[PF];
-    uint32_t sr[PF];
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-        const int gl = u < G ? u : G - 1;
-        wr[u] = load16_stream(wb + static_cast<int64_t>(gl) * 1024);
-        sr[u] = static_cast<uint32_t>(sp[static_cast<int64_t>(gl) * N]);
-    }
-    load_x(0);
-    store_x(0);
-    __syncthreads();
-
-    for (int g0 = 0; g0 < G; g0 += PF) {
+    float tot = 0.f;
+    if (c0 < c1) {
+        const uint8_t *wb = w + static_cast<int64_t>(nt) * G * 1024 + lane * 16;
+        const uint16_t *sp = scales + nt * 16 + c;
+        u32x4 wr[PF];
+        uint32_t sr[PF];
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-            const int g = g0 + u;
-            const int ch = g / XC;
-            const int last_ch = G / XC - 1;
-            if (u % XC == 0) {
-                load_x(ch + 1 <= last_ch ? ch + 1 : last_ch);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const u32x4 wq = wr[u];
-            const float s = __uint_as_float(sr[u] << 16);
-            {
-                const int gl = g + PF < G ? g + PF : G - 1;
-                wr[u] = load16_stream(wb + static_cast<int64_t>(gl) * 1024);
-                sr[u] = static_cast<uint32_t>(sp[static_cast<int64_t>(gl) * N]);
-            }
-            const int buf = ch & 1, gi = u % XC;
-            float acc[M];
+            wr[u] = load16_stream(wb + static_cast<int64_t>(g_first + u) * 1024);
+            sr[u] = static_cast<uint32_t>(sp[static_cast<int64_t>(g_first + u) * N]);
+        }
+        load_x(c0);
+        store_x(0);
+        for (int ch = c0; ch < c1; ++ch) {
+            const int buf = (ch - c0) & 1;
+            load_x(ch + 1 < c1 ? ch + 1 : ch);   // unconditional: clamped into this wave's range
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int m = 0; m < M; ++m)
-                acc[m] = 0.f;
+            for (int u = 0; u < PF; ++u) {
+                const int g = ch * XC + u;
+                const u32x4 wq = wr[u];
+                const float s = __uint_as_float(sr[u] << 16);
+                {
+                    const int gl = g + PF <= g_last ? g + PF : g_last;
+                    wr[u] = load16_stream(wb + static_cast<int64_t>(gl) * 1024);
+                    sr[u] = static_cast<uint32_t>(sp[static_cast<int64_t>(gl) * N]);
+                }
+                float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < 4; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // (u & 15) ^ 8 | 0x4300 == (u & 15) ^ 0x4308: one 3-input logic op
-                    const uint32_t t = ((wq[j] >> (4 * i)) & 0x000F000Fu) ^ 0x43084308u;
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        const uint32_t xp = xs[buf][m][gi * 64 + (4 * j + kq) * 4 + i];
-                        acc[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, t),
-                                                                 __builtin_bit_cast(bf16x2, xp), acc[m], false);
+                    for (int i = 0; i < 4; ++i) {
+                        // (u & 15) ^ 8 | 0x4300 == (u & 15) ^ 0x4308: one 3-input logic op
+                        const uint32_t t = ((wq[j] >> (4 * i)) & 0x000F000Fu) ^ 0x43084308u;
+                        const uint32_t xp = xs[wave][buf][u * 64 + (4 * j + kq) * 4 + i];
+                        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, t),
+                                                              __builtin_bit_cast(bf16x2, xp), acc, false);
                     }
                 }
+                tot = __builtin_fmaf(s, acc - 136.0f * xsum[wave][buf][u][kq], tot);
             }
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-                tot[m] = __builtin_fmaf(s, acc[m] - 136.0f * xsum[buf][m][gi][kq], tot[m]);
-            if (u % XC == XC - 1) {
-                store_x((ch + 1) & 1);
-                __syncthreads();
-            }
+            // the wave's own LDS: its DS operations run in order, no barrier
+            store_x(buf ^ 1);
         }
     }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        float v = tot[m] + shfl_xor_f(tot[m], 16);
+    red[wave][lane] = tot;
+    __syncthreads();
+    if (wave == 0) {
+        float v = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+        v += shfl_xor_f(v, 16);
         v += shfl_xor_f(v, 32);
-        if (live && kq == 0)
-            y[static_cast<int64_t>(m) * N + nt * 16 + c] = v;
+        if (kq == 0)
+            y[nt * 16 + c] = v;
     }
 }
 
@@ -331,11 +316,8 @@ hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const ui
     const int mt = (M + 15) / 16;
     const bool pf8 = (K / kGroup) % 8 == 0;   // K % 512 == 0 gives a multiple of 4
     if (M == 1) {
-#define PAFP8_DOT(M_)                                                                             \
-        hipLaunchKernelGGL((int4_gemv_dot_kernel<M_, 4>), grid, dim3(kGemvThreads), 0, stream, x, w, \
+        hipLaunchKernelGGL(int4_gemv_row_kernel, dim3(n_tiles), dim3(kGemvThreads), 0, stream, x, w,
                            scales, N, K, y);
-        PAFP8_DOT(1)
-#undef PAFP8_DOT
         return hipGetLastError();
     }
 #define PAFP8_GEMV(MT_)                                                                            \
