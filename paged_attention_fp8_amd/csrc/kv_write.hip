@@ -4,9 +4,9 @@
 // Cloudflare, "Smaller, faster, safer: running Kimi and GLM at scale",
 // section "KV 缓存量化" (KV cache quantization): decode stores K/V as FP8
 // e4m3 instead of BF16 (half the bytes), while prefill keeps BF16.  The same
-// kernel serves the decode step's append (one token per request, at position
-// context_lens[b] - 1) and the prefill-to-decode hand-off (a block of tokens
-// per request).
+// encoder serves the decode step's append (one token per request, at
+// position context_lens[b] - 1) and the prefill-to-decode hand-off (a block
+// of tokens per request); each has its kernel.
 //
 // Append (one token per request): one work-group per (request, KV head),
 // thread d owning head dimension d.  The checked variant first derives the
