@@ -544,11 +544,15 @@ def main():
             "kernel": "decode_attn_mfma_kernel<e4m3, 128>",
             "algorithmic_bytes_per_launch": p.bytes,
             "launch_ms_mean": attn_ms,
+            "launch_ms_median": statistics.median(r["attn_ms"]),
             "launch_ms_p10_p90": [sorted(r["attn_ms"])[len(r["attn_ms"]) // 10],
                                   sorted(r["attn_ms"])[(9 * len(r["attn_ms"])) // 10]],
         },
         "context_tokens_per_s": float(sum(int(L) for L in p.lens)) / (attn_ms * 1e-3),
     }
+    if result["roofline"]["traffic"] is not None:
+        # the counters' HBM bytes over the same mean launch time
+        result["roofline"]["traffic_GBps"] = result["roofline"]["traffic"] / (attn_ms * 1e-3) / 1e9
     if not args.no_extras:
         r0 = p.run(args.steps, args.warmup, args.splits, check=False)
         result["check_overhead_pct"] = 100.0 * (r["ms_per_step"] - r0["ms_per_step"]) / r0["ms_per_step"]
