@@ -431,7 +431,7 @@ __device__ __forceinline__ void merge_and_write(const AttnParams &p, MergeSmem<D
 }
 
 template <bool BF16, int D, bool BIG>
-__global__ __launch_bounds__(kThreads, 3) void decode_attn_mfma_kernel(AttnParams p)
+__global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel(AttnParams p)
 {
     using G_ = Geo<BF16, D>;
     __shared__ MergeSmem<D> sm;
