@@ -100,7 +100,8 @@ typedef struct pafp8_cache {
     void *k_pool;          /* device, K pool */
     void *v_pool;          /* device, V pool */
     const float *k_scale;  /* device [num_kv_heads]: value = decode(code) * k_scale[g]; e4m3 only */
-    const float *v_scale;  /* device [num_kv_heads]; e4m3 only.  Scales must be positive and finite. */
+    const float *v_scale;  /* device [num_kv_heads]; e4m3 only.  Scales must be finite and
+                              non-zero; others give unspecified codes. */
 } pafp8_cache;
 
 /* One decode step's batch: each request's logical-to-physical page mapping. */

@@ -56,53 +56,83 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t x) { return __uint_as
 // rounded as an IEEE single-precision division would round it.
 //
 // For scales in [2^-64, 2^64] the quotient is formed from the reciprocal and
-// one FMA correction (r = 1/s rounded, q0 = |x|*r, e = |x| - q0*s exactly,
-// q = q0 + e*r; Markstein's correction step), with |x| first clamped to
-// 1024*s (anything larger saturates either way) and the sign copied back.
-// An exhaustive comparison with IEEE division over every bf16 significand and
-// every fp32 scale significand, plus random signs and exponents over that
-// scale range, found no difference; outside the range, or for zero, infinite
-// or NaN scales, the kernels divide.
+// one FMA correction (Markstein's step: r = 1/s rounded, q0 = x*r rounded,
+// t = q0*s - x exactly, q = q0 - t*r), after clamping x to +-c, c = 440*s
+// rounded.  Every |x| >= c lies above 432*s, where the code is the one of 448
+// whatever the exact quotient, and the clamped quotient never exceeds 448, so
+// the conversion needs no clamp of its own.  Forming the remainder as
+// q0*s - x and subtracting it keeps the sign of a zero quotient.
+//
+// Any other finite non-zero scale (negative ones included) is first written
+// as |s| = m 2^e with m in [1, 2); x / s equals ldexp(+-x, -e) / m exactly
+// unless the rescaled x overflows (then the code saturates either way) or
+// underflows (then the quotient is below 2^-126 and its code is a zero of
+// the right sign either way), and the same steps run on the rescaled pair.
+// Zero, infinite and NaN scales give unspecified codes.
+//
+// An exhaustive CPU comparison with IEEE division (every bf16 significand of
+// both signs against every fp32 scale significand, every value of the clamp
+// region, random values against random scales over the range and, rescaled,
+// outside it) found no difference in the quotient where no clamp acts and
+// none in the code anywhere.  NaN inputs are patched afterwards
+// (e4m3_nan_byte).
 // ---------------------------------------------------------------------------
 struct E4m3Quantizer {
-    float s, r, lim;
-    bool fast;
+    float s, r, lim;   // divisor (the scale, or m), its reciprocal, the clamp
+    int shift;         // exponent added to x before dividing (rescaled form)
+    uint32_t sign;     // sign bit flipped on x (rescaled form, negative scales)
+    bool fast;         // s in [2^-64, 2^64]: no rescaling
 };
 
 __device__ __forceinline__ E4m3Quantizer make_quantizer(float s)
 {
     E4m3Quantizer q;
-    q.s = s;
-    q.r = 1.0f / s;
-    q.lim = 1024.0f * s;
     q.fast = s >= 0x1p-64f && s <= 0x1p64f;
+    q.shift = 0;
+    q.sign = 0u;
+    q.s = s;
+    if (!q.fast) {
+        const float a = __builtin_fabsf(s);
+        q.s = 2.0f * __builtin_amdgcn_frexp_mantf(a);          // [1, 2) for finite non-zero s
+        q.shift = 1 - __builtin_amdgcn_frexp_expf(a);
+        q.sign = __float_as_uint(s) & 0x80000000u;
+    }
+    q.r = 1.0f / q.s;
+    q.lim = 440.0f * q.s;
     return q;
 }
 
-__device__ __forceinline__ float quotient_fast(float x, const E4m3Quantizer &q)
+// the quotient, ready for the conversion (|result| <= 448 unless x is NaN)
+template <bool FAST>
+__device__ __forceinline__ float quotient(float x, const E4m3Quantizer &q)
 {
-    const float a = __builtin_fminf(__builtin_fabsf(x), q.lim);
-    const float q0 = a * q.r;
-    const float e = __builtin_fmaf(-q0, q.s, a);
-    const float d = __builtin_copysignf(__builtin_fmaf(e, q.r, q0), x);
-    return x != x ? x : d;
+    if constexpr (!FAST)
+        x = __builtin_amdgcn_ldexpf(__uint_as_float(__float_as_uint(x) ^ q.sign), q.shift);
+    const float xc = __builtin_amdgcn_fmed3f(x, -q.lim, q.lim);
+    const float q0 = xc * q.r;
+    const float t = __builtin_fmaf(q0, q.s, -xc);
+    return __builtin_fmaf(-t, q.r, q0);
+}
+
+// two quotients -> two codes in half HI of w (the other half kept)
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t w)
+{
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, static_cast<int>(w), HI));
+}
+
+// byte i of w replaced by the NaN code of x when x is NaN
+__device__ __forceinline__ uint32_t e4m3_patch_nan(uint32_t w, int i, float x)
+{
+    return x != x ? (w & ~(0xFFu << (8 * i))) | (e4m3_nan_byte(x) << (8 * i)) : w;
 }
 
 __device__ __forceinline__ uint32_t quantize_bf16(uint16_t x, const E4m3Quantizer &q)
 {
     const float xf = bf16_bits_to_f32(x);
-    return e4m3_encode(q.fast ? quotient_fast(xf, q) : xf / q.s);
-}
-
-// Four bf16 (two dwords, element 0 in the low half of w0) -> four codes.
-__device__ __forceinline__ uint32_t quantize_bf16x4(uint32_t w0, uint32_t w1, const E4m3Quantizer &q)
-{
-    const float x0 = bf16_bits_to_f32(w0 & 0xFFFFu), x1 = bf16_bits_to_f32(w0 >> 16);
-    const float x2 = bf16_bits_to_f32(w1 & 0xFFFFu), x3 = bf16_bits_to_f32(w1 >> 16);
-    if (q.fast)
-        return e4m3_encode4(quotient_fast(x0, q), quotient_fast(x1, q), quotient_fast(x2, q),
-                            quotient_fast(x3, q));
-    return e4m3_encode4(x0 / q.s, x1 / q.s, x2 / q.s, x3 / q.s);
+    const float v = q.fast ? quotient<true>(xf, q) : quotient<false>(xf, q);
+    const uint32_t w = e4m3_pack2<false>(v, 0.0f, 0u) & 0xFFu;
+    return xf != xf ? e4m3_nan_byte(xf) : w;
 }
 
 }  // namespace pafp8

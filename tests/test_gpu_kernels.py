@@ -216,9 +216,11 @@ def test_append_skips_aborted_and_invalid_lengths():
 
 
 SCALE_ROUNDS = [
-    # fast-path scales, its boundaries, and scales outside it (exact division)
+    # fast-path scales, its boundaries, and scales outside it (rescaled form)
     [1.0, 3.7e-3, 0.0137, 2.0 ** -64, 2.0 ** 64, 2.0 ** -70, 5e30, 1.5e-20],
     [0.5, 1.0 / 448, 7.77, 2.0 ** -63.5, 2.0 ** 63.9, 1e-30, 2.0 ** 70, 0.1],
+    # negative scales, subnormal scales, the largest finite ones
+    [-1.0, -3.7e-3, 1e-40, -2.0 ** 100, 3.0e38, -1e-38, 2.0 ** -126, 2.0 ** -149],
 ]
 
 

@@ -1,9 +1,11 @@
 """The quantising kernels form e4m3(f32(x) / s) with a reciprocal and one
-FMA correction for scales in [2^-64, 2^64]; the encoding is defined on the
-IEEE single-precision quotient.  This compiles and runs an exhaustive and
-randomised comparison of that method with IEEE division on the CPU (gcc,
-no fast-math, no contraction).  The kernels themselves are compared with the
-oracle, which divides, by the GPU tests."""
+FMA correction for scales in [2^-64, 2^64], after clamping x to +-RN(440 s);
+the encoding is defined on the IEEE single-precision quotient.  This
+compiles and runs an exhaustive and randomised comparison of that method
+with IEEE division on the CPU (gcc, no fast-math, no contraction): the
+quotient bit for bit where no clamp acts, the e4m3 code and |q| <= 448
+everywhere.  The kernels themselves are compared with the oracle, which
+divides, by the GPU tests."""
 import os
 import subprocess
 
