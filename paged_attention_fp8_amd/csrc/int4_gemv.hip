@@ -52,10 +52,26 @@ __device__ __forceinline__ bf16x8 int4x8_to_bf16_div16(uint32_t w)
     return r;
 }
 
+// 8 int4 weights (one dword) -> the bf16 pairs (136 + q_i, 136 + q_{i+4}),
+// i = 0..3: ((w >> 4i) & 0x000F000F) ^ 0x43084308 flips the nibble's top bit
+// (q + 8 < 16) and puts it under the exponent of 128, a shift and one logic
+// operation per pair
+__device__ __forceinline__ bf16x8 int4x8_to_bf16_plus136(uint32_t w)
+{
+    u32x4 t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        t[i] = ((w >> (4 * i)) & 0x000F000Fu) ^ 0x43084308u;
+    return __builtin_bit_cast(bf16x8, t);
+}
+
 // MT: 16-row tiles of x; PF: weight blocks in flight per wave, a divisor of
 // K / 128 (so the unrolled group loop needs no early exit, which would let
-// the compiler sink the x loads to their use)
-template <int MT, int PF>
+// the compiler sink the x loads to their use).  PLUS136: weights expanded as
+// 136 + q (fewer VALU operations, features of each 8-block paired (i, i+4) in
+// both operands) and the 136 taken back out by MFMAs of the same x against a
+// constant -136, which the matrix cores absorb while they idle at few rows.
+template <int MT, int PF, bool PLUS136>
 __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ w,
     const uint16_t *__restrict__ scales, int N, int K, float *__restrict__ y)
@@ -93,7 +109,14 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
         for (int it = 0; it < XP; ++it) {
             const int idx = tid + it * kGemvThreads;
             const int m = idx / (XC * kGroup / 8), c8 = idx % (XC * kGroup / 8);
-            const u32x4 v = m < M ? xr[it] : u32x4{0u, 0u, 0u, 0u};
+            u32x4 v = m < M ? xr[it] : u32x4{0u, 0u, 0u, 0u};
+            if (PLUS136) {
+                const u32x4 a = v;
+                v[0] = __builtin_amdgcn_perm(a[2], a[0], 0x05040100u);   // features 0, 4
+                v[1] = __builtin_amdgcn_perm(a[2], a[0], 0x07060302u);   // 1, 5
+                v[2] = __builtin_amdgcn_perm(a[3], a[1], 0x05040100u);   // 2, 6
+                v[3] = __builtin_amdgcn_perm(a[3], a[1], 0x07060302u);   // 3, 7
+            }
             *reinterpret_cast<u32x4 *>(&xs[buf][m * XS + c8 * 8]) = v;
         }
     };
@@ -134,8 +157,8 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
             bf16x8 bop[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bop[j] = int4x8_to_bf16_div16(wr[u][j]);
-            const float s16 = 16.0f * __uint_as_float(sr[u] << 16);
+                bop[j] = PLUS136 ? int4x8_to_bf16_plus136(wr[u][j]) : int4x8_to_bf16_div16(wr[u][j]);
+            const float s16 = (PLUS136 ? 1.0f : 16.0f) * __uint_as_float(sr[u] << 16);
             {
                 const int gl = g + PF < G ? g + PF : G - 1;
                 wr[u] = load16_stream(wb + static_cast<int64_t>(gl) * 1024);
@@ -149,6 +172,11 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
                 for (int j = 0; j < 4; ++j) {
                     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xa + mt * 16 * XS + 32 * j);
                     part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[j], part, 0, 0, 0);
+                    if (PLUS136) {
+                        const bf16x8 neg136 = __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u,
+                                                                               0xC308C308u, 0xC308C308u});
+                        part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, neg136, part, 0, 0, 0);
+                    }
                 }
                 acc[mt] += s16 * part;
             }
@@ -322,11 +350,11 @@ hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const ui
     }
 #define PAFP8_GEMV(MT_)                                                                            \
     if (pf8)                                                                                       \
-        hipLaunchKernelGGL((int4_gemv_kernel<MT_, 8>), grid, dim3(kGemvThreads), 0, stream, x, M, w, \
-                           scales, N, K, y);                                                       \
+        hipLaunchKernelGGL((int4_gemv_kernel<MT_, 8, (MT_ <= 2)>), grid, dim3(kGemvThreads), 0, stream, \
+                           x, M, w, scales, N, K, y);                                             \
     else                                                                                           \
-        hipLaunchKernelGGL((int4_gemv_kernel<MT_, 4>), grid, dim3(kGemvThreads), 0, stream, x, M, w, \
-                           scales, N, K, y);
+        hipLaunchKernelGGL((int4_gemv_kernel<MT_, 4, (MT_ <= 2)>), grid, dim3(kGemvThreads), 0, stream, \
+                           x, M, w, scales, N, K, y);
     if (mt == 1) {
         PAFP8_GEMV(1)
     } else if (mt == 2) {
