@@ -12,6 +12,8 @@ Workloads (named by what they are):
                       bf16 twin at 32 requests (1 sampled request)
   gqa8_256k_b4        4 requests x 262144 tokens, 64 splits, one stale request that must
                       be aborted (1 sampled request, one KV group)
+  handoff_8k_b8       kv_quant_fill of 8 prompts x 8192 tokens into e4m3 pages (whole
+                      pools byte for byte)
 For sampled requests the pool pages they own must equal the oracle's byte for
 byte, and every output within 2e-3 abs + 1e-2 rel.
 """
@@ -171,3 +173,32 @@ def test_long_context_256k_with_stale_request():
     assert np.all(out[bad] == 0) and np.all(np.isneginf(lse[bad]))
     good = [b for b in range(4) if b != bad]
     check_sampled(step, inp, ops.KV_FP8_E4M3, out, lse, [good[0]], heads=range(8, 16))
+
+
+def test_prefill_handoff_full_size_pools_bit_exact():
+    """The prefill-to-decode hand-off the bench times (8 prompts x 8192 bf16
+    tokens, 8 KV heads, d128, 64-token pages -> e4m3; one kv_quant_fill
+    launch): both pools byte for byte against the oracle.  A second fill of
+    the same sources at ragged starts and counts (partial tiles and groups in
+    every request) into a fresh pool, likewise."""
+    w = I.Workload("handoff_8k_b8", 8, 64, 8, 128, 64, 8192, 8192, pool_factor=1.0)
+    say(f"workload {w.name}")
+    inp = I.make_device_decode_inputs(w, 1006, DEV)
+    B, T = w.batch, w.max_len
+    k, v = inp.k_tokens[:, :T].contiguous(), inp.v_tokens[:, :T].contiguous()
+    kh, vh = host_bits(k), host_bits(v)
+    dbatch, _, _ = H.upload_batch(inp.batch, inp.pool, DEV)
+    g = np.random.default_rng(6)
+    cases = [(np.zeros(B, np.int32), np.full(B, T, np.int32))]
+    cases.append((g.integers(0, 200, B).astype(np.int32), g.integers(T - 700, T - 200, B).astype(np.int32)))
+    for start, count in cases:
+        cache = H.new_cache(w, inp.num_pages, ops.KV_FP8_E4M3, DEV, inp.k_scale, inp.v_scale)
+        ops.kv_quant_fill(cache, dbatch, torch.from_numpy(start).to(DEV), torch.from_numpy(count).to(DEV), k, v)
+        ref = oracle.Pool(oracle.KV_FP8, inp.num_pages, w.kv_heads, w.page_size, w.head_dim,
+                          fill=H.FP8_NAN_CODE)
+        oracle.kv_write(ref, inp.batch.page_table, start, count, kh, vh, inp.k_scale, inp.v_scale)
+        assert np.array_equal(cache.k_pool.cpu().numpy(), ref.k)
+        assert np.array_equal(cache.v_pool.cpu().numpy(), ref.v)
+        say(f"  starts {start[:3]}..., counts {count[:3]}...: pools bit-exact")
+        del cache, ref
+        torch.cuda.empty_cache()
