@@ -202,20 +202,17 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
         }
 }
 
-// One row of x: the MFMA tiles would be 15/16 padding, so the dot products
-// run on v_dot2_f32_bf16 instead.  The weights are expanded with a shift and
-// one logic op per pair: ((w >> 4i) & 0x000F000F) ^ 0x43084308 is the bf16
-// pair (136 + q_i, 136 + q_{i+4}) of features i and i + 4 of the dword (the
-// nibble's top bit flipped turns q into q + 8 < 16, and 0x4300 is 128).  x
-// is staged in LDS with the same pairing, and each lane subtracts 136 times
-// the sum of its own x features per group (staged alongside) before applying
-// the group's scale.
+// One row of x.  The weights expand as in the PLUS136 path (bf16 pairs
+// (136 + q_i, 136 + q_{i+4}), x staged in the same pairing) and x is
+// broadcast to all 16 rows of the MFMA's A operand, so every output row of
+// the MFMA is y's row and lanes 0..15 read it off; a second MFMA of the same
+// x against a constant -136 takes the offset back out.  Against dot-product
+// instructions on the VALU this halves the VALU work per weight, and the
+// matrix cores, otherwise idle, absorb the rest.
 //
 // A work-group owns one 16-row tile; its four waves take consecutive quarters
 // of K (in chunks of 4 groups), each with its own prefetch ring and its own
-// x staging, so no wave waits for another until the final sum.  Lanes c,
-// c+16, c+32, c+48 of every wave hold row c's four feature quarters of each
-// group.
+// x staging, so no wave waits for another until the final sum.
 __global__ __launch_bounds__(kGemvThreads) void int4_gemv_row_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w, const uint16_t *__restrict__ scales,
     int N, int K, float *__restrict__ y)
@@ -223,8 +220,7 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_row_kernel(
     constexpr int PF = 4;   // weight blocks in flight per wave (one chunk)
     constexpr int XC = 4;   // groups per staged x chunk: one 16-byte piece per lane
     __shared__ __align__(16) uint32_t xs[kGemvWaves][2][XC * kGroup / 2];  // bf16 pairs (x_i, x_{i+4})
-    __shared__ float xsum[kGemvWaves][2][XC][4];                           // per (group, quarter kq)
-    __shared__ float red[kGemvWaves][64];
+    __shared__ float red[kGemvWaves][16];
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int nt = blockIdx.x;
@@ -233,6 +229,7 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_row_kernel(
     const int c0 = wave * C / kGemvWaves, c1 = (wave + 1) * C / kGemvWaves;
     const int c = lane & 15, kq = lane >> 4;
     const int g_first = c0 * XC, g_last = c1 * XC - 1;      // this wave's groups (none if c0 == c1)
+    const bf16x8 neg136 = __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
 
     u32x4 xr;
     auto load_x = [&](int ch) {
@@ -240,21 +237,11 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_row_kernel(
     };
     auto store_x = [&](int buf) {
         u32x4 v;
-        v[0] = __builtin_amdgcn_perm(xr[2], xr[0], 0x05040100u);
-        v[1] = __builtin_amdgcn_perm(xr[2], xr[0], 0x07060302u);
-        v[2] = __builtin_amdgcn_perm(xr[3], xr[1], 0x05040100u);
-        v[3] = __builtin_amdgcn_perm(xr[3], xr[1], 0x07060302u);
+        v[0] = __builtin_amdgcn_perm(xr[2], xr[0], 0x05040100u);   // features 0, 4
+        v[1] = __builtin_amdgcn_perm(xr[2], xr[0], 0x07060302u);   // 1, 5
+        v[2] = __builtin_amdgcn_perm(xr[3], xr[1], 0x05040100u);   // 2, 6
+        v[3] = __builtin_amdgcn_perm(xr[3], xr[1], 0x07060302u);   // 3, 7
         *reinterpret_cast<u32x4 *>(&xs[wave][buf][lane * 4]) = v;
-        // sum of the piece, then over the four pieces j of one quarter kq
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            sum += __uint_as_float(xr[i] << 16) + __uint_as_float(xr[i] & 0xFFFF0000u);
-        sum += shfl_xor_f(sum, 4);
-        sum += shfl_xor_f(sum, 8);
-        const int c8 = lane & 15;
-        if (c8 < 4)
-            xsum[wave][buf][lane >> 4][c8] = sum;
     };
 
     float tot = 0.f;
@@ -284,33 +271,26 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_row_kernel(
                     wr[u] = load16_stream(wb + static_cast<int64_t>(gl) * 1024);
                     sr[u] = static_cast<uint32_t>(sp[static_cast<int64_t>(gl) * N]);
                 }
-                float acc = 0.f;
+                // lane (c, kq) feeds features 32j + 8kq .. + 8 of the group
+                f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        // (u & 15) ^ 8 | 0x4300 == (u & 15) ^ 0x4308: one 3-input logic op
-                        const uint32_t t = ((wq[j] >> (4 * i)) & 0x000F000Fu) ^ 0x43084308u;
-                        const uint32_t xp = xs[wave][buf][u * 64 + (4 * j + kq) * 4 + i];
-                        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, t),
-                                                              __builtin_bit_cast(bf16x2, xp), acc, false);
-                    }
+                    const bf16x8 a = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4 *>(&xs[wave][buf][(u * 16 + 4 * j + kq) * 4]));
+                    part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, int4x8_to_bf16_plus136(wq[j]), part, 0, 0, 0);
+                    part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, neg136, part, 0, 0, 0);
                 }
-                tot = __builtin_fmaf(s, acc - 136.0f * xsum[wave][buf][u][kq], tot);
+                tot = __builtin_fmaf(s, part[0], tot);   // part[i]: output row 4kq + i, column c
             }
             // the wave's own LDS: its DS operations run in order, no barrier
             store_x(buf ^ 1);
         }
     }
-    red[wave][lane] = tot;
+    if (kq == 0)
+        red[wave][c] = tot;
     __syncthreads();
-    if (wave == 0) {
-        float v = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-        v += shfl_xor_f(v, 16);
-        v += shfl_xor_f(v, 32);
-        if (kq == 0)
-            y[nt * 16 + c] = v;
-    }
+    if (wave == 0 && lane < 16)
+        y[nt * 16 + c] = red[0][c] + red[1][c] + red[2][c] + red[3][c];
 }
 
 // row-major int4 [N][K/2] -> packed blocks: a permutation of 4-byte words
