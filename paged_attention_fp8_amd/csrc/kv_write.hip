@@ -13,10 +13,12 @@
 // request's page-tag verdict (every work-group of the request computes the
 // same value) and writes nothing for a request that fails it.
 //
-// Fill (a block of tokens per request): one work-group per (request, aligned
-// 64-position tile, KV head), no LDS: K rows are quantised in registers and
-// stored as 8-byte halves of their chunks, and V is transposed by pairing the
-// quantised values of one head dim across tokens in the packed conversion.
+// Fill (a block of tokens per request): work-groups per (request, aligned
+// 64-position tile, KV head) and pool.  K rows are quantised in registers and
+// stored as 8-byte halves of their chunks; V is transposed by pairing the
+// quantised values of one head dim across tokens in the packed conversion,
+// and in a whole e4m3 tile of a page of 64 tokens or more its rows are
+// assembled in LDS so that they leave as 1 KiB runs.
 #include "pafp8_device.hpp"
 #include "pafp8_internal.hpp"
 #include "pafp8_quant.hpp"
