@@ -105,6 +105,7 @@ __global__ __launch_bounds__(D) void kv_append_kernel(WriteParams p)
 constexpr int kFillTile = 64;
 constexpr int kFillWaves = 4;
 constexpr uint32_t kNoWrite = 0x80000000u;   // at or past every descriptor's range
+constexpr int kStreamLoad = 2;                // buffer load policy: non-temporal (the source is read once)
 constexpr int kFillLdsRow = 80;               // bytes per head dim of the V tile in LDS
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const void *base)
@@ -155,9 +156,9 @@ __device__ __forceinline__ void fill_k_group(const FillGroup &f, float scale, in
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         if (WHOLE)
-            x[i] = __builtin_amdgcn_raw_buffer_load_b128(src, rr * f.row_bytes + pc * 16, i * RPI * f.row_bytes, 0);
+            x[i] = __builtin_amdgcn_raw_buffer_load_b128(src, rr * f.row_bytes + pc * 16, i * RPI * f.row_bytes, kStreamLoad);
         else
-            x[i] = __builtin_amdgcn_raw_buffer_load_b128(src, fill_src_row(f, i * RPI + rr) + pc * 16, 0, 0);
+            x[i] = __builtin_amdgcn_raw_buffer_load_b128(src, fill_src_row(f, i * RPI + rr) + pc * 16, 0, kStreamLoad);
     }
     u32x2 w[NI];
     if (!BF16) {
@@ -223,9 +224,9 @@ __device__ __forceinline__ void fill_v_group(const FillGroup &f, float scale, in
         const uint32_t voff = static_cast<uint32_t>(d0 * 2);
         const uint32_t soff = WHOLE ? static_cast<uint32_t>(t * f.row_bytes) : fill_src_row(f, t);
         if (DPL == 2)
-            x[t] = __builtin_amdgcn_raw_buffer_load_b32(src, voff, soff, 0);
+            x[t] = __builtin_amdgcn_raw_buffer_load_b32(src, voff, soff, kStreamLoad);
         else
-            x[t] = __builtin_amdgcn_raw_buffer_load_b16(src, voff, soff, 0);
+            x[t] = __builtin_amdgcn_raw_buffer_load_b16(src, voff, soff, kStreamLoad);
     }
     if (BF16) {
         // a dword of the run holds tokens 2m (low half) and 2m + 1
