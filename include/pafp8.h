@@ -205,7 +205,8 @@ pafp8_status page_tag_realloc(int32_t n, const int32_t *page_ids, const int32_t 
  *   src_tokens                T, the row count of the source arrays (>= 1)
  *   k_src, v_src              device bf16 [B][T][num_kv_heads][head_dim],
  *                             16-byte aligned
- * Requires token_count[b] <= T (larger counts are clipped to T).  Positions
+ * Requires token_count[b] <= T (larger counts are clipped to T) and
+ * num_kv_heads * head_dim <= 2^25 (PAFP8_EUNSUPPORTED otherwise).  Positions
  * outside [0, max_pages_per_req * page_size), page ids outside the pool and
  * requests with a non-zero batch->req_status are skipped.  context_lens is
  * not read.  Bit-exact.

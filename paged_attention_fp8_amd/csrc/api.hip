@@ -234,6 +234,10 @@ pafp8_status write_impl(const pafp8_cache *cache, const pafp8_batch *batch, bool
             return fail(PAFP8_EINVAL, "src_tokens = %d < 1", T);
         if (!aligned16(k_src) || !aligned16(v_src))
             return fail(PAFP8_EINVAL, "k_src and v_src must be 16-byte aligned");
+        // the fill addresses 16 source rows from one base with 32-bit offsets
+        if (static_cast<int64_t>(cache->num_kv_heads) * cache->head_dim > (int64_t{1} << 25))
+            return fail(PAFP8_EUNSUPPORTED, "num_kv_heads * head_dim = %lld exceeds 2^25 for kv_quant_fill",
+                        static_cast<long long>(cache->num_kv_heads) * cache->head_dim);
     }
     pafp8::WriteParams p{};
     p.k_pool = static_cast<uint8_t *>(cache->k_pool);

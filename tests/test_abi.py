@@ -144,6 +144,9 @@ def test_other_entry_points_validate_without_gpu(L):
     assert L.kv_quant_append(ctypes.byref(c), ctypes.byref(b), None, 64, None) == 1
     assert L.kv_quant_fill(ctypes.byref(c), ctypes.byref(b), None, 64, 8, 64, 64, None) == 1
     assert L.kv_quant_fill(ctypes.byref(c), ctypes.byref(b), 64, 64, 0, 64, 64, None) == 1
+    wide = _cache(num_kv_heads=1 << 19)     # 2^19 heads x 128 dims: 16 source rows exceed 1 GiB
+    assert L.kv_quant_fill(ctypes.byref(wide), ctypes.byref(b), 64, 64, 8, 64, 64, None) == 2
+    assert b"2^25" in L.pafp8_last_error()
     assert L.page_tag_check(ctypes.byref(_batch(batch=-1)), 64, 64, 10, 64, 64, None) == 1
     assert L.page_tag_check(ctypes.byref(b), 24, 64, 10, 64, 64, None) == 2
     assert L.page_tag_check(ctypes.byref(b), 64, 64, 10, None, 64, None) == 1
