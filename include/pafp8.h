@@ -28,6 +28,9 @@
  *    never keeps a pointer after the call returns.  Calls are asynchronous on
  *    the caller's HIP stream; outputs are valid once that stream has reached
  *    the call.  Pointers marked "host" are read before the call returns.
+ *  - A call launches kernels on that stream and does nothing else (no
+ *    allocation, no memset, no synchronisation), so it may be captured in a
+ *    HIP graph; replays then read the buffers the captured call was given.
  *  - A call that finds a problem on the host (NULL pointer, bad size,
  *    unsupported shape, workspace too small) returns a status other than
  *    PAFP8_OK and launches nothing; pafp8_last_error() then describes it.
