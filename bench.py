@@ -228,8 +228,21 @@ def cpu_baseline(point, target_s):
         n = min(len(lens), max(n + 1, int(n * target_s / max(t, 1e-3))))
         t = timed(n)
     return {"value": n / t, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"first {n} of {len(lens)} requests of the same batch (all 64 heads, "
                       f"16384 tokens each), fp64 oracle, one call, {t:.1f} s"}
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None where it is not given."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def long_context(args, dev):
@@ -252,6 +265,9 @@ def long_context(args, dev):
         "ms_per_step_checked": rc["ms_per_step"],
         "ms_per_step_no_tracker": rn["ms_per_step"],
         "check_overhead_pct": 100.0 * (rc["ms_per_step"] - rn["ms_per_step"]) / rn["ms_per_step"],
+        # the check's cost per step in absolute terms: one check per decode
+        # step shared by N layers costs this / N per layer call
+        "check_us_per_step": 1e3 * (rc["ms_per_step"] - rn["ms_per_step"]),
         "attn_us": 1e3 * clean_ms,
         "attn_GBps": pc.bytes / (clean_ms * 1e-3) / 1e9,
         "attn_frac": pc.bytes / (clean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -556,6 +572,7 @@ def main():
     if not args.no_extras:
         r0 = p.run(args.steps, args.warmup, args.splits, check=False)
         result["check_overhead_pct"] = 100.0 * (r["ms_per_step"] - r0["ms_per_step"]) / r0["ms_per_step"]
+        result["check_us_per_step"] = 1e3 * (r["ms_per_step"] - r0["ms_per_step"])
         result["no_tracker_ms_per_step"] = r0["ms_per_step"]
         rf = p.run(args.steps, args.warmup, args.splits, fused=True)
         if not torch.all(rf["status"] == 0):
