@@ -59,6 +59,7 @@ CASES = [
     I.Workload("gqa16_d64_p32", 2, 32, 2, 64, 32, 300, 900, pool_factor=1.3),
     I.Workload("gqa5_d128_p256", 2, 10, 2, 128, 256, 700, 1300, pool_factor=1.3),
     I.Workload("gqa8_d64_p128_short", 5, 8, 1, 64, 128, 1, 70, pool_factor=2.0),
+    I.Workload("gqa16_d128_p64", 2, 32, 2, 128, 64, 200, 800, pool_factor=1.3),   # the largest group
 ]
 
 
