@@ -17,12 +17,16 @@
 // order, low nibble first), which is exactly lane L's B operand of the j-th
 // v_mfma_f32_16x16x32_bf16 over the block.
 //
-// Work split: a work-group of 4 waves owns 64 output rows (one 16-row tile
-// per wave) over all of K.  Per group of 128 features the work-group stages
-// x[0:16*MT][group] in LDS; each wave expands its 1 KiB block to bf16
-// (v_cvt_off_f32_i4 gives q/16 exactly; the factor 16 goes into the scale),
-// runs 4 MFMAs per 16-row tile of x and adds 16*s times the group's partial
-// sums into its fp32 accumulators.
+// Two rows of x or more: a work-group of 4 waves owns 64 output rows (one
+// 16-row tile per wave) over all of K.  Per group of 128 features the
+// work-group stages x[0:16*MT][group] in LDS; each wave expands its 1 KiB
+// block to bf16, runs 4 MFMAs per 16-row tile of x and adds s times the
+// group's partial sums into its fp32 accumulators.  Up to 32 rows the
+// expansion is 136 + q (a shift and one logic op per pair) with the offset
+// taken back out by MFMAs against -136; from 33 rows on v_cvt_off_f32_i4
+// gives q/16 exactly and the factor 16 goes into the scale.
+// One row of x: a work-group per 16-row tile whose waves split K, with x
+// broadcast to the MFMA's 16 rows (int4_gemv_row_kernel).
 #include "pafp8_device.hpp"
 #include "pafp8_internal.hpp"
 
