@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void splitk_combine_kernel(
     }
     acc_sm[threadIdx.x] = acc;
     __syncthreads();
-    if (threadIdx.x < nd4) {
+    if (static_cast<int>(threadIdx.x) < nd4) {
         f32x4 t = acc_sm[threadIdx.x];
         for (int gi = 1; gi < ngrp; ++gi)
             t += acc_sm[gi * nd4 + threadIdx.x];
