@@ -4,7 +4,6 @@ the e4m3 codec, the page-tag check, quantise-on-write, and the split-K combine.
 Bar: bit-exact against the oracle for codes, pools and request status; the
 combine (float) within max-abs 2e-3 / rel 1e-2 (in practice ~1e-6).
 """
-import math
 
 import numpy as np
 import pytest

@@ -18,7 +18,7 @@ from scipy.special import logsumexp
 
 import oracle
 from paged_attention_fp8_amd import inputs as I
-from helpers import e4m3_table_torch, oracle_pool
+from helpers import oracle_pool
 
 
 def _brute_status(table, lens, expected, tags, P):
