@@ -414,6 +414,40 @@ def int4_decode(args, dev):
                         "bf16 activations, fp32 output", "kernel": "int4_gemv_kernel", "points": res}
 
 
+def fp8_vs_bf16(args, dev):
+    """The ragged workload (32 requests of 1k-32k tokens, GQA 64/8, 64-token
+    pages, fragmented pool) on an e4m3 cache and on a bf16 cache built from
+    the identical bf16 source: attention time of each, and how far the e4m3
+    outputs lie from the bf16 ones (a statistic, not a gate: the pages call the
+    two indistinguishable in accuracy without a kernel-level figure)."""
+    import torch
+    from paged_attention_fp8_amd import inputs as I
+    from paged_attention_fp8_amd import ops
+    w = I.WORKLOADS["gqa8_ragged_32k"]
+    runs = {}
+    for kv_dtype, name in ((ops.KV_FP8_E4M3, "e4m3"), (ops.KV_BF16, "bf16")):
+        pt = Point(w.batch, kv_dtype, dev, workload=w)
+        r = pt.run(args.steps, args.warmup, 0, flush=True)
+        ms = statistics.mean(r["attn_ms"])
+        runs[name] = {"attn_us": 1e3 * ms, "attn_GBps": pt.bytes / (ms * 1e-3) / 1e9,
+                      "attn_frac": pt.bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "splits": r["splits"],
+                      "out": r["out"].clone(), "lse": r["lse"].clone()}
+        del pt, r
+        torch.cuda.empty_cache()
+    d = (runs["e4m3"]["out"] - runs["bf16"]["out"]).abs()
+    ref = runs["bf16"]["out"].abs()
+    dl = (runs["e4m3"]["lse"] - runs["bf16"]["lse"]).abs()
+    res = {"workload": "gqa8_ragged_32k: 32 requests x U[1024, 32768] tokens, 64 query / 8 KV heads, "
+                       "head_dim 128, 64-token pages, fragmented pool, identical bf16 source"}
+    for name in ("e4m3", "bf16"):
+        res[name] = {k: v for k, v in runs[name].items() if k not in ("out", "lse")}
+    res["out_abs_diff"] = {"max": float(d.max()), "mean": float(d.mean()),
+                           "p99": float(torch.quantile(d.flatten()[:1 << 24].float(), 0.99))}
+    res["out_rel_diff_mean"] = float((d.sum() / ref.sum()))
+    res["lse_abs_diff_max"] = float(dl.max())
+    return res
+
+
 def _pmc_values(directory, counter, kernel_substr):
     """Per-dispatch values of one counter for kernels whose name contains
     kernel_substr, from a rocprofv3 --pmc csv run directory."""
@@ -600,6 +634,7 @@ def main():
         result["prefill_handoff"] = handoff(args, dev)
         result["decode_loop"] = decode_loop(args, dev)
         result["int4_decode_gemv"] = int4_decode(args, dev)
+        result["fp8_vs_bf16"] = fp8_vs_bf16(args, dev)
     if args.sweep:
         sweep = []
         for kv_dtype, name in ((ops.KV_FP8_E4M3, "fp8"), (ops.KV_BF16, "bf16")):
