@@ -21,8 +21,10 @@ the no-op tracker are reported beside it, and so is the long-context point
 (4 requests of 262,144 tokens in 64 splits: check overhead, and the batch
 with one stale request) and the prefill-to-decode hand-off (kv_quant_fill of
 8 prompts of 8,192 tokens) and a continuous decode loop with admission
-under the same 2 GiB budget (e4m3 vs bf16), and INT4 weight streaming
-(int4_gemv over 940 MB of int4 weights at 1-64 rows).  --sweep adds the 1/8/16/32/64 concurrency points,
+under the same 2 GiB budget (e4m3 vs bf16), INT4 weight streaming
+(int4_gemv over 940 MB of int4 weights at 1-64 rows), and the ragged batch
+(32 requests of 1k-32k tokens) on e4m3 and bf16 caches from one bf16 source,
+with default splits and the balanced partition.  --sweep adds the 1/8/16/32/64 concurrency points,
 each step preceded by a 1 GiB read of other memory so that no point runs
 out of the MALL.  cpu_baseline times the CPU oracle on a bounded sample
 of the same batch.
@@ -136,9 +138,12 @@ class Point:
         ops, H, st = self.ops, self.H, self.step
         B, Hq, D = st.batch.batch, self.w.q_heads, self.w.head_dim
         dev = st.q.device
-        S = splits or ops.default_num_splits(B, self.w.kv_heads, st.batch.max_pages,
-                                             self.w.page_size)
-        S = min(S, st.batch.max_pages)
+        if splits == ops.BALANCED:
+            S = -ops.default_balanced_groups(self.w.kv_heads)
+        else:
+            S = splits or ops.default_num_splits(B, self.w.kv_heads, st.batch.max_pages,
+                                                 self.w.page_size)
+            S = min(S, st.batch.max_pages)
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
         status = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -417,9 +422,12 @@ def int4_decode(args, dev):
 def fp8_vs_bf16(args, dev):
     """The ragged workload (32 requests of 1k-32k tokens, GQA 64/8, 64-token
     pages, fragmented pool) on an e4m3 cache and on a bf16 cache built from
-    the identical bf16 source: attention time of each, and how far the e4m3
-    outputs lie from the bf16 ones (a statistic, not a gate: the pages call the
-    two indistinguishable in accuracy without a kernel-level figure)."""
+    the identical bf16 source: attention time of each, with the library's
+    default splits and with the balanced partition (negative `splits`: W
+    work-groups per KV head sharing all requests' pages equally), and how far
+    the e4m3 outputs lie from the bf16 ones (a statistic, not a gate: the
+    pages call the two indistinguishable in accuracy without a kernel-level
+    figure)."""
     import torch
     from paged_attention_fp8_amd import inputs as I
     from paged_attention_fp8_amd import ops
@@ -427,12 +435,17 @@ def fp8_vs_bf16(args, dev):
     runs = {}
     for kv_dtype, name in ((ops.KV_FP8_E4M3, "e4m3"), (ops.KV_BF16, "bf16")):
         pt = Point(w.batch, kv_dtype, dev, workload=w)
-        r = pt.run(args.steps, args.warmup, 0, flush=True)
-        ms = statistics.mean(r["attn_ms"])
-        runs[name] = {"attn_us": 1e3 * ms, "attn_GBps": pt.bytes / (ms * 1e-3) / 1e9,
-                      "attn_frac": pt.bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "splits": r["splits"],
-                      "out": r["out"].clone(), "lse": r["lse"].clone()}
-        del pt, r
+        for mode in (0, ops.BALANCED):
+            r = pt.run(args.steps, args.warmup, mode, flush=True)
+            ms = statistics.mean(r["attn_ms"])
+            res = {"attn_us": 1e3 * ms, "attn_GBps": pt.bytes / (ms * 1e-3) / 1e9,
+                   "attn_frac": pt.bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "splits": r["splits"]}
+            if mode == 0:
+                runs[name] = dict(res, out=r["out"].clone(), lse=r["lse"].clone())
+            else:
+                runs[name]["balanced"] = res
+            del r
+        del pt
         torch.cuda.empty_cache()
     d = (runs["e4m3"]["out"] - runs["bf16"]["out"]).abs()
     ref = runs["bf16"]["out"].abs()

@@ -263,17 +263,32 @@ pafp8_status int4_gemv(const uint16_t *x, int32_t M, const uint8_t *w_packed, co
  * Split-K (flash-decoding) sizing.  With num_splits = S > 1 each request's
  * pages are cut into S consecutive chunks of ceil(max_pages_per_req / S)
  * pages; each chunk produces a partial (o, lse) in the workspace and
- * splitk_combine merges them.  pafp8_decode_workspace_bytes gives the
- * workspace size (0 when S == 1); pafp8_default_num_splits picks S so that
+ * splitk_combine merges them.  pafp8_default_num_splits picks S so that
  * batch * num_kv_heads * S is about one work-group per CU, with splits of at
- * least 1024 tokens (num_cus <= 0: query the current device).  Pure host
- * functions.
+ * least 1024 tokens (num_cus <= 0: query the current device).
+ *
+ * Balanced partition, num_splits = -W (1 <= W <= 65536): for each KV head the
+ * pages of all live requests, in request order, form one sequence of T pages
+ * (aborted, empty and invalid requests add none), and W work-groups take
+ * consecutive ranges of ceil(T / W) pages.  Every work-group then streams
+ * the same bytes whatever the spread of context lengths; a request cut by a
+ * range boundary is merged afterwards like split-K partials (the outputs are
+ * the same attention, up to fp32 rounding order).  The ranges are found on the
+ * device from context_lens, so the host needs no lengths.
+ * pafp8_default_balanced_groups gives W = ceil(num_cus / num_kv_heads), one
+ * work-group per CU (num_cus <= 0: query the current device).
+ *
+ * pafp8_decode_workspace_bytes gives the workspace size for num_splits
+ * (0 when S == 1; for -W: (num_q_heads * (batch + W - 1) * (head_dim + 1))
+ * floats, each part rounded up to 16 bytes, plus (batch + 1) int64).
+ * Pure host functions.
  * ------------------------------------------------------------------------- */
 size_t pafp8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                     int32_t num_splits);
 int32_t pafp8_default_num_splits(int32_t batch, int32_t num_kv_heads,
                                  int32_t max_pages_per_req, int32_t page_size,
                                  int32_t num_cus);
+int32_t pafp8_default_balanced_groups(int32_t num_kv_heads, int32_t num_cus);
 
 /* ---------------------------------------------------------------------------
  * paged_decode_attn_fp8 / paged_decode_attn_bf16 -- decode attention over the
@@ -288,7 +303,9 @@ int32_t pafp8_default_num_splits(int32_t batch, int32_t num_kv_heads,
  * Arithmetic: K/V are decoded exactly; products and sums accumulate in fp32.
  *   q        device bf16 bits [B][num_q_heads][head_dim]
  *   sm_scale positive, finite (typically 1/sqrt(head_dim))
- *   num_splits S >= 1 (0: pafp8_default_num_splits); S > 1 needs workspace
+ *   num_splits S >= 1 (0: pafp8_default_num_splits), or -W for the balanced
+ *            partition; S > 1 and S < 0 need workspace (16-byte aligned, at
+ *            least pafp8_decode_workspace_bytes; its contents are ignored)
  *   out      device fp32 [B][num_q_heads][head_dim]
  *   lse      device fp32 [B][num_q_heads], or NULL
  * G must be 1..16; cache->kv_dtype must match the entry point.

@@ -51,6 +51,11 @@ int log2_exact(int v)
     return -1;
 }
 
+// largest W of a balanced launch (num_splits = -W)
+constexpr int32_t kMaxBalancedGroups = 65536;
+
+size_t align16_up(size_t n) { return (n + 15) & ~size_t{15}; }
+
 bool page_size_ok(int P) { return P == 16 || P == 32 || P == 64 || P == 128 || P == 256; }
 
 pafp8_status check_batch(const pafp8_batch *b, bool need_lens)
@@ -117,8 +122,12 @@ pafp8_status check_attn(const pafp8_cache *cache, const pafp8_batch *batch, cons
         return fail(PAFP8_EUNSUPPORTED, "query group size %d > 16", G);
     if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f)
         return fail(PAFP8_EINVAL, "sm_scale must be positive and finite");
-    if (S < 0)
-        return fail(PAFP8_EINVAL, "num_splits = %d < 0", S);
+    if (S < -kMaxBalancedGroups)
+        return fail(PAFP8_EINVAL, "num_splits = %d: a balanced launch takes at most %d work-groups per KV head",
+                    S, kMaxBalancedGroups);
+    if (S < 0 && (static_cast<int64_t>(cache->num_kv_heads) * -S > 0x7FFFFFFF ||
+                  static_cast<int64_t>(batch->batch) - S - 1 > 0x7FFFFFFF))
+        return fail(PAFP8_EUNSUPPORTED, "a balanced launch of %d work-groups per KV head is too large", -S);
     if (batch->batch > 0 && (q == nullptr || out == nullptr))
         return fail(PAFP8_EINVAL, "q or out is NULL");
     if (batch->batch > 0 && (!aligned16(q) || !aligned16(out)))
@@ -164,6 +173,7 @@ pafp8_status attn_impl(const pafp8_cache *cache, const pafp8_batch *batch, const
                                      cache->page_size, 0);
     if (S > batch->max_pages_per_req)
         S = batch->max_pages_per_req;  // more splits than pages would all be empty
+    const bool balanced = S < 0;
     const size_t need = pafp8_decode_workspace_bytes(batch->batch, Hq, cache->head_dim, S);
     if (need > 0) {
         if (ws == nullptr || ws_bytes < need)
@@ -190,10 +200,18 @@ pafp8_status attn_impl(const pafp8_cache *cache, const pafp8_batch *batch, const
     p.max_pages = batch->max_pages_per_req;
     p.num_q_heads = Hq;
     p.group = Hq / cache->num_kv_heads;
-    p.num_splits = S;
-    p.pages_per_split = (batch->max_pages_per_req + S - 1) / S;
+    p.num_splits = balanced ? 1 : S;
+    p.pages_per_split = balanced ? batch->max_pages_per_req : (batch->max_pages_per_req + S - 1) / S;
+    p.bal_groups = balanced ? -S : 0;
     p.sm_scale = sm_scale;
-    if (S > 1) {
+    if (balanced) {
+        const size_t R = static_cast<size_t>(batch->batch) - S - 1;  // B + W - 1
+        const size_t o_bytes = align16_up(static_cast<size_t>(Hq) * R * cache->head_dim * sizeof(float));
+        const size_t l_bytes = align16_up(static_cast<size_t>(Hq) * R * sizeof(float));
+        p.part_o = static_cast<float *>(ws);
+        p.part_lse = reinterpret_cast<float *>(static_cast<char *>(ws) + o_bytes);
+        p.bal_prefix = reinterpret_cast<int64_t *>(static_cast<char *>(ws) + o_bytes + l_bytes);
+    } else if (S > 1) {
         p.part_o = static_cast<float *>(ws);
         p.part_lse = p.part_o + static_cast<size_t>(batch->batch) * Hq * S * cache->head_dim;
     }
@@ -201,7 +219,13 @@ pafp8_status attn_impl(const pafp8_cache *cache, const pafp8_batch *batch, const
                                              stream);
     if (e != hipSuccess)
         return hip_status(e, "paged_decode_attn launch");
-    if (S > 1) {
+    if (balanced) {
+        e = pafp8::launch_bal_combine(p.part_o, p.part_lse, p.bal_prefix, batch->batch, Hq, -S,
+                                      cache->head_dim, batch->req_status, batch->context_lens,
+                                      batch->max_pages_per_req, p.log2_page, out, lse, stream);
+        if (e != hipSuccess)
+            return hip_status(e, "balanced combine launch");
+    } else if (S > 1) {
         e = pafp8::launch_splitk_combine(p.part_o, p.part_lse, batch->batch, Hq, S,
                                          cache->head_dim, batch->req_status, out, lse, stream);
         if (e != hipSuccess)
@@ -345,10 +369,28 @@ pafp8_status kv_quant_fill(const pafp8_cache *cache, const pafp8_batch *batch,
 size_t pafp8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                     int32_t num_splits)
 {
-    if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 1)
+    if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits == 0 || num_splits == 1 ||
+        num_splits < -kMaxBalancedGroups)
         return 0;
+    if (num_splits < 0) {
+        // partial rows [Hq][B + W - 1][D], their LSEs, then B + 1 int64
+        const size_t rows = static_cast<size_t>(num_q_heads) * (static_cast<size_t>(batch) - num_splits - 1);
+        return align16_up(rows * static_cast<size_t>(head_dim) * sizeof(float)) +
+               align16_up(rows * sizeof(float)) + (static_cast<size_t>(batch) + 1) * sizeof(int64_t);
+    }
     const size_t rows = static_cast<size_t>(batch) * num_q_heads * num_splits;
     return rows * static_cast<size_t>(head_dim) * sizeof(float) + rows * sizeof(float);
+}
+
+int32_t pafp8_default_balanced_groups(int32_t num_kv_heads, int32_t num_cus)
+{
+    if (num_kv_heads <= 0)
+        return 1;
+    if (num_cus <= 0)
+        num_cus = device_cu_count();
+    // one work-group per CU
+    const int64_t W = (static_cast<int64_t>(num_cus) + num_kv_heads - 1) / num_kv_heads;
+    return static_cast<int32_t>(W < 1 ? 1 : (W > kMaxBalancedGroups ? kMaxBalancedGroups : W));
 }
 
 int32_t pafp8_default_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_pages_per_req,

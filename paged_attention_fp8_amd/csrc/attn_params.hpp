@@ -17,10 +17,11 @@ struct AttnParams {
     const int32_t *context_lens;
     const int32_t *req_status;  // nullable
     const uint16_t *q;
-    float *out;        // final [B][Hq][D] (when S == 1)
-    float *lse;        // final [B][Hq] or nullptr (when S == 1)
-    float *part_o;     // [B][Hq][S][D] (when S > 1)
-    float *part_lse;   // [B][Hq][S]
+    float *out;        // final [B][Hq][D] (when S == 1, and whole requests of a balanced launch)
+    float *lse;        // final [B][Hq] or nullptr
+    float *part_o;     // [B][Hq][S][D] (when S > 1); balanced: [Hq][B + W - 1][D]
+    float *part_lse;   // [B][Hq][S]; balanced: [Hq][B + W - 1]
+    int64_t *bal_prefix;  // balanced: [B + 1] first page of each request in the sequence, then C
     int32_t num_pages;
     int32_t log2_page;  // page_size = 1 << log2_page
     int32_t num_kv_heads;
@@ -28,8 +29,9 @@ struct AttnParams {
     int32_t max_pages;
     int32_t num_q_heads;
     int32_t group;            // num_q_heads / num_kv_heads
-    int32_t num_splits;       // S
+    int32_t num_splits;       // S (1 in a balanced launch)
     int32_t pages_per_split;  // ceil(max_pages / S)
+    int32_t bal_groups;       // W work-groups per KV head in a balanced launch, else 0
     float sm_scale;
 };
 

@@ -381,12 +381,29 @@ struct MergeSmem {
     float l[kWaves][16];
 };
 
+// Where a group's merged rows go: query head h of the group to o + h*stride*D
+// and lse[h*stride] (lse may be nullptr).
+struct MergeDst {
+    float *o;
+    float *lse;
+    int64_t stride;
+};
+
+// final output (one split) or the split's partial rows
 template <int D>
-__device__ __forceinline__ void merge_and_write(const AttnParams &p, MergeSmem<D> &sm, int b,
-                                                int g, int s, int nheads, int state, int bad,
-                                                float v_scale)
+__device__ __forceinline__ MergeDst split_dst(const AttnParams &p, int b, int g, int s)
 {
-    const int Hq = p.num_q_heads;
+    const int64_t bh0 = static_cast<int64_t>(b) * p.num_q_heads + static_cast<int64_t>(g) * p.group;
+    if (p.num_splits == 1)
+        return MergeDst{p.out + bh0 * D, p.lse != nullptr ? p.lse + bh0 : nullptr, 1};
+    const int64_t row0 = bh0 * p.num_splits + s;
+    return MergeDst{p.part_o + row0 * D, p.part_lse + row0, p.num_splits};
+}
+
+template <int D>
+__device__ __forceinline__ void merge_and_write(MergeSmem<D> &sm, int nheads, int state, int bad,
+                                                float v_scale, MergeDst dst)
+{
     for (int idx = threadIdx.x; idx < nheads * (D / 4); idx += kThreads) {
         const int h = idx / (D / 4);
         const int d4 = (idx % (D / 4)) * 4;
@@ -416,36 +433,168 @@ __device__ __forceinline__ void merge_and_write(const AttnParams &p, MergeSmem<D
             o = f32x4{nan, nan, nan, nan};
             lse = nan;
         }
-        const int64_t bh = static_cast<int64_t>(b) * Hq + static_cast<int64_t>(g) * nheads + h;
-        if (p.num_splits == 1) {
-            *reinterpret_cast<f32x4 *>(p.out + bh * D + d4) = o;
-            if (d4 == 0 && p.lse != nullptr)
-                p.lse[bh] = lse;
-        } else {
-            const int64_t row = bh * p.num_splits + s;
-            *reinterpret_cast<f32x4 *>(p.part_o + row * D + d4) = o;
-            if (d4 == 0)
-                p.part_lse[row] = lse;
-        }
+        const int64_t row = h * dst.stride;
+        *reinterpret_cast<f32x4 *>(dst.o + row * D + d4) = o;
+        if (d4 == 0 && dst.lse != nullptr)
+            dst.lse[row] = lse;
     }
 }
 
+// ---------------------------------------------------------------------------
+// Balanced partition (num_splits < 0).  For one KV head, the pages of all
+// live requests taken in request order form one sequence of T pages; W
+// work-groups take consecutive ranges of C = ceil(T / W) pages each, so every
+// work-group streams the same bytes however ragged the context lengths are.
+// A range may cut a request (and hold several): a request piece lying wholly
+// inside one range is the request itself and goes straight to the output;
+// any other piece leaves a partial at row b + w of its query head (rows
+// [Hq][R], R = B + W - 1).  Pieces (b, w) and (b', w') with b + w == b' + w'
+// cannot both exist -- b' > b would make request b' start after b ends while
+// range w' ends before w starts -- so a request's partials are the
+// consecutive rows b + w_first .. b + w_last, which the balanced combine
+// merges.  Work-group 0 of KV head 0 also stores every request's first page
+// in the sequence and C, from which the combine finds those rows.
+// ---------------------------------------------------------------------------
+struct ReqPages {
+    int64_t n;  // pages in the sequence (0: aborted, empty or invalid)
+    int64_t L;
+};
+
+__device__ __forceinline__ ReqPages request_pages(const AttnParams &p, int b)
+{
+    ReqPages r{0, 0};
+    if (p.req_status != nullptr && p.req_status[b] != 0)
+        return r;
+    const int64_t L = p.context_lens[b];
+    if (L <= 0 || L > (static_cast<int64_t>(p.max_pages) << p.log2_page))
+        return r;
+    r.L = L;
+    r.n = (L + (int64_t{1} << p.log2_page) - 1) >> p.log2_page;
+    return r;
+}
+
+struct BalSmem {
+    int64_t wave_total[kWaves];
+    int64_t ps0;
+    int b0;
+};
+
+struct BalRange {
+    int64_t lo, hi;  // the work-group's pages of the sequence
+    int64_t C;       // pages per work-group
+    int64_t ps0;     // sequence offset of request b0's first page
+    int b0;          // the request holding page lo (batch if the range is empty)
+};
+
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t u = __shfl_up(v, d, 64);
+        v += lane >= d ? u : 0;
+    }
+    return v;
+}
+
+// Every work-group scans the request lengths (threads take consecutive runs of
+// requests), then finds its range and the request that holds its first page.
+__device__ __forceinline__ BalRange bal_range(const AttnParams &p, BalSmem &bs, int w,
+                                              bool store_prefix)
+{
+    const int B = p.batch;
+    const int per = (B + kThreads - 1) / kThreads;
+    const int first = static_cast<int>(threadIdx.x) * per;
+    const int last = first + per < B ? first + per : B;
+    int64_t sum = 0;
+    for (int b = first; b < last; ++b)
+        sum += request_pages(p, b).n;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t incl = wave_incl_scan(sum);
+    if (lane == 63)
+        bs.wave_total[wave] = incl;
+    __syncthreads();
+    int64_t before = 0, T = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        before += i < wave ? bs.wave_total[i] : 0;
+        T += bs.wave_total[i];
+    }
+    const int64_t ex = before + incl - sum;  // sequence offset of request `first`
+    BalRange r;
+    r.C = T > 0 ? (T + p.bal_groups - 1) / p.bal_groups : 1;
+    r.lo = static_cast<int64_t>(w) * r.C;
+    r.hi = r.lo + r.C < T ? r.lo + r.C : T;
+    if (store_prefix) {
+        int64_t at = ex;
+        for (int b = first; b < last; ++b) {
+            p.bal_prefix[b] = at;
+            at += request_pages(p, b).n;
+        }
+        if (threadIdx.x == 0)
+            p.bal_prefix[B] = r.C;
+    }
+    r.b0 = B;
+    r.ps0 = T;
+    if (r.lo >= r.hi)
+        return r;  // uniform: the whole work-group has nothing to do
+    // exactly one thread's run of pages [ex, ex + sum) holds page lo
+    if (ex <= r.lo && r.lo < ex + sum) {
+        int64_t at = ex;
+        for (int b = first; b < last; ++b) {
+            const int64_t n = request_pages(p, b).n;
+            if (r.lo < at + n) {
+                bs.b0 = b;
+                bs.ps0 = at;
+                break;
+            }
+            at += n;
+        }
+    }
+    __syncthreads();
+    r.b0 = bs.b0;
+    r.ps0 = bs.ps0;
+    return r;
+}
+
+// the tokens of the piece of request rq (first page ps in the sequence) that
+// falls in range r; page offsets are relative to the request
+__device__ __forceinline__ SplitRange piece_range(const AttnParams &p, const BalRange &r,
+                                                  int64_t ps, const ReqPages &rq)
+{
+    const int64_t p0 = (r.lo > ps ? r.lo : ps) - ps;
+    const int64_t p1 = (r.hi < ps + rq.n ? r.hi : ps + rq.n) - ps;
+    SplitRange s;
+    s.t0 = p0 << p.log2_page;
+    s.t1 = p1 << p.log2_page;
+    if (s.t1 > rq.L)
+        s.t1 = rq.L;
+    s.p_last = p1 - 1;
+    s.state = 0;
+    return s;
+}
+
+template <int D>
+__device__ __forceinline__ MergeDst piece_dst(const AttnParams &p, const BalRange &r, int64_t ps,
+                                              const ReqPages &rq, int b, int g, int w)
+{
+    if (ps >= r.lo && ps + rq.n <= r.hi)  // the whole request
+        return split_dst<D>(p, b, g, 0);
+    const int64_t R = static_cast<int64_t>(p.batch) + p.bal_groups - 1;
+    const int64_t row0 = static_cast<int64_t>(g) * p.group * R + b + w;
+    return MergeDst{p.part_o + row0 * D, p.part_lse + row0, R};
+}
+
+// Request b, KV head g over tokens [rng.t0, rng.t1): each wave's softmax
+// state ends up in sm.  Returns non-zero if a page id lay outside the pool.
 template <bool BF16, int D, bool BIG>
-__global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel(AttnParams p)
+__device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm, int b, int g,
+                                          const SplitRange &rng)
 {
     using G_ = Geo<BF16, D>;
-    __shared__ MergeSmem<D> sm;
-
-    int idx = blockIdx.x;
-    const int s = idx % p.num_splits;
-    idx /= p.num_splits;
-    const int g = idx % p.num_kv_heads;
-    const int b = idx / p.num_kv_heads;
     const int G = p.group;
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
-
-    const SplitRange rng = split_range(p, b, s);
     MfmaState<BF16, D> st;
 #pragma unroll
     for (int dt = 0; dt < G_::NDT; ++dt)
@@ -534,8 +683,51 @@ __global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel
         for (int dt = 0; dt < G_::NDT; ++dt)
             *reinterpret_cast<f32x4 *>(&sm.o[wave][r][dt * 16 + lg * 4]) = st.o[dt];
     }
+    return bad;
+}
+
+template <bool BF16, int D, bool BIG>
+__global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel(AttnParams p)
+{
+    __shared__ MergeSmem<D> sm;
+
+    int idx = blockIdx.x;
+    const int s = idx % p.num_splits;
+    idx /= p.num_splits;
+    const int g = idx % p.num_kv_heads;
+    const int b = idx / p.num_kv_heads;
+
+    const SplitRange rng = split_range(p, b, s);
+    int bad = mfma_range<BF16, D, BIG>(p, sm, b, g, rng);
     bad = __syncthreads_or(bad);
-    merge_and_write<D>(p, sm, b, g, s, G, rng.state, bad, BF16 ? 1.0f : p.v_scale[g]);
+    merge_and_write<D>(sm, p.group, rng.state, bad, BF16 ? 1.0f : p.v_scale[g],
+                       split_dst<D>(p, b, g, s));
+}
+
+// Balanced partition: the work-group takes pages [lo, hi) of its KV head's
+// concatenated live pages and attends to each request piece in turn.
+template <bool BF16, int D, bool BIG>
+__global__ __launch_bounds__(kThreads, 2) void decode_attn_bal_mfma_kernel(AttnParams p)
+{
+    __shared__ MergeSmem<D> sm;
+    __shared__ BalSmem bs;
+
+    const int g = blockIdx.x % p.num_kv_heads;
+    const int w = blockIdx.x / p.num_kv_heads;
+    const BalRange r = bal_range(p, bs, w, g == 0 && w == 0);
+    int64_t ps = r.ps0;
+    for (int b = r.b0; b < p.batch && ps < r.hi; ++b) {
+        const ReqPages rq = request_pages(p, b);
+        if (rq.n > 0) {
+            const SplitRange rng = piece_range(p, r, ps, rq);
+            int bad = mfma_range<BF16, D, BIG>(p, sm, b, g, rng);
+            bad = __syncthreads_or(bad);
+            merge_and_write<D>(sm, p.group, 0, bad, BF16 ? 1.0f : p.v_scale[g],
+                               piece_dst<D>(p, r, ps, rq, b, g, w));
+            __syncthreads();  // sm is written again by the next piece
+        }
+        ps += rq.n;
+    }
 }
 
 // ===========================================================================
@@ -582,20 +774,13 @@ struct VecSmem {
 };
 
 template <bool BF16, int D>
-__global__ __launch_bounds__(kThreads) void decode_attn_vec_kernel(AttnParams p)
+__device__ __forceinline__ int vec_range(const AttnParams &p, VecSmem<D> &sm, int b, int g,
+                                         const SplitRange &rng)
 {
     using V_ = VecGeo<BF16, D>;
-    __shared__ VecSmem<D> sm;
-
-    int idx = blockIdx.x;
-    const int s = idx % p.num_splits;
-    idx /= p.num_splits;
-    const int g = idx % p.num_kv_heads;
-    const int b = idx / p.num_kv_heads;
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
 
-    const SplitRange rng = split_range(p, b, s);
     for (int d = threadIdx.x; d < D; d += kThreads)
         sm.q[d] = __uint_as_float(static_cast<uint32_t>(p.q[(static_cast<int64_t>(b) * p.num_q_heads + g) * D + d]) << 16);
     __syncthreads();
@@ -704,25 +889,76 @@ __global__ __launch_bounds__(kThreads) void decode_attn_vec_kernel(AttnParams p)
 #pragma unroll
     for (int r = 0; r < V_::ROWS; ++r)
         sm.merge.o[wave][0][lane + 64 * r] = acc[r];
+    return bad;
+}
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads) void decode_attn_vec_kernel(AttnParams p)
+{
+    __shared__ VecSmem<D> sm;
+
+    int idx = blockIdx.x;
+    const int s = idx % p.num_splits;
+    idx /= p.num_splits;
+    const int g = idx % p.num_kv_heads;
+    const int b = idx / p.num_kv_heads;
+
+    const SplitRange rng = split_range(p, b, s);
+    int bad = vec_range<BF16, D>(p, sm, b, g, rng);
     bad = __syncthreads_or(bad);
-    merge_and_write<D>(p, sm.merge, b, g, s, 1, rng.state, bad, BF16 ? 1.0f : p.v_scale[g]);
+    merge_and_write<D>(sm.merge, 1, rng.state, bad, BF16 ? 1.0f : p.v_scale[g],
+                       split_dst<D>(p, b, g, s));
+}
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads) void decode_attn_bal_vec_kernel(AttnParams p)
+{
+    __shared__ VecSmem<D> sm;
+    __shared__ BalSmem bs;
+
+    const int g = blockIdx.x % p.num_kv_heads;
+    const int w = blockIdx.x / p.num_kv_heads;
+    const BalRange r = bal_range(p, bs, w, g == 0 && w == 0);
+    int64_t ps = r.ps0;
+    for (int b = r.b0; b < p.batch && ps < r.hi; ++b) {
+        const ReqPages rq = request_pages(p, b);
+        if (rq.n > 0) {
+            const SplitRange rng = piece_range(p, r, ps, rq);
+            int bad = vec_range<BF16, D>(p, sm, b, g, rng);
+            bad = __syncthreads_or(bad);
+            merge_and_write<D>(sm.merge, 1, 0, bad, BF16 ? 1.0f : p.v_scale[g],
+                               piece_dst<D>(p, r, ps, rq, b, g, w));
+            __syncthreads();  // sm is written again by the next piece
+        }
+        ps += rq.n;
+    }
 }
 
 template <bool BF16, int D>
 hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
 {
-    const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_splits;
+    const bool bal = p.bal_groups > 0;
+    const int64_t blocks = bal ? static_cast<int64_t>(p.num_kv_heads) * p.bal_groups
+                               : static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_splits;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
-    if (p.group == 1)
-        hipLaunchKernelGGL((decode_attn_vec_kernel<BF16, D>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(kThreads), 0, stream, p);
-    else if (p.log2_page >= Geo<BF16, D>::LOG2_TT)
-        hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, true>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, false>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(kThreads), 0, stream, p);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    if (p.group == 1) {
+        if (bal)
+            hipLaunchKernelGGL((decode_attn_bal_vec_kernel<BF16, D>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_attn_vec_kernel<BF16, D>), grid, block, 0, stream, p);
+    } else if (p.log2_page >= Geo<BF16, D>::LOG2_TT) {
+        if (bal)
+            hipLaunchKernelGGL((decode_attn_bal_mfma_kernel<BF16, D, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, true>), grid, block, 0, stream, p);
+    } else {
+        if (bal)
+            hipLaunchKernelGGL((decode_attn_bal_mfma_kernel<BF16, D, false>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

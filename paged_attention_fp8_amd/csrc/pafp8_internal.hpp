@@ -16,6 +16,14 @@ hipError_t launch_splitk_combine(const float *part_o, const float *part_lse, int
                                  const int32_t *req_status, float *out, float *lse,
                                  hipStream_t stream);
 
+// merge of a balanced attention launch's partials (W = groups work-groups
+// per KV head; prefix = the [B + 1] array the attention kernel stored)
+hipError_t launch_bal_combine(const float *part_o, const float *part_lse, const int64_t *prefix,
+                              int batch, int num_q_heads, int groups, int head_dim,
+                              const int32_t *req_status, const int32_t *context_lens,
+                              int max_pages, int log2_page, float *out, float *lse,
+                              hipStream_t stream);
+
 hipError_t launch_tag_realloc(int n, const int32_t *page_ids, const int32_t *owner_req,
                               const int32_t *owner_slot, uint32_t *page_tags, int num_pages,
                               int32_t *page_table, uint32_t *expected_tags, int batch,

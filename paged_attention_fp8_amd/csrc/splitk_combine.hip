@@ -93,26 +93,35 @@ __global__ __launch_bounds__(kThreads) void splitk_combine_kernel(
         lse_out[bh] = LSE;
 }
 
-// Wave-per-head combine for the attention's own head dims: one wave owns a
-// (request, query head); lane (g, c) handles float4 column c of the splits
-// k = g (mod 64 / (D/4)).  The first PF partial rows of every lane are
-// loaded together with the split LSEs, so the whole reduction costs one
-// memory round trip when S * D <= 64 * 4 * PF.
+// one output row of D floats (and its lse unless lse is nullptr) set by a wave
 template <int D>
-__global__ __launch_bounds__(kThreads) void splitk_combine_wave_kernel(
-    const float *__restrict__ part_o, const float *__restrict__ part_lse, int BH, int Hq, int S,
-    const int32_t *__restrict__ req_status, float *__restrict__ out, float *__restrict__ lse_out)
+__device__ __forceinline__ void fill_row(float *o, float *lse, float v, float lse_v)
+{
+    constexpr int NC = D / 4;
+    const int lane = threadIdx.x & 63;
+    if (lane < NC)
+        *reinterpret_cast<f32x4 *>(o + lane * 4) = f32x4{v, v, v, v};
+    if (lane == 0 && lse != nullptr)
+        *lse = lse_v;
+}
+
+// Wave-per-head combine for the attention's own head dims: one wave merges
+// the S partial rows po[S][D] (LSEs pl[S]) of one (request, query head) into
+// o (and *lse unless lse is nullptr); lane (g, c) handles float4 column c of
+// the rows k = g (mod 64 / (D/4)).  The first PF partial rows of every lane
+// are loaded together with the LSEs, so the whole reduction costs one memory
+// round trip when S * D <= 64 * 4 * PF.
+template <int D>
+__device__ __forceinline__ void combine_rows(const float *__restrict__ pl, const float *__restrict__ po,
+                                             int S, bool aborted, float *__restrict__ o,
+                                             float *__restrict__ lse)
 {
     constexpr int NC = D / 4;    // float4 columns of a row
-    constexpr int NG = 64 / NC;  // split groups in a wave
+    constexpr int NG = 64 / NC;  // row groups in a wave
     constexpr int PF = 8;        // partial rows per lane loaded up front
     const int lane = threadIdx.x & 63;
-    const int bh = blockIdx.x * kWaves + uniform(threadIdx.x >> 6);
-    if (bh >= BH)
-        return;
     const int col = lane % NC, grp = lane / NC;
-    const float *pl = part_lse + static_cast<int64_t>(bh) * S;
-    const float *po = part_o + static_cast<int64_t>(bh) * S * D + col * 4;
+    po += col * 4;
     f32x4 pre[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
@@ -121,7 +130,6 @@ __global__ __launch_bounds__(kThreads) void splitk_combine_wave_kernel(
                        : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float l0 = lane < S ? pl[lane] : kNegInf;
-    const bool aborted = req_status != nullptr && req_status[bh / Hq] != 0;
     float M = l0;
     bool nan = l0 != l0;
     for (int k = lane + 64; k < S; k += 64) {
@@ -131,13 +139,9 @@ __global__ __launch_bounds__(kThreads) void splitk_combine_wave_kernel(
     }
     M = wave_max(M);
     const bool has_nan = __builtin_amdgcn_ballot_w64(nan) != 0;
-    float *o = out + static_cast<int64_t>(bh) * D;
     if (aborted || has_nan || M == kNegInf) {
         const float fill = (has_nan && !aborted) ? __builtin_nanf("") : 0.f;
-        if (grp == 0)
-            *reinterpret_cast<f32x4 *>(o + col * 4) = f32x4{fill, fill, fill, fill};
-        if (lane == 0 && lse_out != nullptr)
-            lse_out[bh] = (has_nan && !aborted) ? fill : kNegInf;
+        fill_row<D>(o, lse, fill, (has_nan && !aborted) ? fill : kNegInf);
         return;
     }
     float sum = lane < S ? __expf(l0 - M) : 0.f;
@@ -179,8 +183,60 @@ __global__ __launch_bounds__(kThreads) void splitk_combine_wave_kernel(
     }
     if (grp == 0)
         *reinterpret_cast<f32x4 *>(o + col * 4) = acc;
-    if (lane == 0 && lse_out != nullptr)
-        lse_out[bh] = LSE;
+    if (lane == 0 && lse != nullptr)
+        *lse = LSE;
+}
+
+// split-K partials: rows [B][Hq][S]
+template <int D>
+__global__ __launch_bounds__(kThreads) void splitk_combine_wave_kernel(
+    const float *__restrict__ part_o, const float *__restrict__ part_lse, int BH, int Hq, int S,
+    const int32_t *__restrict__ req_status, float *__restrict__ out, float *__restrict__ lse_out)
+{
+    const int bh = blockIdx.x * kWaves + uniform(threadIdx.x >> 6);
+    if (bh >= BH)
+        return;
+    const bool aborted = req_status != nullptr && req_status[bh / Hq] != 0;
+    combine_rows<D>(part_lse + static_cast<int64_t>(bh) * S, part_o + static_cast<int64_t>(bh) * S * D,
+                    S, aborted, out + static_cast<int64_t>(bh) * D,
+                    lse_out != nullptr ? lse_out + bh : nullptr);
+}
+
+// Balanced-partition partials (decode_attn.hip): request b's pieces are rows
+// b + w_first .. b + w_last of its query head's [R] rows, w_first and w_last
+// following from the request's first page ps in the sequence and the pages per
+// work-group C (prefix[b], prefix[B]).  A request inside one range was
+// written whole by the attention kernel; requests with no pages (aborted,
+// empty, invalid length) get their fixed outputs here.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bal_combine_wave_kernel(
+    const float *__restrict__ part_o, const float *__restrict__ part_lse,
+    const int64_t *__restrict__ prefix, int B, int Hq, int R, const int32_t *__restrict__ req_status,
+    const int32_t *__restrict__ context_lens, int max_pages, int log2_page, float *__restrict__ out,
+    float *__restrict__ lse_out)
+{
+    const int bh = blockIdx.x * kWaves + uniform(threadIdx.x >> 6);
+    if (bh >= B * Hq)
+        return;
+    const int b = bh / Hq, h = bh % Hq;
+    float *o = out + static_cast<int64_t>(bh) * D;
+    float *lse = lse_out != nullptr ? lse_out + bh : nullptr;
+    // all four loads go out together (prefix holds an entry for every request)
+    const bool aborted = req_status != nullptr && req_status[b] != 0;
+    const int64_t L = context_lens[b];
+    const int64_t ps = prefix[b], C = prefix[B];
+    const bool invalid = L < 0 || L > (static_cast<int64_t>(max_pages) << log2_page);
+    if (aborted || invalid || L == 0) {
+        const float v = aborted || !invalid ? 0.f : __builtin_nanf("");
+        fill_row<D>(o, lse, v, aborted || !invalid ? kNegInf : v);
+        return;
+    }
+    const int64_t n = (L + (int64_t{1} << log2_page) - 1) >> log2_page;
+    const int64_t w0 = ps / C, w1 = (ps + n - 1) / C;
+    if (w0 == w1)
+        return;
+    const int64_t row0 = static_cast<int64_t>(h) * R + b + w0;
+    combine_rows<D>(part_lse + row0, part_o + row0 * D, static_cast<int>(w1 - w0 + 1), false, o, lse);
 }
 
 }  // namespace
@@ -208,6 +264,28 @@ hipError_t launch_splitk_combine(const float *part_o, const float *part_lse, int
     hipLaunchKernelGGL(splitk_combine_kernel, dim3(static_cast<unsigned>(bh)), dim3(kThreads), 0,
                        stream, part_o, part_lse, num_q_heads, num_splits, head_dim, req_status, out,
                        lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_bal_combine(const float *part_o, const float *part_lse, const int64_t *prefix,
+                              int batch, int num_q_heads, int groups, int head_dim,
+                              const int32_t *req_status, const int32_t *context_lens,
+                              int max_pages, int log2_page, float *out, float *lse,
+                              hipStream_t stream)
+{
+    const int64_t bh = static_cast<int64_t>(batch) * num_q_heads;
+    const int64_t R = static_cast<int64_t>(batch) + groups - 1;
+    if (bh > 0x7FFFFFFF || R > 0x7FFFFFFF || (head_dim != 64 && head_dim != 128))
+        return hipErrorInvalidConfiguration;
+    const unsigned blocks = static_cast<unsigned>((bh + kWaves - 1) / kWaves);
+    if (head_dim == 64)
+        hipLaunchKernelGGL(bal_combine_wave_kernel<64>, dim3(blocks), dim3(kThreads), 0, stream, part_o,
+                           part_lse, prefix, batch, num_q_heads, static_cast<int>(R), req_status,
+                           context_lens, max_pages, log2_page, out, lse);
+    else
+        hipLaunchKernelGGL(bal_combine_wave_kernel<128>, dim3(blocks), dim3(kThreads), 0, stream, part_o,
+                           part_lse, prefix, batch, num_q_heads, static_cast<int>(R), req_status,
+                           context_lens, max_pages, log2_page, out, lse);
     return hipGetLastError();
 }
 

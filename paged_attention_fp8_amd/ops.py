@@ -58,6 +58,7 @@ _SIGNATURES = {
     "int4_gemv": (_I32, [_V, _I32, _V, _V, _I32, _I32, _V, _V]),
     "pafp8_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "pafp8_default_num_splits": (_I32, [_I32, _I32, _I32, _I32, _I32]),
+    "pafp8_default_balanced_groups": (_I32, [_I32, _I32]),
     "paged_decode_attn_fp8": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V]),
     "paged_decode_attn_bf16": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V]),
     "splitk_combine": (_I32, [_V, _V, _I32, _I32, _I32, _I32, _V, _V, _V, _V]),
@@ -335,12 +336,22 @@ def default_num_splits(batch: int, num_kv_heads: int, max_pages: int, page_size:
     return int(lib().pafp8_default_num_splits(batch, num_kv_heads, max_pages, page_size, num_cus))
 
 
+def default_balanced_groups(num_kv_heads: int, num_cus: int = 0) -> int:
+    return int(lib().pafp8_default_balanced_groups(num_kv_heads, num_cus))
+
+
+BALANCED = "balanced"
+
+
 def paged_decode_attn(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor, sm_scale: float,
-                      num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+                      num_splits=0, workspace: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       return_lse: bool = True):
     """Decode attention over the paged cache; dispatches to
     paged_decode_attn_fp8 or paged_decode_attn_bf16 by the pool's dtype.
+    num_splits: S >= 1 uniform splits, 0 the library's default, -W (or
+    BALANCED for pafp8_default_balanced_groups) the balanced partition over W
+    work-groups per KV head.
     Returns (out fp32 [B][Hq][D], lse fp32 [B][Hq] or None)."""
     dev = cache.device
     cs, bs = cache._struct(), batch._struct(dev)
@@ -348,9 +359,13 @@ def paged_decode_attn(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor, 
         raise ValueError("q must be [B][Hq][D]")
     B, Hq, D = (int(x) for x in q.shape)
     _need(q, "q", torch.bfloat16, (batch.batch, Hq, cache.head_dim), dev)
+    if num_splits == BALANCED:
+        num_splits = -default_balanced_groups(cache.num_kv_heads)
+    num_splits = int(num_splits)
     if num_splits == 0:
         num_splits = default_num_splits(B, cache.num_kv_heads, batch.max_pages, cache.page_size)
-    num_splits = min(num_splits, batch.max_pages)
+    if num_splits > 0:
+        num_splits = min(num_splits, batch.max_pages)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, (B, Hq, D), dev)

@@ -82,6 +82,86 @@ def test_attention_matches_oracle(w, kv_dtype, splits):
     compare(out, lse, ro, rl, w.name)
 
 
+@pytest.mark.parametrize("kv_dtype", [ops.KV_FP8_E4M3, ops.KV_BF16], ids=["fp8", "bf16"])
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("groups", [1, 3, 40])
+def test_balanced_matches_oracle(w, kv_dtype, groups):
+    """The balanced partition (num_splits = -W): one work-group per head
+    (every request written whole), ranges that cut requests, and more
+    work-groups than pages (empty ranges)."""
+    say(f"attn balanced: {w.name} dtype={kv_dtype} W={groups}")
+    inp = I.make_decode_inputs(w, 21)
+    step = H.build_step(inp, kv_dtype, DEV, poison=True)
+    sm = 1.0 / math.sqrt(w.head_dim)
+    out, lse, status = run_gpu(step, sm, -groups)
+    assert np.all(status == 0)
+    ref = oracle_pool(inp, kv_dtype, poison=True)
+    assert pools_equal(step, ref, kv_dtype), "caches differ"
+    ks = inp.k_scale if kv_dtype == ops.KV_FP8_E4M3 else None
+    vs = inp.v_scale if kv_dtype == ops.KV_FP8_E4M3 else None
+    ro, rl = oracle.paged_attention(ref, inp.q, inp.batch.page_table, inp.batch.context_lens, sm,
+                                    ks, vs)
+    compare(out, lse, ro, rl, f"{w.name} W={groups}")
+
+
+def test_balanced_edge_requests():
+    """Balanced partition with aborted, empty and invalid requests between live
+    ones, a page id outside the pool inside a cut request, and the library's
+    default W: aborted and empty rows give 0 / -inf, invalid ones NaN, the bad
+    page's request NaN, and every other row matches the oracle."""
+    w = CASES[4]
+    inp = I.make_decode_inputs(w, 22)
+    step = H.build_step(inp, ops.KV_FP8_E4M3, DEV)
+    ops.kv_quant_append(step.cache, step.batch, step.k_new, step.v_new)
+    order = [0, 1, 2, 3, 0, 1, 2, 3]
+    q = step.q[order].contiguous()
+    pt = step.batch.page_table[order].clone()
+    lens = step.batch.context_lens[order].clone()
+    status = torch.zeros(8, dtype=torch.int32, device=DEV)
+    status[1] = 3                                   # aborted
+    lens[2] = 0                                     # empty
+    lens[5] = pt.shape[1] * w.page_size + 1         # past the table: invalid
+    live = [0, 3, 4, 6, 7]
+    bad_row = max(live, key=lambda r: int(lens[r]))
+    assert int(lens[bad_row]) > w.page_size
+    pt[bad_row, 1] = step.cache.num_pages + 7       # outside the pool, in page 1 of the longest
+    batch = ops.DecodeBatch(pt, lens, status)
+    want = oracle.paged_attention(oracle_pool(inp, oracle.KV_FP8), inp.q[order], pt.cpu().numpy(),
+                                  lens.cpu().numpy(), 0.09, inp.k_scale, inp.v_scale,
+                                  status=status.cpu().numpy())
+    for groups in (2, 5, ops.default_balanced_groups(w.kv_heads)):
+        out, lse = ops.paged_decode_attn(step.cache, batch, q, 0.09, -groups)
+        out, lse = out.cpu().numpy(), lse.cpu().numpy()
+        say(f"  balanced edges W={groups}")
+        for b in (1, 2):
+            assert np.all(out[b] == 0) and np.all(np.isneginf(lse[b])), b
+        assert np.all(np.isnan(out[5])) and np.all(np.isnan(lse[5]))
+        assert np.all(np.isnan(out[bad_row])) and np.all(np.isnan(lse[bad_row]))
+        good = [b for b in range(8) if b not in (1, 2, 5, bad_row)]
+        compare(out[good], lse[good], want[0][good], want[1][good], f"edges W={groups}")
+
+
+def test_balanced_against_uniform_splits_and_deterministic():
+    """Same attention as the uniform split path up to the fp16 rounding of P
+    against different running maxima (bound as in the split-invariance test),
+    and bitwise repeatable."""
+    w = CASES[4]
+    inp = I.make_decode_inputs(w, 23)
+    step = H.build_step(inp, ops.KV_FP8_E4M3, DEV)
+    ops.kv_quant_append(step.cache, step.batch, step.k_new, step.v_new)
+    base = [t.cpu().numpy() for t in ops.paged_decode_attn(step.cache, step.batch, step.q, 0.09, 1)]
+    vmax = 448.0 * float(inp.v_scale.max())
+    bound = 2.0 ** -10 * vmax + 1e-5
+    for groups in (2, 7, 64):
+        a = [t.cpu().numpy() for t in ops.paged_decode_attn(step.cache, step.batch, step.q, 0.09, -groups)]
+        b = [t.cpu().numpy() for t in ops.paged_decode_attn(step.cache, step.batch, step.q, 0.09, -groups)]
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), groups
+        diff = np.abs(a[0] - base[0]).max()
+        say(f"  balanced W={groups} vs S=1: max |diff| = {diff:.3e} (bound {bound:.3e})")
+        assert diff <= bound
+        assert np.allclose(a[1], base[1], rtol=1e-5, atol=1e-5)
+
+
 def test_default_split_choice_matches_oracle():
     w = CASES[4]
     inp = I.make_decode_inputs(w, 12)
@@ -241,3 +321,9 @@ def test_host_errors_are_reported():
     q33 = torch.zeros((2, 34, 128), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ops.Pafp8Error, match="group size"):
         ops.paged_decode_attn(step.cache, step.batch, q33[:, :34].contiguous(), 0.1, 1)
+    with pytest.raises(ops.Pafp8Error, match="at most 65536"):
+        ops.paged_decode_attn(step.cache, step.batch, step.q, 0.1, -65537)
+    need = ops.workspace_bytes(step.batch.batch, w.q_heads, w.head_dim, -8)
+    with pytest.raises(ops.Pafp8Error, match="workspace"):
+        ops.paged_decode_attn(step.cache, step.batch, step.q, 0.1, -8,
+                              torch.empty(need - 16, dtype=torch.uint8, device=DEV))

@@ -50,9 +50,11 @@ def check_replays(g, outputs, want, scramble, eager_between):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("kv_dtype,splits", [(ops.KV_FP8_E4M3, 4), (ops.KV_FP8_E4M3, 1), (ops.KV_BF16, 2)])
+@pytest.mark.parametrize("kv_dtype,splits", [(ops.KV_FP8_E4M3, 4), (ops.KV_FP8_E4M3, 1), (ops.KV_BF16, 2),
+                                             (ops.KV_FP8_E4M3, -8)])
 def test_decode_step_replays(kv_dtype, splits):
-    """Check + append + attention (+ combine when split) captured as one graph."""
+    """Check + append + attention (+ combine when split; splits < 0: the
+    balanced partition) captured as one graph."""
     say(f"graph: decode step dtype={kv_dtype} S={splits}")
     w = I.Workload("graph_step", 3, 16, 4, 128, 64, 300, 900, pool_factor=1.3, stale_requests=1)
     inp = I.make_decode_inputs(w, 31)

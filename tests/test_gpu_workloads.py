@@ -7,7 +7,8 @@ Workloads (named by what they are):
   gqa4_4k_outliers    8 requests, 32/8 heads, d128, 4096 tokens, 16-token pages,
                       1% outliers x20 saturating (all outputs)
   gqa8_ragged_32k     32 requests, 64/8 heads, d128, 1024..32768 tokens, 64-token pages,
-                      fragmented pool; e4m3 and the identical-source bf16 cache (3 sampled requests)
+                      fragmented pool; e4m3 and the identical-source bf16 cache, default
+                      splits and the balanced partition (3 sampled requests)
   gqa8_16k_b64        64 requests x 16384 tokens, 2 GiB pool (2 sampled requests); the
                       bf16 twin at 32 requests (1 sampled request)
   gqa8_256k_b4        4 requests x 262144 tokens, 64 splits, one stale request that must
@@ -124,12 +125,15 @@ def test_small_workloads_all_outputs(name):
     assert ok1 and ok2
 
 
+@pytest.mark.parametrize("splits", [0, ops.BALANCED], ids=["default", "balanced"])
 @pytest.mark.parametrize("kv_dtype", [ops.KV_FP8_E4M3, ops.KV_BF16], ids=["fp8", "bf16"])
-def test_ragged_32k(kv_dtype):
+def test_ragged_32k(kv_dtype, splits):
+    """Default splits and the balanced partition, whose ranges cut the longest
+    requests (sampled: the shortest, the longest and request 7)."""
     w = I.WORKLOADS["gqa8_ragged_32k"]
-    say(f"workload {w.name} dtype={kv_dtype}")
+    say(f"workload {w.name} dtype={kv_dtype} splits={splits}")
     inp = I.make_device_decode_inputs(w, 1002, DEV)
-    step, out, lse, status = run_step(inp, kv_dtype)
+    step, out, lse, status = run_step(inp, kv_dtype, splits)
     assert np.all(status == 0)
     lens = inp.batch.context_lens
     reqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 7})
