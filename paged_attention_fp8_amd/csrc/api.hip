@@ -205,7 +205,7 @@ pafp8_status attn_impl(const pafp8_cache *cache, const pafp8_batch *batch, const
     p.bal_groups = balanced ? -S : 0;
     p.sm_scale = sm_scale;
     if (balanced) {
-        const size_t R = static_cast<size_t>(batch->batch) - S - 1;  // B + W - 1
+        const size_t R = static_cast<size_t>(batch->batch) + static_cast<size_t>(-S) - 1;  // B + W - 1
         const size_t o_bytes = align16_up(static_cast<size_t>(Hq) * R * cache->head_dim * sizeof(float));
         const size_t l_bytes = align16_up(static_cast<size_t>(Hq) * R * sizeof(float));
         p.part_o = static_cast<float *>(ws);
@@ -374,7 +374,8 @@ size_t pafp8_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
         return 0;
     if (num_splits < 0) {
         // partial rows [Hq][B + W - 1][D], their LSEs, then B + 1 int64
-        const size_t rows = static_cast<size_t>(num_q_heads) * (static_cast<size_t>(batch) - num_splits - 1);
+        const size_t W = static_cast<size_t>(-num_splits);
+        const size_t rows = static_cast<size_t>(num_q_heads) * (static_cast<size_t>(batch) + W - 1);
         return align16_up(rows * static_cast<size_t>(head_dim) * sizeof(float)) +
                align16_up(rows * sizeof(float)) + (static_cast<size_t>(batch) + 1) * sizeof(int64_t);
     }
