@@ -15,7 +15,9 @@
 //  * one work-group = 4 wave64s = one (request, KV head, split); the split's
 //    tokens are dealt to the waves in tiles of 64 tokens (32 for bf16 pools,
 //    so that a tile is 16 KB of K+V either way) and the four partial softmax
-//    states are merged through LDS at the end;
+//    states are merged through LDS at the end.  In the balanced partition a
+//    work-group instead takes an equal range of all requests' pages of its
+//    KV head and runs the same per-range code on each request piece in it;
 //  * every lane issues 16-byte loads; a wave keeps about one tile (16 KB) in
 //    flight at all times with a single register buffer: the next tile's K
 //    loads go out as soon as Q.K^T has consumed this tile's K, its V loads as
