@@ -104,12 +104,15 @@ def run_step(inp, kv_dtype, splits=0):
     return step, out.cpu().numpy(), lse.cpu().numpy(), status.cpu().numpy()
 
 
+@pytest.mark.parametrize("balanced", [False, True], ids=["splits", "balanced"])
 @pytest.mark.parametrize("name", ["tiny_mha_d64_256", "gqa4_4k_outliers"])
-def test_small_workloads_all_outputs(name):
+def test_small_workloads_all_outputs(name, balanced):
+    """Every output, with the workload's split count and with the balanced
+    partition (for the single tiny request every range cuts it)."""
     w = I.WORKLOADS[name]
-    say(f"workload {name}")
+    say(f"workload {name} balanced={balanced}")
     inp = I.make_decode_inputs(w, 1001)
-    step, out, lse, status = run_step(inp, ops.KV_FP8_E4M3, w.num_splits)
+    step, out, lse, status = run_step(inp, ops.KV_FP8_E4M3, ops.BALANCED if balanced else w.num_splits)
     assert np.all(status == 0)
     ref = oracle_pool(inp, oracle.KV_FP8, poison=True)
     assert np.array_equal(step.cache.k_pool.cpu().numpy(), ref.k)
