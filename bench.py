@@ -554,8 +554,9 @@ def copy_calibration():
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
-              "the path shards by request or KV head with no exchange (see DESIGN.md)",
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); decode attention "
+              "shards by request or KV head with no exchange between GPUs, so the one-GPU figure "
+              "is the per-GPU throughput",
               file=sys.stderr)
         sys.exit(2)
     if args.summarize_counters:

@@ -34,7 +34,7 @@
  *          no infinities, a single NaN mantissa pattern (S.1111.111), largest
  *          finite magnitude 448.
  *
- * Readings where the pages are silent (all listed in the design doc):
+ * Readings where the pages are silent:
  *   - encoding rounds to nearest, ties to the even code, and saturates
  *     magnitudes >= 448 (and infinities) to +-448; NaN encodes as 0x7F|sign;
  *   - quantisation is enc(f32(x) / scale) with an IEEE single-precision
