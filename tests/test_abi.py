@@ -16,7 +16,8 @@ HEADER = os.path.join(ROOT, "include", "pafp8.h")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return re.findall(r"^\s*(?:const\s+)?(?:pafp8_status|size_t|int32_t|char)\s*\*?\s*(\w+)\s*\(",
                       text, flags=re.M)
@@ -47,7 +48,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_single_hip_runtime_mapped(L):
-    maps = open("/proc/self/maps").read()
+    with open("/proc/self/maps") as f:
+        maps = f.read()
     paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(paths) == 1, paths
 
