@@ -1,0 +1,71 @@
+"""Host-side logic of bench.py, without a GPU: the algorithmic byte count the
+roofline divides by, the one-GPU guard, and the scaling of the HBM counters
+by a copy of known size."""
+import csv
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_bytes_of_the_headline_launch():
+    """64 requests x 16384 tokens, 64 query / 8 KV heads, D = 128, 64-token
+    pages, e4m3: the sum written out term by term."""
+    B, L, Hq, Hkv, D, P = 64, 16384, 64, 8, 128, 64
+    kv = B * L * Hkv * D * 2 * 1          # K and V, one byte per element
+    table = B * (L // P) * 4              # one int32 page id per page
+    q = B * Hq * D * 2                    # bf16 queries
+    out = B * Hq * (D + 1) * 4            # fp32 out and lse
+    small = 2 * Hkv * 4 + B * 4 + B * 4   # scales, lengths, status
+    assert bench.algorithmic_bytes([L] * B, Hq, Hkv, D, P, 1) == kv + table + q + out + small
+    assert bench.algorithmic_bytes([L] * B, Hq, Hkv, D, P, 1) == 2150711872
+    # bf16 doubles only the KV term; no status without a check
+    assert (bench.algorithmic_bytes([L] * B, Hq, Hkv, D, P, 2, checked=False)
+            == 2 * kv + table + q + out + 2 * Hkv * 4 + B * 4)
+    # a ragged batch counts its own pages (a partial last page is one entry)
+    assert bench.algorithmic_bytes([1, 65], 8, 1, 64, 64, 1, checked=False) == \
+        (66 * 64 * 2) + 3 * 4 + 2 * 8 * 64 * 2 + 2 * 8 * 65 * 4 + 8 + 8
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and not r.stdout.strip()
+
+
+def _counter_dir(path, rows):
+    os.makedirs(path)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for kernel, counter, value in rows:
+            w.writerow({"Kernel_Name": kernel, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_counter_summary_scales_by_the_copy(tmp_path, monkeypatch):
+    """FETCH_SIZE and WRITE_SIZE (KiB) of the attention launches, each scaled
+    by known bytes / counted bytes of a 1 GiB copy; the median launch counts."""
+    attn = bench.ATTN_KERNEL + ", true>(pafp8::AttnParams)"
+    _counter_dir(tmp_path / "f", [(attn, "FETCH_SIZE", v) for v in (1000.0, 1100.0, 1050.0)]
+                 + [("other_kernel", "FETCH_SIZE", 9e9)])
+    _counter_dir(tmp_path / "w", [(attn, "WRITE_SIZE", v) for v in (10.0, 12.0, 11.0)])
+    gib_kib = (1 << 30) / 1024.0
+    _counter_dir(tmp_path / "cf", [("copyBuffer", "FETCH_SIZE", gib_kib / 2), ("copyBuffer", "FETCH_SIZE", 4.0)])
+    _counter_dir(tmp_path / "cw", [("copyBuffer", "WRITE_SIZE", gib_kib)])
+    out = tmp_path / "summary.md"
+    monkeypatch.setattr(bench, "COUNTERS_SUMMARY", str(out))
+    bench.summarize_counters(*(str(tmp_path / d) for d in ("f", "w", "cf", "cw")))
+    vals = dict(line.split(":", 1) for line in out.read_text().splitlines()
+                if ":" in line and not line.startswith(" "))
+    # fetch counts half the copy's bytes -> factor 2; write counts them all -> factor 1
+    assert float(vals["fetch_bytes_per_launch"]) == 1050.0 * 1024 * 2
+    assert float(vals["write_bytes_per_launch"]) == 11.0 * 1024
+    assert float(vals["traffic_bytes_per_launch"]) == 1050.0 * 1024 * 2 + 11.0 * 1024
+    assert bench.read_traffic(str(out)) == 1050.0 * 1024 * 2 + 11.0 * 1024
+    # figures taken on other sources are not used
+    out.write_text(out.read_text().replace(vals["source_hash"].strip(), "0" * 16))
+    assert bench.read_traffic(str(out)) is None
