@@ -49,25 +49,29 @@ _D = ctypes.c_double
 _F = ctypes.c_float
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (plain -O2, no fast-math, no FMA contraction)."""
-    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
-        return _LIB_PATH
-    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math, no FMA contraction).
+    src/out: another source and library path (the pins' mutation check
+    compiles altered copies this way)."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-o", tmp, _SRC, "-lm"]
+           "-fno-fast-math", "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 _lib = None
 
 
 def lib() -> ctypes.CDLL:
+    """The compiled oracle; PAFP8_ORACLE_LIB names another build of it (used
+    only by the pins' mutation check)."""
     global _lib
     if _lib is None:
-        _lib = ctypes.CDLL(build())
+        _lib = ctypes.CDLL(os.environ.get("PAFP8_ORACLE_LIB") or build())
         L = _lib
         L.oracle_e4m3_decode.restype = _D
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
