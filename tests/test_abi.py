@@ -123,7 +123,9 @@ def _attn(L, cache, batch, hq=64, sm=0.1, splits=1, q=4096, out=8192, fn="paged_
     (dict(hq=8 * 17), 2, "group size"),
     (dict(sm=0.0), 1, "sm_scale"),
     (dict(sm=float("nan")), 1, "sm_scale"),
-    (dict(splits=-1), 1, "num_splits"),
+    (dict(splits=-1), 1, "num_splits = -1 needs a workspace"),     # balanced, W = 1
+    (dict(splits=-65537), 1, "at most 65536"),
+    (dict(splits=-65536, batch_kw=dict(batch=2147483000)), 2, "too large"),
     (dict(splits=4), 1, "workspace"),
     (dict(q=0), 1, "q or out is NULL"),
 ])
@@ -132,6 +134,7 @@ def test_attention_validation_without_gpu(L, case, status, msg):
     batch = None if case.get("batch", 1) is None else _batch(**case.get("batch_kw", {}))
     st = _attn(L, cache, batch, hq=case.get("hq", 64), sm=case.get("sm", 0.1),
                splits=case.get("splits", 1), q=case.get("q", 4096))
+    assert msg in L.pafp8_last_error().decode(), L.pafp8_last_error()
     assert st == status
     assert msg in L.pafp8_last_error().decode()
 
