@@ -112,3 +112,23 @@ def test_gemv_edges():
         ops.int4_gemv(torch.zeros((1, 384), dtype=torch.bfloat16, device=DEV),
                       torch.zeros(16 * 384 // 2, dtype=torch.uint8, device=DEV),
                       torch.zeros((3, 16), dtype=torch.bfloat16, device=DEV), 16, 384)
+
+
+def _random_shapes(n, seed=2028):
+    g = np.random.default_rng(seed)
+    return [(int(g.integers(1, 81)), 16 * int(g.integers(1, 65)), 512 * int(g.integers(1, 9)))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(20))
+def test_gemv_random_shapes(M, N, K):
+    """Seeded random shapes (every launch path: 1 row, 2-32, 33-64, more than
+    64 rows), within the stated bound of the oracle."""
+    say(f"int4 gemv random: M={M} N={N} K={K}")
+    q, x, s = _case(M, N, K, 7 * M + 3 * N + K)
+    packed = int4_blocks(q)
+    y = ops.int4_gemv(_dev_bf16(x), _dev_u8(packed), _dev_bf16(s), N, K).cpu().numpy()
+    ref = oracle.int4_gemv(x, packed, s, N, K)
+    err = np.abs(y - ref)
+    bound = _bound(q, x, s)
+    assert np.all(err <= bound), (err.max(), (err / bound).max())
