@@ -16,8 +16,9 @@ Prints one JSON line.  value = attention tokens/s (one decode token per
 request through one attention layer per step).  roofline.achieved is the
 algorithmic bytes of one attention launch divided by its mean duration,
 measured with HIP events on the launch stream over the timed steps.  The
-bf16 twin (32 requests: the same KV bytes) and the tag-check overhead against
-the no-op tracker are reported beside it, and so is the long-context point
+bf16 twin (32 requests: the same KV bytes), the tag-check overhead against
+the no-op tracker, the step with the append inside the attention launch (at
+64 requests and at one) are reported beside it, and so is the long-context point
 (4 requests of 262,144 tokens in 64 splits: check overhead, and the batch
 with one stale request) and the prefill-to-decode hand-off (kv_quant_fill of
 8 prompts of 8,192 tokens) and a continuous decode loop with admission
@@ -128,7 +129,8 @@ class Point:
         live = [0 if b in self.inp.stale else int(L) for b, L in enumerate(self.lens)]
         self.bytes = algorithmic_bytes(live, Hq, self.w.kv_heads, D, self.w.page_size, elem)
 
-    def run(self, steps, warmup, splits, check=True, events=True, flush=False, fused=False):
+    def run(self, steps, warmup, splits, check=True, events=True, flush=False, fused=False,
+            append_in_attention=False):
         """Time `steps` decode steps.  flush: before every step, read
         FLUSH_BYTES of other device memory so that no step finds the previous
         one's KV bytes in the last-level caches (the 256 MB MALL holds a
@@ -161,6 +163,20 @@ class Point:
             if i is not None and flush:
                 sev[i][0].record()
             stat = None
+            if append_in_attention:   # the append inside the attention launch
+                if check:
+                    stat = ops.page_tag_check(st.batch, self.w.page_size, st.page_tags,
+                                              st.expected_tags, out=status)
+                b = st.batch.with_status(stat)
+                if i is not None and events:
+                    ev[i][0].record()
+                ops.paged_decode_attn(st.cache, b, st.q, self.sm, S, ws, out, lse,
+                                      k_new=st.k_new, v_new=st.v_new)
+                if i is not None and events:
+                    ev[i][1].record()
+                if i is not None and flush:
+                    sev[i][1].record()
+                return
             if fused:   # check and append in one launch
                 stat = ops.kv_quant_append_checked(st.cache, st.batch, st.page_tags,
                                                    st.expected_tags, st.k_new, st.v_new, out=status)
@@ -630,6 +646,22 @@ def main():
             "check_overhead_pct": 100.0 * (rf["ms_per_step"] - r0["ms_per_step"]) / r0["ms_per_step"],
         }
         del r0, rf
+        # the append inside the attention launch: same pool bytes and outputs,
+        # one launch fewer (at 64 requests, and at one request where launches
+        # weigh most)
+        ra = p.run(args.steps, args.warmup, args.splits, append_in_attention=True)
+        one = Point(1, ops.KV_FP8_E4M3, dev)
+        r1s = one.run(args.steps, args.warmup, 0)
+        r1f = one.run(args.steps, args.warmup, 0, append_in_attention=True)
+        result["append_in_attention"] = {
+            "step": "tag check + attention with the append in its launch, against tag check + "
+                    "append + attention",
+            "b64": {"ms_per_step": ra["ms_per_step"], "separate_ms_per_step": r["ms_per_step"],
+                    "tokens_per_s": B / (ra["ms_per_step"] * 1e-3)},
+            "b1": {"ms_per_step": r1f["ms_per_step"], "separate_ms_per_step": r1s["ms_per_step"],
+                   "tokens_per_s": 1 / (r1f["ms_per_step"] * 1e-3), "splits": r1f["splits"]},
+        }
+        del ra, one, r1s, r1f
         q = Point(32, ops.KV_BF16, dev)
         rb = q.run(args.steps, args.warmup, args.splits)
         bms = statistics.mean(rb["attn_ms"])

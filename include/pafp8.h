@@ -326,6 +326,32 @@ pafp8_status paged_decode_attn_bf16(const pafp8_cache *cache, const pafp8_batch 
                                     float *out, float *lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * paged_decode_attn_fp8_append / paged_decode_attn_bf16_append --
+ * kv_quant_append and the attention call of the same step in one launch
+ * (section "KV 缓存量化": decode writes this step's token into the e4m3 cache,
+ * then reads the cache converting on read).  Exactly as kv_quant_append(cache,
+ * batch, k_new, v_new) followed by paged_decode_attn_{fp8,bf16} with the same
+ * arguments: the same pool bytes and bitwise the same out and lse.  The one
+ * work-group of each (request, KV head) whose tokens end at the request's
+ * last token writes that token before it reads its tiles; no other
+ * work-group reads that slot.  Saves the append's launch and the gap after it.
+ *   k_new, v_new  device bf16 bit patterns [B][num_kv_heads][head_dim]
+ * Requests with a non-zero batch->req_status entry, an invalid length or a
+ * page id outside the pool are skipped by the append, as by kv_quant_append.
+ * ------------------------------------------------------------------------- */
+pafp8_status paged_decode_attn_fp8_append(const pafp8_cache *cache, const pafp8_batch *batch,
+                                          const uint16_t *q, int32_t num_q_heads, float sm_scale,
+                                          int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                          const uint16_t *k_new, const uint16_t *v_new, float *out,
+                                          float *lse, hipStream_t stream);
+
+pafp8_status paged_decode_attn_bf16_append(const pafp8_cache *cache, const pafp8_batch *batch,
+                                           const uint16_t *q, int32_t num_q_heads, float sm_scale,
+                                           int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                           const uint16_t *k_new, const uint16_t *v_new, float *out,
+                                           float *lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * splitk_combine -- merge per-split softmax partials (flash-decoding; not on
  * the pages, which leave long-context scheduling open).  For each (b, h):
  *   LSE = log sum_s exp(part_lse[b][h][s])

@@ -161,11 +161,15 @@ int device_cu_count()
 
 pafp8_status attn_impl(const pafp8_cache *cache, const pafp8_batch *batch, const uint16_t *q,
                        int32_t Hq, float sm_scale, int32_t S, void *ws, size_t ws_bytes,
-                       float *out, float *lse, hipStream_t stream, int want_dtype)
+                       float *out, float *lse, hipStream_t stream, int want_dtype,
+                       bool append = false, const uint16_t *k_new = nullptr,
+                       const uint16_t *v_new = nullptr)
 {
     pafp8_status st = check_attn(cache, batch, q, Hq, sm_scale, S, ws, ws_bytes, out, want_dtype);
     if (st != PAFP8_OK)
         return st;
+    if (append && batch->batch > 0 && (k_new == nullptr || v_new == nullptr))
+        return fail(PAFP8_EINVAL, "k_new or v_new is NULL");
     if (batch->batch == 0)
         return ok();
     if (S == 0)
@@ -191,6 +195,8 @@ pafp8_status attn_impl(const pafp8_cache *cache, const pafp8_batch *batch, const
     p.context_lens = batch->context_lens;
     p.req_status = batch->req_status;
     p.q = q;
+    p.k_new = append ? k_new : nullptr;
+    p.v_new = append ? v_new : nullptr;
     p.out = out;
     p.lse = lse;
     p.num_pages = cache->num_pages;
@@ -434,6 +440,26 @@ pafp8_status paged_decode_attn_bf16(const pafp8_cache *cache, const pafp8_batch 
 {
     return attn_impl(cache, batch, q, num_q_heads, sm_scale, num_splits, workspace,
                      workspace_bytes, out, lse, stream, PAFP8_KV_BF16);
+}
+
+pafp8_status paged_decode_attn_fp8_append(const pafp8_cache *cache, const pafp8_batch *batch,
+                                          const uint16_t *q, int32_t num_q_heads, float sm_scale,
+                                          int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                          const uint16_t *k_new, const uint16_t *v_new, float *out,
+                                          float *lse, hipStream_t stream)
+{
+    return attn_impl(cache, batch, q, num_q_heads, sm_scale, num_splits, workspace,
+                     workspace_bytes, out, lse, stream, PAFP8_KV_FP8_E4M3, true, k_new, v_new);
+}
+
+pafp8_status paged_decode_attn_bf16_append(const pafp8_cache *cache, const pafp8_batch *batch,
+                                           const uint16_t *q, int32_t num_q_heads, float sm_scale,
+                                           int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                           const uint16_t *k_new, const uint16_t *v_new, float *out,
+                                           float *lse, hipStream_t stream)
+{
+    return attn_impl(cache, batch, q, num_q_heads, sm_scale, num_splits, workspace,
+                     workspace_bytes, out, lse, stream, PAFP8_KV_BF16, true, k_new, v_new);
 }
 
 pafp8_status splitk_combine(const float *part_o, const float *part_lse, int32_t batch,

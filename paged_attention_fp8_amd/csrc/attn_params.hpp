@@ -17,6 +17,8 @@ struct AttnParams {
     const int32_t *context_lens;
     const int32_t *req_status;  // nullable
     const uint16_t *q;
+    const uint16_t *k_new;  // this step's token [B][Hkv][D] when the launch also appends it, else nullptr
+    const uint16_t *v_new;
     float *out;        // final [B][Hq][D] (when S == 1, and whole requests of a balanced launch)
     float *lse;        // final [B][Hq] or nullptr
     float *part_o;     // [B][Hq][S][D] (when S > 1); balanced: [Hq][B + W - 1][D]

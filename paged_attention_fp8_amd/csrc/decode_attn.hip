@@ -38,6 +38,7 @@
 // Arithmetic: scores and outputs accumulate in fp32, softmax in the exp2
 // domain; the result is exact up to fp32 rounding.
 #include "attn_params.hpp"
+#include "pafp8_append.hpp"
 #include "pafp8_device.hpp"
 
 namespace pafp8 {
@@ -82,6 +83,33 @@ __device__ __forceinline__ SplitRange split_range(const AttnParams &p, int b, in
     return r;
 }
 
+// The append taken into the attention launch: the one work-group of a
+// (request, KV head) whose tokens end at the request's last token writes that
+// token first (thread d, head dim d; nothing when its page lies outside the
+// pool), and the work-group barrier orders the stores before any of its waves
+// loads the tile that holds them.  No other work-group reads that slot.
+// The token's V bytes land one in each of D rows of its segment; written
+// while the rest of the GPU streams, such scattered partial-line stores slow
+// the launch when every work-group of a large batch makes them (one request
+// per work-group), so the fused launch pays off where launches dominate.
+template <bool BF16, int D>
+__device__ __forceinline__ void append_new_token(const AttnParams &p, int b, int g, int64_t L)
+{
+    const int64_t pos = L - 1;
+    const int32_t page = p.page_table[static_cast<int64_t>(b) * p.max_pages + (pos >> p.log2_page)];
+    if (page >= 0 && page < p.num_pages) {
+        const int slot = static_cast<int>(pos & ((int64_t{1} << p.log2_page) - 1));
+        for (int d = threadIdx.x; d < D; d += kThreads) {
+            const int64_t src = (static_cast<int64_t>(b) * p.num_kv_heads + g) * D + d;
+            append_token_element<BF16, D, true>(const_cast<uint8_t *>(p.k_pool), const_cast<uint8_t *>(p.v_pool),
+                                          page, p.num_kv_heads, g, p.log2_page, slot, d, p.k_new[src],
+                                          p.v_new[src], BF16 ? 1.0f : p.k_scale[g],
+                                          BF16 ? 1.0f : p.v_scale[g]);
+        }
+    }
+    __syncthreads();
+}
+
 // Physical pages of the four token groups of a tile (group q covers tokens
 // T0 + q*tpg .. + tpg, always inside one page).  The page ids are
 // wave-uniform and come in through scalar loads; they are fetched a tile ahead
@@ -91,8 +119,21 @@ struct TilePages {
     int32_t pid[4];
 };
 
+// A request's page-table row, read through the constant address space: the
+// table does not change during a launch, and saying so keeps its wave-uniform
+// reads on the scalar path even in kernels that also write the pool (the
+// append taken into the launch), where the compiler could otherwise not rule
+// out that the stores change the table and would issue vector loads, which
+// queue behind the tile loads and stall the pipeline.
+typedef const __attribute__((address_space(4))) int32_t *page_row_t;
+
+__device__ __forceinline__ page_row_t page_row(const AttnParams &p, int b)
+{
+    return (page_row_t)(p.page_table + static_cast<int64_t>(b) * p.max_pages);
+}
+
 template <bool ONE_PAGE = false>
-__device__ __forceinline__ TilePages fetch_pages(const int32_t *__restrict__ row, int64_t T0,
+__device__ __forceinline__ TilePages fetch_pages(page_row_t __restrict__ row, int64_t T0,
                                                  int tpg, int log2_page, int64_t p_last)
 {
     TilePages t;
@@ -629,7 +670,7 @@ __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm,
             }
         }
         const float cs = (BF16 ? 1.0f : p.k_scale[g]) * p.sm_scale * kLog2e;
-        const int32_t *row = p.page_table + static_cast<int64_t>(b) * p.max_pages;
+        const page_row_t row = page_row(p, b);
         const int stride = kWaves * G_::TT;
 
         // Staggered pipeline, one tile buffer per wave: the next tile's K is
@@ -688,7 +729,7 @@ __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm,
     return bad;
 }
 
-template <bool BF16, int D, bool BIG>
+template <bool BF16, int D, bool BIG, bool APPEND>
 __global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel(AttnParams p)
 {
     __shared__ MergeSmem<D> sm;
@@ -700,6 +741,11 @@ __global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel
     const int b = idx / p.num_kv_heads;
 
     const SplitRange rng = split_range(p, b, s);
+    if constexpr (APPEND) {
+        const int64_t L = p.context_lens[b];
+        if (rng.state == 0 && rng.t0 < rng.t1 && rng.t1 == L)
+            append_new_token<BF16, D>(p, b, g, L);
+    }
     int bad = mfma_range<BF16, D, BIG>(p, sm, b, g, rng);
     bad = __syncthreads_or(bad);
     merge_and_write<D>(sm, p.group, rng.state, bad, BF16 ? 1.0f : p.v_scale[g],
@@ -708,7 +754,7 @@ __global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel
 
 // Balanced partition: the work-group takes pages [lo, hi) of its KV head's
 // concatenated live pages and attends to each request piece in turn.
-template <bool BF16, int D, bool BIG>
+template <bool BF16, int D, bool BIG, bool APPEND>
 __global__ __launch_bounds__(kThreads, 2) void decode_attn_bal_mfma_kernel(AttnParams p)
 {
     __shared__ MergeSmem<D> sm;
@@ -722,6 +768,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_bal_mfma_kernel(AttnP
         const ReqPages rq = request_pages(p, b);
         if (rq.n > 0) {
             const SplitRange rng = piece_range(p, r, ps, rq);
+            if constexpr (APPEND) {
+                if (ps + rq.n <= r.hi)  // the piece ends at the request's last token
+                    append_new_token<BF16, D>(p, b, g, rq.L);
+            }
             int bad = mfma_range<BF16, D, BIG>(p, sm, b, g, rng);
             bad = __syncthreads_or(bad);
             merge_and_write<D>(sm, p.group, 0, bad, BF16 ? 1.0f : p.v_scale[g],
@@ -801,7 +851,7 @@ __device__ __forceinline__ int vec_range(const AttnParams &p, VecSmem<D> &sm, in
     const int64_t page_bytes = head_bytes * p.num_kv_heads;
     const uint8_t *k_head = p.k_pool + g * head_bytes;
     const uint8_t *v_head = p.v_pool + g * head_bytes;
-    const int32_t *row = p.page_table + static_cast<int64_t>(b) * p.max_pages;
+    const page_row_t row = page_row(p, b);
     // segment of the block layout: min(page, 64 bytes / element) tokens
     const int log2_seg = p.log2_page < (BF16 ? 5 : 6) ? p.log2_page : (BF16 ? 5 : 6);
 
@@ -894,7 +944,7 @@ __device__ __forceinline__ int vec_range(const AttnParams &p, VecSmem<D> &sm, in
     return bad;
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool APPEND>
 __global__ __launch_bounds__(kThreads) void decode_attn_vec_kernel(AttnParams p)
 {
     __shared__ VecSmem<D> sm;
@@ -906,13 +956,18 @@ __global__ __launch_bounds__(kThreads) void decode_attn_vec_kernel(AttnParams p)
     const int b = idx / p.num_kv_heads;
 
     const SplitRange rng = split_range(p, b, s);
+    if constexpr (APPEND) {
+        const int64_t L = p.context_lens[b];
+        if (rng.state == 0 && rng.t0 < rng.t1 && rng.t1 == L)
+            append_new_token<BF16, D>(p, b, g, L);
+    }
     int bad = vec_range<BF16, D>(p, sm, b, g, rng);
     bad = __syncthreads_or(bad);
     merge_and_write<D>(sm.merge, 1, rng.state, bad, BF16 ? 1.0f : p.v_scale[g],
                        split_dst<D>(p, b, g, s));
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool APPEND>
 __global__ __launch_bounds__(kThreads) void decode_attn_bal_vec_kernel(AttnParams p)
 {
     __shared__ VecSmem<D> sm;
@@ -926,6 +981,10 @@ __global__ __launch_bounds__(kThreads) void decode_attn_bal_vec_kernel(AttnParam
         const ReqPages rq = request_pages(p, b);
         if (rq.n > 0) {
             const SplitRange rng = piece_range(p, r, ps, rq);
+            if constexpr (APPEND) {
+                if (ps + rq.n <= r.hi)  // the piece ends at the request's last token
+                    append_new_token<BF16, D>(p, b, g, rq.L);
+            }
             int bad = vec_range<BF16, D>(p, sm, b, g, rng);
             bad = __syncthreads_or(bad);
             merge_and_write<D>(sm.merge, 1, 0, bad, BF16 ? 1.0f : p.v_scale[g],
@@ -936,7 +995,7 @@ __global__ __launch_bounds__(kThreads) void decode_attn_bal_vec_kernel(AttnParam
     }
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool APPEND>
 hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
 {
     const bool bal = p.bal_groups > 0;
@@ -947,19 +1006,19 @@ hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
     const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
     if (p.group == 1) {
         if (bal)
-            hipLaunchKernelGGL((decode_attn_bal_vec_kernel<BF16, D>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((decode_attn_bal_vec_kernel<BF16, D, APPEND>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((decode_attn_vec_kernel<BF16, D>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((decode_attn_vec_kernel<BF16, D, APPEND>), grid, block, 0, stream, p);
     } else if (p.log2_page >= Geo<BF16, D>::LOG2_TT) {
         if (bal)
-            hipLaunchKernelGGL((decode_attn_bal_mfma_kernel<BF16, D, true>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((decode_attn_bal_mfma_kernel<BF16, D, true, APPEND>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, true>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, true, APPEND>), grid, block, 0, stream, p);
     } else {
         if (bal)
-            hipLaunchKernelGGL((decode_attn_bal_mfma_kernel<BF16, D, false>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((decode_attn_bal_mfma_kernel<BF16, D, false, APPEND>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, false>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, false, APPEND>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }
@@ -969,9 +1028,15 @@ hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
 hipError_t launch_decode_attn(bool bf16_pool, int head_dim, const AttnParams &p,
                               hipStream_t stream)
 {
-    if (bf16_pool)
-        return head_dim == 64 ? launch_attn_t<true, 64>(p, stream) : launch_attn_t<true, 128>(p, stream);
-    return head_dim == 64 ? launch_attn_t<false, 64>(p, stream) : launch_attn_t<false, 128>(p, stream);
+    const bool app = p.k_new != nullptr;
+    if (bf16_pool) {
+        if (head_dim == 64)
+            return app ? launch_attn_t<true, 64, true>(p, stream) : launch_attn_t<true, 64, false>(p, stream);
+        return app ? launch_attn_t<true, 128, true>(p, stream) : launch_attn_t<true, 128, false>(p, stream);
+    }
+    if (head_dim == 64)
+        return app ? launch_attn_t<false, 64, true>(p, stream) : launch_attn_t<false, 64, false>(p, stream);
+    return app ? launch_attn_t<false, 128, true>(p, stream) : launch_attn_t<false, 128, false>(p, stream);
 }
 
 }  // namespace pafp8

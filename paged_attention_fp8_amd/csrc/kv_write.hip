@@ -19,6 +19,7 @@
 // quantised values of one head dim across tokens in the packed conversion,
 // and in a whole e4m3 tile of a page of 64 tokens or more its rows are
 // assembled in LDS so that they leave as 1 KiB runs.
+#include "pafp8_append.hpp"
 #include "pafp8_device.hpp"
 #include "pafp8_internal.hpp"
 #include "pafp8_quant.hpp"
@@ -53,35 +54,11 @@ __global__ __launch_bounds__(D) void kv_append_kernel(WriteParams p)
     const int32_t page = p.page_table[static_cast<int64_t>(b) * p.max_pages + (pos >> p.log2_page)];
     if (page < 0 || page >= p.num_pages)
         return;
-    constexpr int E = BF16 ? 2 : 1;
-    constexpr int LOG2_TG = BF16 ? 3 : 4, KL = D * E / 64;
     const int slot = static_cast<int>(pos & ((int64_t{1} << p.log2_page) - 1));
-    const int64_t head_block = (static_cast<int64_t>(page) * p.num_kv_heads + g) << p.log2_page;
-    // Block layout (include/pafp8.h): segments of SEG = min(P, 64/E) slots.
-    // K: slot TG*sub + 4j + a of a segment (TG = 16/E) keeps its 16-byte
-    // chunk q*KL + l at chunk ((j*KL + l)*4 + q)*(4*NS) + 4*sub + a, NS =
-    // SEG/TG; thread d's element is byte (d*E) % 16 of chunk d*E/16.  V: a
-    // segment is [D][SEG].
-    const int log2_seg = p.log2_page < (BF16 ? 5 : 6) ? p.log2_page : (BF16 ? 5 : 6);
-    const int log2_ns = log2_seg - LOG2_TG;
-    const int seg = slot >> log2_seg, u = slot & ((1 << log2_seg) - 1);
-    const int w = u & ((1 << LOG2_TG) - 1);
-    const int c = d * E / 16;
-    const int kq = c / KL, kl = c % KL;
-    uint8_t *kdst = p.k_pool + (head_block * D + (static_cast<int64_t>(seg) * D << log2_seg)) * E +
-                    (((((w >> 2) * KL + kl) * 4 + kq) << (2 + log2_ns)) + ((u >> LOG2_TG) << 2) + (w & 3)) * 16 +
-                    (d * E) % 16;
-    uint8_t *vdst = p.v_pool + (head_block * D + ((static_cast<int64_t>(seg) * D + d) << log2_seg) + u) * E;
     const int64_t src = (static_cast<int64_t>(b) * p.num_kv_heads + g) * D + d;
-    const uint16_t kx = p.k_src[src];
-    const uint16_t vx = p.v_src[src];
-    if (BF16) {
-        *reinterpret_cast<uint16_t *>(kdst) = kx;
-        *reinterpret_cast<uint16_t *>(vdst) = vx;
-    } else {
-        *kdst = static_cast<uint8_t>(quantize_bf16(kx, make_quantizer(p.k_scale[g])));
-        *vdst = static_cast<uint8_t>(quantize_bf16(vx, make_quantizer(p.v_scale[g])));
-    }
+    append_token_element<BF16, D>(p.k_pool, p.v_pool, page, p.num_kv_heads, g, p.log2_page, slot, d,
+                                  p.k_src[src], p.v_src[src], BF16 ? 1.0f : p.k_scale[g],
+                                  BF16 ? 1.0f : p.v_scale[g]);
 }
 
 // --- fill ---------------------------------------------------------------------

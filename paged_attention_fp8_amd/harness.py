@@ -120,11 +120,20 @@ def build_step(inp, kv_dtype: int, device, poison: bool = True) -> DeviceStep:
 
 def decode_step(step: DeviceStep, sm_scale: float, num_splits: int = 0, check: bool = True,
                 workspace: Optional[torch.Tensor] = None, out=None, lse=None,
-                fused: bool = False):
+                fused: bool = False, append_in_attention: bool = False):
     """One decode step of the path: tag check (unless check=False: no-op
     tracker), append, attention (with its split-K combine).  fused: the check
-    runs inside the append launch (kv_quant_append_checked)."""
+    runs inside the append launch (kv_quant_append_checked).
+    append_in_attention: the append runs inside the attention launch."""
     status = None
+    if append_in_attention:
+        if check:
+            status = ops.page_tag_check(step.batch, step.cache.page_size, step.page_tags,
+                                        step.expected_tags)
+        b = step.batch.with_status(status)
+        o, l = ops.paged_decode_attn(step.cache, b, step.q, sm_scale, num_splits, workspace, out, lse,
+                                     k_new=step.k_new, v_new=step.v_new)
+        return o, l, status
     if fused:
         status = ops.kv_quant_append_checked(step.cache, step.batch, step.page_tags,
                                              step.expected_tags, step.k_new, step.v_new)

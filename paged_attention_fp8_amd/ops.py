@@ -61,6 +61,8 @@ _SIGNATURES = {
     "pafp8_default_balanced_groups": (_I32, [_I32, _I32]),
     "paged_decode_attn_fp8": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V]),
     "paged_decode_attn_bf16": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V]),
+    "paged_decode_attn_fp8_append": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V, _V, _V]),
+    "paged_decode_attn_bf16_append": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V, _V, _V]),
     "splitk_combine": (_I32, [_V, _V, _I32, _I32, _I32, _I32, _V, _V, _V, _V]),
     "pafp8_e4m3_encode": (_I32, [_V, _V, _I64, _V]),
     "pafp8_e4m3_decode": (_I32, [_V, _V, _V, _V, _I64, _V]),
@@ -346,9 +348,12 @@ BALANCED = "balanced"
 def paged_decode_attn(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor, sm_scale: float,
                       num_splits=0, workspace: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                      return_lse: bool = True):
+                      return_lse: bool = True, k_new: Optional[torch.Tensor] = None,
+                      v_new: Optional[torch.Tensor] = None):
     """Decode attention over the paged cache; dispatches to
-    paged_decode_attn_fp8 or paged_decode_attn_bf16 by the pool's dtype.
+    paged_decode_attn_fp8 or paged_decode_attn_bf16 by the pool's dtype, or,
+    given this step's k_new and v_new (bf16 [B][Hkv][D]), to their _append
+    forms, which write that token in the same launch.
     num_splits: S >= 1 uniform splits, 0 the library's default, -W (or
     BALANCED for pafp8_default_balanced_groups) the balanced partition over W
     work-groups per KV head.
@@ -380,6 +385,18 @@ def paged_decode_attn(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor, 
     if workspace is not None:
         _need(workspace, "workspace", workspace.dtype, device=dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        shape = (B, cache.num_kv_heads, cache.head_dim)
+        _kv_src(k_new, "k_new", shape, dev)
+        _kv_src(v_new, "v_new", shape, dev)
+        fn = (lib().paged_decode_attn_bf16_append if cache.kv_dtype == KV_BF16
+              else lib().paged_decode_attn_fp8_append)
+        _check(fn(ctypes.byref(cs), ctypes.byref(bs), q.data_ptr(), Hq, float(sm_scale), num_splits,
+                  ws_ptr, ws_bytes, k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(), _ptr(lse),
+                  _stream(dev)), "paged_decode_attn (append)")
+        return out, lse
     fn = lib().paged_decode_attn_bf16 if cache.kv_dtype == KV_BF16 else lib().paged_decode_attn_fp8
     _check(fn(ctypes.byref(cs), ctypes.byref(bs), q.data_ptr(), Hq, float(sm_scale), num_splits,
               ws_ptr, ws_bytes, out.data_ptr(), _ptr(lse), _stream(dev)),
