@@ -188,3 +188,18 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ops, "_lib", None)
     with pytest.raises(ops.Pafp8Error, match="not built"):
         ops.lib()
+
+
+def test_fused_append_entries_validate_without_gpu(L):
+    """The append-in-attention entries check what the attention entries check,
+    plus the new token's pointers, before any HIP call."""
+    def call(fn, cache, k_new=8192, v_new=8192, batch=None):
+        b = batch if batch is not None else _batch()
+        return getattr(L, fn)(ctypes.byref(cache), ctypes.byref(b), 4096, 64, 0.1, 1, None, 0,
+                              k_new, v_new, 8192, None, None)
+    assert call("paged_decode_attn_fp8_append", _cache(), k_new=None) == 1
+    assert "k_new or v_new is NULL" in L.pafp8_last_error().decode()
+    assert call("paged_decode_attn_fp8_append", _cache(), v_new=None) == 1
+    assert call("paged_decode_attn_bf16_append", _cache()) == 1        # e4m3 pool
+    assert "does not match" in L.pafp8_last_error().decode()
+    assert call("paged_decode_attn_fp8_append", _cache(), k_new=None, batch=_batch(batch=0)) == 0
