@@ -34,7 +34,9 @@
 //    online softmax needs two cross-lane max exchanges per tile and no other
 //    data movement;
 //  * G == 1: there is no contraction to speak of, so a vector path does the
-//    dot products with FMAs (lane = token for Q.K, lane = head dim for P.V).
+//    dot products with FMAs (lane = token for Q.K, lane = head dim for P.V);
+//  * every kernel has an APPEND instantiation that also writes the step's new
+//    token (the append taken into the attention launch).
 // Arithmetic: scores and outputs accumulate in fp32, softmax in the exp2
 // domain; the result is exact up to fp32 rounding.
 #include "attn_params.hpp"
