@@ -1,8 +1,9 @@
 """Build libpafp8.so (HIP, gfx950) in-tree.
 
-    python -m paged_attention_fp8_amd.build [--asm]
+    python -m paged_attention_fp8_amd.build [--asm OUT_DIR]
 
-Compiles every csrc/*.hip into one shared library next to this file.  Packed
+Compiles every csrc/*.hip into one shared library next to this file (with
+--asm, also writes each source's device assembly into OUT_DIR).  Packed
 FP32 instructions are disabled (-packed-fp32-ops) and no fast-math flag is
 used, so fp32 division stays correctly rounded.
 """
@@ -60,5 +61,8 @@ def emit_asm(out_dir: str) -> None:
 
 if __name__ == "__main__":
     if "--asm" in sys.argv:
-        emit_asm(os.path.join(ROOT, "_work", "asm"))
+        i = sys.argv.index("--asm")
+        if i + 1 >= len(sys.argv):
+            sys.exit("--asm needs an output directory")
+        emit_asm(os.path.abspath(sys.argv[i + 1]))
     print(build(verbose=True))

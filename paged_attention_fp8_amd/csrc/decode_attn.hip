@@ -27,8 +27,10 @@
 //    the whole query group shares one K/V tile held in registers.  Q.K^T takes
 //    the tile's tokens as rows and the group's heads as columns (K decoded
 //    exactly to bf16; Q is bf16 already); P.V takes head dims as rows (V
-//    decoded exactly to fp16, P rounded to fp16; bf16 pools split P into a
-//    bf16 high and low part).  Token order inside a tile is permuted so that
+//    exact in bf16, P split into a bf16 high and low part; with at most 8
+//    heads in the group the low part rides in the MFMA columns the group
+//    leaves free, otherwise it takes a second MFMA).
+//    Token order inside a tile is permuted so that
 //    the scores an MFMA leaves in a lane are exactly the P operand that lane
 //    feeds to the next MFMA, and the head a lane owns never changes: the
 //    online softmax needs two cross-lane max exchanges per tile and no other
@@ -336,12 +338,15 @@ __device__ __forceinline__ void mfma_qk(const MfmaTile<BF16, D> &t,
 
 // Online softmax of one tile's scores, then O^T += V^T P^T (rows = head dims,
 // columns = heads).  TAIL masks tokens at or past t1 (only a split's last
-// tile can hold such tokens).
-template <bool BF16, int D, bool TAIL>
+// tile can hold such tokens).  DUP (groups of at most 8 heads): column h + 8
+// holds a copy of head h (the same query, hence the same scores and softmax
+// state), and feeds the low part of P where column h feeds the high part, so
+// one MFMA takes both; lo_lane marks the lanes of columns 8..15.
+template <bool BF16, int D, bool TAIL, bool DUP>
 __device__ __forceinline__ void mfma_softmax_pv(const MfmaTile<BF16, D> &t,
                                                 const f32x4 (&sacc)[Geo<BF16, D>::NJ],
                                                 MfmaState<BF16, D> &st, float cs, int64_t T0,
-                                                int64_t t1, int lane_g)
+                                                int64_t t1, int lane_g, bool lo_lane)
 {
     using G_ = Geo<BF16, D>;
     // lane holds the scores of tokens T0 + lane_g*TPG + n, n = 4j + v
@@ -379,41 +384,44 @@ __device__ __forceinline__ void mfma_softmax_pv(const MfmaTile<BF16, D> &t,
 #pragma unroll
     for (int dt = 0; dt < G_::NDT; ++dt)
         st.o[dt] *= alpha;
+    // P enters the P.V MFMAs as a bf16 high part plus a bf16 low part (the
+    // rounding error of the high part, itself rounded): together they carry
+    // P to about 2^-16 relative, over the whole fp32 exponent range, so that
+    // no weight is flushed however peaked the softmax.  V is exact in bf16
+    // for both pool types (e4m3 decodes exactly to bf16).
 #pragma unroll
     for (int c = 0; c < G_::NPC; ++c) {
-        if constexpr (BF16) {
-            u32x4 hi, lo;
+        u32x4 hi, lo;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float a = pr[c * 8 + 2 * e], b = pr[c * 8 + 2 * e + 1];
-                hi[e] = pack_bf16x2(a, b);
-                lo[e] = pack_bf16x2(a - bf16_lo(hi[e]), b - bf16_hi(hi[e]));
-            }
-            const bf16x8 phi = __builtin_bit_cast(bf16x8, hi);
-            const bf16x8 plo = __builtin_bit_cast(bf16x8, lo);
-#pragma unroll
-            for (int dt = 0; dt < G_::NDT; ++dt) {
-                u32x4 w = t.v[dt];
-                if constexpr (TAIL)
-                    w = keep_bytes(w, nvalid * 2);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, w);
-                st.o[dt] = mfma_bf16(a, phi, st.o[dt]);
-                st.o[dt] = mfma_bf16(a, plo, st.o[dt]);
-            }
-        } else {
-            u32x4 pw;
+        for (int e = 0; e < 4; ++e) {
+            const float a = pr[c * 8 + 2 * e], b = pr[c * 8 + 2 * e + 1];
+            hi[e] = pack_bf16x2(a, b);
+            lo[e] = pack_bf16x2(a - bf16_lo(hi[e]), b - bf16_hi(hi[e]));
+        }
+        u32x4 mine;
+        if constexpr (DUP) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                pw[e] = pack_f16x2(pr[c * 8 + 2 * e], pr[c * 8 + 2 * e + 1]);
-            const f16x8 pb = __builtin_bit_cast(f16x8, pw);
+                mine[e] = lo_lane ? lo[e] : hi[e];
+        }
+        const bf16x8 phi = __builtin_bit_cast(bf16x8, DUP ? mine : hi);
+        const bf16x8 plo = __builtin_bit_cast(bf16x8, lo);
 #pragma unroll
-            for (int dt = 0; dt < G_::NDT; ++dt) {
-                u32x4 w = t.v[dt];
+        for (int dt = 0; dt < G_::NDT; ++dt) {
+            u32x4 w = t.v[dt];
+            bf16x8 a;
+            if constexpr (BF16) {
+                if constexpr (TAIL)
+                    w = keep_bytes(w, nvalid * 2);
+                a = __builtin_bit_cast(bf16x8, w);
+            } else {
                 if constexpr (TAIL)
                     w = keep_bytes(w, nvalid);
-                const f16x8 a = e4m3x8_to_f16x8(w[2 * c], w[2 * c + 1]);
-                st.o[dt] = mfma_f16(a, pb, st.o[dt]);
+                a = e4m3x8_to_bf16x8(w[2 * c], w[2 * c + 1]);
             }
+            st.o[dt] = mfma_bf16(a, phi, st.o[dt]);
+            if constexpr (!DUP)
+                st.o[dt] = mfma_bf16(a, plo, st.o[dt]);
         }
     }
 }
@@ -632,7 +640,7 @@ __device__ __forceinline__ MergeDst piece_dst(const AttnParams &p, const BalRang
 
 // Request b, KV head g over tokens [rng.t0, rng.t1): each wave's softmax
 // state ends up in sm.  Returns non-zero if a page id lay outside the pool.
-template <bool BF16, int D, bool BIG>
+template <bool BF16, int D, bool BIG, bool DUP>
 __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm, int b, int g,
                                           const SplitRange &rng)
 {
@@ -659,10 +667,11 @@ __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm,
         c.log2_page = p.log2_page;
         c.lane_r = lane & 15;
         c.lane_g = lane >> 4;
-        // Q operand: head r of the group, head dims [g*D/4, (g+1)*D/4)
+        // Q operand: head r of the group (with DUP, head r mod 8), head dims
+        // [g*D/4, (g+1)*D/4)
         bf16x8 qop[G_::NC];
         {
-            const int r = c.lane_r;
+            const int r = DUP ? (c.lane_r & 7) : c.lane_r;
             const uint16_t *qrow = p.q + (static_cast<int64_t>(b) * p.num_q_heads + g * G + r) * D +
                                    c.lane_g * (D / 4);
 #pragma unroll
@@ -674,6 +683,7 @@ __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm,
         const float cs = (BF16 ? 1.0f : p.k_scale[g]) * p.sm_scale * kLog2e;
         const page_row_t row = page_row(p, b);
         const int stride = kWaves * G_::TT;
+        const bool lo_lane = c.lane_r >= 8;
 
         // Staggered pipeline, one tile buffer per wave: the next tile's K is
         // loaded as soon as Q.K^T has consumed this tile's K, and its V as
@@ -701,7 +711,7 @@ __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm,
             __builtin_amdgcn_sched_barrier(0);
             mfma_load_k<BF16, D, BIG>(t, c, T0 + stride, pn);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_softmax_pv<BF16, D, false>(t, sacc, st, cs, T0, rng.t1, c.lane_g);
+            mfma_softmax_pv<BF16, D, false, DUP>(t, sacc, st, cs, T0, rng.t1, c.lane_g, lo_lane);
             __builtin_amdgcn_sched_barrier(0);
             mfma_load_v<BF16, D, BIG>(t, c, T0 + stride, pn);
             __builtin_amdgcn_sched_barrier(0);
@@ -711,9 +721,17 @@ __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm,
         }
         mfma_qk(t, qop, sacc);
         if (T0 + G_::TT > rng.t1)
-            mfma_softmax_pv<BF16, D, true>(t, sacc, st, cs, T0, rng.t1, c.lane_g);
+            mfma_softmax_pv<BF16, D, true, DUP>(t, sacc, st, cs, T0, rng.t1, c.lane_g, lo_lane);
         else
-            mfma_softmax_pv<BF16, D, false>(t, sacc, st, cs, T0, rng.t1, c.lane_g);
+            mfma_softmax_pv<BF16, D, false, DUP>(t, sacc, st, cs, T0, rng.t1, c.lane_g, lo_lane);
+    }
+    if constexpr (DUP) {
+        // column h + 8 accumulated V times the low part of head h's weights
+#pragma unroll
+        for (int dt = 0; dt < G_::NDT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                st.o[dt][e] += shfl_xor_f(st.o[dt][e], 8);
     }
     // the four lanes of a head each hold a quarter of its denominator
     float l = st.l + shfl_xor_f(st.l, 16);
@@ -731,7 +749,7 @@ __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm,
     return bad;
 }
 
-template <bool BF16, int D, bool BIG, bool APPEND>
+template <bool BF16, int D, bool BIG, bool APPEND, bool DUP>
 __global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel(AttnParams p)
 {
     __shared__ MergeSmem<D> sm;
@@ -748,7 +766,7 @@ __global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel
         if (rng.state == 0 && rng.t0 < rng.t1 && rng.t1 == L)
             append_new_token<BF16, D>(p, b, g, L);
     }
-    int bad = mfma_range<BF16, D, BIG>(p, sm, b, g, rng);
+    int bad = mfma_range<BF16, D, BIG, DUP>(p, sm, b, g, rng);
     bad = __syncthreads_or(bad);
     merge_and_write<D>(sm, p.group, rng.state, bad, BF16 ? 1.0f : p.v_scale[g],
                        split_dst<D>(p, b, g, s));
@@ -756,7 +774,7 @@ __global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel
 
 // Balanced partition: the work-group takes pages [lo, hi) of its KV head's
 // concatenated live pages and attends to each request piece in turn.
-template <bool BF16, int D, bool BIG, bool APPEND>
+template <bool BF16, int D, bool BIG, bool APPEND, bool DUP>
 __global__ __launch_bounds__(kThreads, 2) void decode_attn_bal_mfma_kernel(AttnParams p)
 {
     __shared__ MergeSmem<D> sm;
@@ -774,7 +792,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_bal_mfma_kernel(AttnP
                 if (ps + rq.n <= r.hi)  // the piece ends at the request's last token
                     append_new_token<BF16, D>(p, b, g, rq.L);
             }
-            int bad = mfma_range<BF16, D, BIG>(p, sm, b, g, rng);
+            int bad = mfma_range<BF16, D, BIG, DUP>(p, sm, b, g, rng);
             bad = __syncthreads_or(bad);
             merge_and_write<D>(sm, p.group, 0, bad, BF16 ? 1.0f : p.v_scale[g],
                                piece_dst<D>(p, r, ps, rq, b, g, w));
@@ -997,6 +1015,22 @@ __global__ __launch_bounds__(kThreads) void decode_attn_bal_vec_kernel(AttnParam
     }
 }
 
+template <bool BF16, int D, bool APPEND, bool DUP>
+void launch_mfma_t(const AttnParams &p, dim3 grid, dim3 block, bool bal, hipStream_t stream)
+{
+    if (p.log2_page >= Geo<BF16, D>::LOG2_TT) {
+        if (bal)
+            hipLaunchKernelGGL((decode_attn_bal_mfma_kernel<BF16, D, true, APPEND, DUP>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, true, APPEND, DUP>), grid, block, 0, stream, p);
+    } else {
+        if (bal)
+            hipLaunchKernelGGL((decode_attn_bal_mfma_kernel<BF16, D, false, APPEND, DUP>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, false, APPEND, DUP>), grid, block, 0, stream, p);
+    }
+}
+
 template <bool BF16, int D, bool APPEND>
 hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
 {
@@ -1011,16 +1045,10 @@ hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
             hipLaunchKernelGGL((decode_attn_bal_vec_kernel<BF16, D, APPEND>), grid, block, 0, stream, p);
         else
             hipLaunchKernelGGL((decode_attn_vec_kernel<BF16, D, APPEND>), grid, block, 0, stream, p);
-    } else if (p.log2_page >= Geo<BF16, D>::LOG2_TT) {
-        if (bal)
-            hipLaunchKernelGGL((decode_attn_bal_mfma_kernel<BF16, D, true, APPEND>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, true, APPEND>), grid, block, 0, stream, p);
+    } else if (p.group <= 8) {
+        launch_mfma_t<BF16, D, APPEND, true>(p, grid, block, bal, stream);
     } else {
-        if (bal)
-            hipLaunchKernelGGL((decode_attn_bal_mfma_kernel<BF16, D, false, APPEND>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((decode_attn_mfma_kernel<BF16, D, false, APPEND>), grid, block, 0, stream, p);
+        launch_mfma_t<BF16, D, APPEND, false>(p, grid, block, bal, stream);
     }
     return hipGetLastError();
 }

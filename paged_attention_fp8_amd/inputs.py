@@ -196,6 +196,13 @@ class Workload:
     outlier_mult: float = 20.0
     num_splits: int = 0           # 0 = library's choice
     stale_requests: int = 0
+    # peaked-softmax and dynamic-range recipes (device inputs only):
+    q_mult: float = 1.0           # q ~ N(0, 1) * q_mult before bf16 rounding
+    k_log2: int = 0               # K data times 2^k_log2 (exact on bf16 values)
+    v_log2: int = 0               # V data times 2^v_log2
+    v_bias: float = 0.0           # added to the even head dims of V before rounding
+    needle_gap: float = 0.0       # > 0: needle tokens (below) score this many nats
+                                  # above a near-flat background
 
     @property
     def group(self) -> int:
@@ -363,6 +370,55 @@ def _device_normal_bf16(g, shape, device, outlier_frac, outlier_mult):
     return bulk, amax
 
 
+NEEDLE_EVERY, NEEDLE_SPAN = 32, 256   # needle tokens: every 32nd token of the first 256
+
+
+def _needle_shape(w: Workload, q, k, v, L: int):
+    """The needle recipe for one request (in place, fp32 [L][Hkv][D] K/V and
+    fp32 [Hq][D] q): the query heads of a KV head share one query vector;
+    background keys are small (N(0, 2^-12)), so their scores are nearly
+    equal; tokens 0, 32, .., 224 are needles whose key is the group's query
+    direction scaled so that its score is needle_gap nats above the
+    background's, with V near zero (N(0, 2^-12)).  Every wave tile of the
+    first 256 tokens then holds a needle, and each later token weighs about
+    exp(-needle_gap) of a needle."""
+    import torch
+    G, D = w.group, w.head_dim
+    qg = q.view(w.kv_heads, G, D)[:, :1, :].expand(-1, G, -1).clone()
+    q.copy_(qg.reshape(w.q_heads, D))
+    k.mul_(2.0 ** -6)
+    sm = 1.0 / math.sqrt(D)
+    qv = q.view(w.kv_heads, G, D)[:, 0, :]                        # [Hkv][D]
+    needle_k = qv * (w.needle_gap / sm) / (qv * qv).sum(-1, keepdim=True)
+    idx = torch.arange(0, min(L, NEEDLE_SPAN), NEEDLE_EVERY, device=k.device)
+    k[idx] = needle_k.to(k.dtype)
+    v[idx] = v[idx] * 2.0 ** -6
+
+
+def _device_kv(w: Workload, g, L: int, device, q=None):
+    """One request's K and V ([L][Hkv][D] bf16) by the workload's recipe, and
+    the per-head amax of the data the scales come from (the bulk before
+    outliers)."""
+    import torch
+    shaped = w.v_bias != 0.0 or w.needle_gap > 0.0 or w.k_log2 != 0 or w.v_log2 != 0
+    kb, ka = _device_normal_bf16(g, (L, w.kv_heads, w.head_dim), device, w.outlier_frac, w.outlier_mult)
+    vb, va = _device_normal_bf16(g, (L, w.kv_heads, w.head_dim), device, w.outlier_frac, w.outlier_mult)
+    if not shaped:
+        return kb, ka, vb, va
+    if w.outlier_frac > 0.0:
+        raise ValueError("outliers and the peaked recipes are not combined")
+    k, v = kb.float(), vb.float()
+    if w.v_bias != 0.0:
+        v[..., 0::2] += w.v_bias
+    if w.needle_gap > 0.0:
+        _needle_shape(w, q, k, v, L)
+    kb = (k.to(torch.bfloat16) * 2.0 ** w.k_log2)   # power-of-two scaling: exact
+    vb = (v.to(torch.bfloat16) * 2.0 ** w.v_log2)
+    ka = kb.abs().float().amax(dim=(0, 2))
+    va = vb.abs().float().amax(dim=(0, 2))
+    return kb, ka, vb, va
+
+
 def make_device_decode_inputs(w: Workload, seed: int, device="cuda",
                               lengths: Optional[Sequence[int]] = None,
                               pool_order: str = "shuffled") -> DeviceDecodeInputs:
@@ -377,7 +433,12 @@ def make_device_decode_inputs(w: Workload, seed: int, device="cuda",
     pool = PagePool(num_pages, seed=seed, order=pool_order)
     batch = allocate_batch(pool, lens, P)
     T = int(lens.max()) if B else 1
-    q, _ = _device_normal_bf16(_torch_gen(device, seed, 2), (B, Hq, D), device, 0.0, 1.0)
+    qg = _torch_gen(device, seed, 2)
+    if w.q_mult == 1.0 and w.needle_gap == 0.0:
+        q, _ = _device_normal_bf16(qg, (B, Hq, D), device, 0.0, 1.0)
+        qf = None
+    else:
+        qf = torch.randn((B, Hq, D), generator=qg, device=device, dtype=torch.float32) * w.q_mult
     k = torch.zeros((B, T, Hkv, D), dtype=torch.bfloat16, device=device)
     v = torch.zeros_like(k)
     k_amax = torch.zeros(Hkv, dtype=torch.float32, device=device)
@@ -385,12 +446,13 @@ def make_device_decode_inputs(w: Workload, seed: int, device="cuda",
     for b in range(B):
         L = int(lens[b])
         g = _torch_gen(device, seed, 1, b)
-        kb, ka = _device_normal_bf16(g, (L, Hkv, D), device, w.outlier_frac, w.outlier_mult)
-        vb, va = _device_normal_bf16(g, (L, Hkv, D), device, w.outlier_frac, w.outlier_mult)
+        kb, ka, vb, va = _device_kv(w, g, L, device, None if qf is None else qf[b])
         k[b, :L] = kb
         v[b, :L] = vb
         k_amax = torch.maximum(k_amax, ka)
         v_amax = torch.maximum(v_amax, va)
+    if qf is not None:
+        q = qf.to(torch.bfloat16)
     stale = []
     if w.stale_requests:
         pick = rng(seed, 5).choice(B, size=min(w.stale_requests, B), replace=False)
