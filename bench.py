@@ -1,34 +1,35 @@
 """Benchmark of the decode hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-extras] [--sweep] [--copy-calibration]
-                    [--traffic-from DIR]
+                    [--no-extras] [--only NAME[,NAME]] [--copy-calibration]
+                    [--summarize-counters ...]
 
 One step = one pass of the path over one batch: the batched page-tag check,
 the quantise-on-append of this step's token for every request, and e4m3 paged
-decode attention (with its split-K combine when the library splits).  The
-workload is the concurrency point the target is quoted on: 64 requests of
-16,384 tokens, 64 query heads on 8 KV heads, head_dim 128, 64-token pages, in
-a 2 GiB pool that holds exactly 64 e4m3 requests (or 32 bf16 ones).  Inputs
-are seeded synthetic data drawn on the GPU and resident in HBM before timing.
+decode attention (with its split-K combine when the library splits).  The workload is the concurrency point the target is quoted
+on: 64 requests of 16,384 tokens, 64 query heads on 8 KV heads, head_dim 128,
+64-token pages, in a 2 GiB pool that holds exactly 64 e4m3 requests (or 32
+bf16 ones).  Inputs are seeded synthetic data drawn on the GPU and resident in
+HBM before timing.
 
 Prints one JSON line.  value = attention tokens/s (one decode token per
 request through one attention layer per step).  roofline.achieved is the
 algorithmic bytes of one attention launch divided by its mean duration,
-measured with HIP events on the launch stream over the timed steps.  The
-bf16 twin (32 requests: the same KV bytes), the tag-check overhead against
-the no-op tracker, the step with the append inside the attention launch (at
-64 requests and at one) are reported beside it, and so is the long-context point
-(4 requests of 262,144 tokens in 64 splits: check overhead, and the batch
-with one stale request) and the prefill-to-decode hand-off (kv_quant_fill of
-8 prompts of 8,192 tokens) and a continuous decode loop with admission
-under the same 2 GiB budget (e4m3 vs bf16), INT4 weight streaming
-(int4_gemv over 940 MB of int4 weights at 1-64 rows), and the ragged batch
-(32 requests of 1k-32k tokens) on e4m3 and bf16 caches from one bf16 source,
-with default splits and the balanced partition.  --sweep adds the 1/8/16/32/64 concurrency points,
-each step preceded by a 1 GiB read of other memory so that no point runs
-out of the MALL.  cpu_baseline times the CPU oracle on a bounded sample
-of the same batch.
+measured with HIP events on the launch stream over the timed steps.  Beside
+it: the tag-check overhead against the no-op tracker (separate pass, and
+inside the append launch), the append inside the attention launch (64
+requests and one), the bf16 twin (32 requests: the same KV bytes), and the
+extras -- the concurrency sweep of the pages' decode table (1/8/16/32/64
+requests, e4m3 and bf16, each step after a 1 GiB read of other memory so
+that no point runs out of the MALL), the 4k-token / 16-token-page workload,
+the long-context point (4 requests of 262,144 tokens in 64 splits: check
+overhead, and the batch with one stale request), the prefill-to-decode
+hand-off (kv_quant_fill of 8 prompts of 8,192 tokens), a continuous decode
+loop with admission under the same 2 GiB budget (e4m3 vs bf16), INT4 weight
+streaming (int4_gemv over 940 MB of int4 weights at 1-64 rows), and the
+ragged batch (32 requests of 1k-32k tokens) on e4m3 and bf16 caches from one
+bf16 source.  --only runs named extras alone (for profiling one workload).
+cpu_baseline times the CPU oracle on a bounded sample of the same batch.
 """
 from __future__ import annotations
 
@@ -71,8 +72,9 @@ def parse_args():
                     help="target wall time of the oracle sample")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the bf16 twin, the check overhead and the long-context point")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also run the 1/8/16/32/64 concurrency sweep (both dtypes)")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated extras to run alone, without the headline point "
+                         "(for profiling one workload): " + ", ".join(EXTRAS))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", default=COUNTERS_SUMMARY,
@@ -477,6 +479,70 @@ def fp8_vs_bf16(args, dev):
     return res
 
 
+def _attn_point(pt, rr):
+    """Figures of one timed point: attention launch (HIP events, flushed
+    caches), the step around it, and the share of peak HBM bandwidth."""
+    ms = statistics.mean(rr["attn_ms"])
+    B = pt.step.batch.batch
+    return {"attn_us": 1e3 * ms, "attn_us_median": 1e3 * statistics.median(rr["attn_ms"]),
+            "attn_GBps": pt.bytes / (ms * 1e-3) / 1e9,
+            "attn_frac": pt.bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "ms_per_step": rr["ms_per_step"], "tokens_per_s": B / (rr["ms_per_step"] * 1e-3),
+            "splits": rr["splits"], "algorithmic_bytes": pt.bytes}
+
+
+def concurrency_sweep(args, dev, head=None):
+    """The concurrency table of the pages' KV-cache section: 1, 8, 16, 32 and
+    64 requests of 16,384 tokens (GQA 64/8, head_dim 128, 64-token pages) in
+    the 2 GiB pool, e4m3 and bf16, library-default splits.  bf16 at 64
+    requests does not fit the pool: the allocator refuses it.  Every step is
+    preceded by a 1 GiB read of other memory, so that no point runs from the
+    256 MB MALL; step = check + append + attention."""
+    import torch
+    from paged_attention_fp8_amd import inputs as I
+    from paged_attention_fp8_amd import ops
+    points = []
+    for kv_dtype, name in ((ops.KV_FP8_E4M3, "e4m3"), (ops.KV_BF16, "bf16")):
+        for b in (1, 8, 16, 32, 64):
+            entry = {"dtype": name, "batch": b}
+            if head is not None and kv_dtype == head.kv_dtype and b == head.step.batch.batch:
+                pt = head
+            else:
+                try:
+                    pt = Point(b, kv_dtype, dev)
+                except I.PoolExhausted as e:
+                    entry["result"] = f"out of pool memory ({e})"
+                    points.append(entry)
+                    continue
+            entry.update(_attn_point(pt, pt.run(args.steps, args.warmup, 0, flush=True)))
+            points.append(entry)
+            log(f"sweep {name} B={b}: {entry['attn_us']:.1f} us, {100 * entry['attn_frac']:.1f}%")
+            if pt is not head:
+                del pt
+                torch.cuda.empty_cache()
+    return {"workload": "gqa8_16k_b{1,8,16,32,64}: B requests x 16384 tokens, 64 query / 8 KV heads, "
+                        "head_dim 128, 64-token pages, 2 GiB pool, flushed caches", "points": points}
+
+
+def gqa4_4k(args, dev):
+    """8 requests of 4,096 tokens, GQA 32/8, head_dim 128, 16-token pages,
+    1% of K/V elements x20 (saturating the e4m3 range): the small-page,
+    latency-bound workload; library-default splits, flushed caches."""
+    import torch
+    from paged_attention_fp8_amd import inputs as I
+    from paged_attention_fp8_amd import ops
+    w = I.WORKLOADS["gqa4_4k_outliers"]
+    res = {"workload": "gqa4_4k_outliers: 8 requests x 4096 tokens, 32 query / 8 KV heads, head_dim 128, "
+                       "16-token pages, 1% outliers x20, flushed caches"}
+    for kv_dtype, name in ((ops.KV_FP8_E4M3, "e4m3"), (ops.KV_BF16, "bf16")):
+        pt = Point(w.batch, kv_dtype, dev, workload=w)
+        res[name] = _attn_point(pt, pt.run(args.steps, args.warmup, 0, flush=True))
+        log(f"gqa4_4k {name}: {res[name]['attn_us']:.1f} us, {100 * res[name]['attn_frac']:.1f}%")
+        del pt
+        torch.cuda.empty_cache()
+    return res
+
+
 def _pmc_values(directory, counter, kernel_substr):
     """Per-dispatch values of one counter for kernels whose name contains
     kernel_substr, from a rocprofv3 --pmc csv run directory."""
@@ -567,6 +633,18 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
 
 
+# the extras of the default run (and of --only), in run order
+EXTRAS = {
+    "concurrency_sweep": concurrency_sweep,
+    "gqa4_4k": gqa4_4k,
+    "long_context": long_context,
+    "prefill_handoff": handoff,
+    "decode_loop": decode_loop,
+    "int4_decode_gemv": int4_decode,
+    "fp8_vs_bf16": fp8_vs_bf16,
+}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -584,6 +662,13 @@ def main():
         return
     from paged_attention_fp8_amd import ops
     dev = torch.device("cuda:0")
+    if args.only:
+        names = [n.strip() for n in args.only.split(",") if n.strip()]
+        unknown = [n for n in names if n not in EXTRAS]
+        if unknown:
+            raise SystemExit(f"--only: unknown extras {unknown} (known: {', '.join(EXTRAS)})")
+        print(json.dumps({n: EXTRAS[n](args, dev) for n in names}), flush=True)
+        return
 
     p = Point(args.batch, ops.KV_FP8_E4M3, dev)
     r = p.run(args.steps, args.warmup, args.splits)
@@ -653,15 +738,17 @@ def main():
         one = Point(1, ops.KV_FP8_E4M3, dev)
         r1s = one.run(args.steps, args.warmup, 0)
         r1f = one.run(args.steps, args.warmup, 0, append_in_attention=True)
+        r1c = one.run(args.steps, args.warmup, 0, fused=True)
         result["append_in_attention"] = {
             "step": "tag check + attention with the append in its launch, against tag check + "
-                    "append + attention",
+                    "append + attention (and, at one request, the check inside the append launch)",
             "b64": {"ms_per_step": ra["ms_per_step"], "separate_ms_per_step": r["ms_per_step"],
                     "tokens_per_s": B / (ra["ms_per_step"] * 1e-3)},
             "b1": {"ms_per_step": r1f["ms_per_step"], "separate_ms_per_step": r1s["ms_per_step"],
+                   "checked_append_ms_per_step": r1c["ms_per_step"],
                    "tokens_per_s": 1 / (r1f["ms_per_step"] * 1e-3), "splits": r1f["splits"]},
         }
-        del ra, one, r1s, r1f
+        del ra, one, r1s, r1f, r1c
         q = Point(32, ops.KV_BF16, dev)
         rb = q.run(args.steps, args.warmup, args.splits)
         bms = statistics.mean(rb["attn_ms"])
@@ -676,29 +763,10 @@ def main():
         }
         del q
         torch.cuda.empty_cache()
-        result["long_context"] = long_context(args, dev)
-        result["prefill_handoff"] = handoff(args, dev)
-        result["decode_loop"] = decode_loop(args, dev)
-        result["int4_decode_gemv"] = int4_decode(args, dev)
-        result["fp8_vs_bf16"] = fp8_vs_bf16(args, dev)
-    if args.sweep:
-        sweep = []
-        for kv_dtype, name in ((ops.KV_FP8_E4M3, "fp8"), (ops.KV_BF16, "bf16")):
-            for b in (1, 8, 16, 32, 64):
-                if kv_dtype == ops.KV_BF16 and b > 32:
-                    sweep.append({"dtype": name, "batch": b, "result": "out of pool memory"})
-                    continue
-                pt = Point(b, kv_dtype, dev)
-                rr = pt.run(args.steps, args.warmup, 0, flush=True)
-                ms = statistics.mean(rr["attn_ms"])
-                sweep.append({"dtype": name, "batch": b, "tokens_per_s": b / (rr["ms_per_step"] * 1e-3),
-                              "ms_per_step": rr["ms_per_step"], "attn_us": 1e3 * ms,
-                              "attn_GBps": pt.bytes / (ms * 1e-3) / 1e9,
-                              "attn_frac": pt.bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                              "splits": rr["splits"]})
-                del pt
-                torch.cuda.empty_cache()
-        result["sweep"] = sweep
+        result["concurrency_sweep"] = concurrency_sweep(args, dev, head=p)
+        for name, fn in EXTRAS.items():
+            if name != "concurrency_sweep":
+                result[name] = fn(args, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(result), flush=True)
