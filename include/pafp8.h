@@ -40,7 +40,9 @@
  *    memory outside the pool for them (see each call).
  *  - No float atomics: the same inputs and split count give bitwise
  *    identical outputs.  The library has no global mutable state apart from a
- *    thread-local error message and a per-device cache of the CU count.
+ *    thread-local error message, a per-device cache of the CU count, and the
+ *    device scratch of paged_decode_attn_fp8_noalloc (with a per-device cache
+ *    of its address).
  *
  * Pool layout (the "shared physical page pool"):
  *   K pool and V pool: [num_pages][num_kv_heads][block], one block of
@@ -350,6 +352,28 @@ pafp8_status paged_decode_attn_bf16_append(const pafp8_cache *cache, const pafp8
                                            int32_t num_splits, void *workspace, size_t workspace_bytes,
                                            const uint16_t *k_new, const uint16_t *v_new, float *out,
                                            float *lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * paged_decode_attn_fp8_noalloc -- paged_decode_attn_fp8 for callers that
+ * cannot allocate memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The same kernels
+ * and results, bitwise, as paged_decode_attn_fp8 with the same num_splits
+ * (0: the default); the split-K or balanced partials go to a device array
+ * the library holds per GPU (pafp8_noalloc_scratch_bytes() = 16 MiB) instead
+ * of a workspace.  Calls whose partials would exceed it (from
+ * pafp8_decode_workspace_bytes) return PAFP8_EUNSUPPORTED and launch
+ * nothing.  The call allocates nothing: the array's device address is looked
+ * up once per device (hipGetSymbolAddress) on the first call that needs it.
+ * Every call on one GPU shares that array and nothing in it is read before
+ * the call writes it, so calls in stream order are independent; calls that
+ * overlap on one GPU (other streams, other threads) race on it and must not
+ * be issued.
+ * ------------------------------------------------------------------------- */
+pafp8_status paged_decode_attn_fp8_noalloc(const pafp8_cache *cache, const pafp8_batch *batch,
+                                           const uint16_t *q, int32_t num_q_heads, float sm_scale,
+                                           int32_t num_splits, float *out, float *lse,
+                                           hipStream_t stream);
+size_t pafp8_noalloc_scratch_bytes(void);
 
 /* ---------------------------------------------------------------------------
  * splitk_combine -- merge per-split softmax partials (flash-decoding; not on

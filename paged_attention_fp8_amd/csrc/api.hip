@@ -159,6 +159,41 @@ int device_cu_count()
     return g_cu[dev];
 }
 
+// Scratch of paged_decode_attn_fp8_noalloc: the split-K / balanced partials
+// of a call live here instead of in a caller's workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  Host code must
+// not pass the array's name to a kernel (on the host it is a stand-in, not a
+// device address): the device address comes from hipGetSymbolAddress, once
+// per device, and only that address is used.
+constexpr size_t kScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch;
+
+// the current device's address of `scratch` (looked up on first use)
+pafp8_status scratch_address(void **addr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_status(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (dev >= static_cast<int>(g_scratch.size()))
+        g_scratch.resize(dev + 1, nullptr);
+    if (g_scratch[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (ptr == nullptr)
+            return fail(PAFP8_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch[dev] = ptr;
+    }
+    *addr = g_scratch[dev];
+    return PAFP8_OK;
+}
+
 pafp8_status attn_impl(const pafp8_cache *cache, const pafp8_batch *batch, const uint16_t *q,
                        int32_t Hq, float sm_scale, int32_t S, void *ws, size_t ws_bytes,
                        float *out, float *lse, hipStream_t stream, int want_dtype,
@@ -440,6 +475,39 @@ pafp8_status paged_decode_attn_bf16(const pafp8_cache *cache, const pafp8_batch 
 {
     return attn_impl(cache, batch, q, num_q_heads, sm_scale, num_splits, workspace,
                      workspace_bytes, out, lse, stream, PAFP8_KV_BF16);
+}
+
+size_t pafp8_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+pafp8_status paged_decode_attn_fp8_noalloc(const pafp8_cache *cache, const pafp8_batch *batch,
+                                           const uint16_t *q, int32_t num_q_heads, float sm_scale,
+                                           int32_t num_splits, float *out, float *lse,
+                                           hipStream_t stream)
+{
+    pafp8_status st = check_attn(cache, batch, q, num_q_heads, sm_scale, num_splits, nullptr, 0,
+                                 out, PAFP8_KV_FP8_E4M3);
+    if (st != PAFP8_OK)
+        return st;
+    if (batch->batch == 0)
+        return ok();
+    // the split count attn_impl will use, and the partials it needs
+    int32_t S = num_splits;
+    if (S == 0)
+        S = pafp8_default_num_splits(batch->batch, cache->num_kv_heads, batch->max_pages_per_req,
+                                     cache->page_size, 0);
+    if (S > batch->max_pages_per_req)
+        S = batch->max_pages_per_req;
+    const size_t need = pafp8_decode_workspace_bytes(batch->batch, num_q_heads, cache->head_dim, S);
+    if (need > kScratchBytes)
+        return fail(PAFP8_EUNSUPPORTED,
+                    "num_splits = %d needs %zu bytes of partials, more than the %zu-byte scratch of "
+                    "paged_decode_attn_fp8_noalloc (use paged_decode_attn_fp8 with a workspace)",
+                    S, need, kScratchBytes);
+    void *ws = nullptr;
+    if (need > 0 && (st = scratch_address(&ws)) != PAFP8_OK)
+        return st;
+    return attn_impl(cache, batch, q, num_q_heads, sm_scale, S, ws, need > 0 ? kScratchBytes : 0,
+                     out, lse, stream, PAFP8_KV_FP8_E4M3);
 }
 
 pafp8_status paged_decode_attn_fp8_append(const pafp8_cache *cache, const pafp8_batch *batch,

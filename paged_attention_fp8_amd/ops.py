@@ -63,6 +63,8 @@ _SIGNATURES = {
     "paged_decode_attn_bf16": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V]),
     "paged_decode_attn_fp8_append": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V, _V, _V]),
     "paged_decode_attn_bf16_append": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _SZ, _V, _V, _V, _V, _V]),
+    "paged_decode_attn_fp8_noalloc": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _V, _V]),
+    "pafp8_noalloc_scratch_bytes": (_SZ, []),
     "splitk_combine": (_I32, [_V, _V, _I32, _I32, _I32, _I32, _V, _V, _V, _V]),
     "pafp8_e4m3_encode": (_I32, [_V, _V, _I64, _V]),
     "pafp8_e4m3_decode": (_I32, [_V, _V, _V, _V, _I64, _V]),
@@ -402,6 +404,40 @@ def paged_decode_attn(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor, 
               ws_ptr, ws_bytes, out.data_ptr(), _ptr(lse), _stream(dev)),
            "paged_decode_attn")
     return out, lse
+
+
+def paged_decode_attn_noalloc(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor,
+                              sm_scale: float, num_splits: int = 0,
+                              out: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None):
+    """paged_decode_attn_fp8_noalloc: e4m3 attention with the split partials
+    in the library's own device scratch (no workspace).  num_splits as for
+    paged_decode_attn (BALANCED allowed); out and lse, when given, are
+    written in place.  Returns (out, lse)."""
+    dev = cache.device
+    if cache.kv_dtype != KV_FP8_E4M3:
+        raise ValueError("paged_decode_attn_noalloc needs an e4m3 pool")
+    cs, bs = cache._struct(), batch._struct(dev)
+    if q.dim() != 3:
+        raise ValueError("q must be [B][Hq][D]")
+    B, Hq, D = (int(x) for x in q.shape)
+    _need(q, "q", torch.bfloat16, (batch.batch, Hq, cache.head_dim), dev)
+    if num_splits == BALANCED:
+        num_splits = -default_balanced_groups(cache.num_kv_heads)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, Hq, D), dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq), dev)
+    _check(lib().paged_decode_attn_fp8_noalloc(ctypes.byref(cs), ctypes.byref(bs), q.data_ptr(), Hq,
+                                               float(sm_scale), int(num_splits), out.data_ptr(),
+                                               _ptr(lse), _stream(dev)),
+           "paged_decode_attn_fp8_noalloc")
+    return out, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().pafp8_noalloc_scratch_bytes())
 
 
 def splitk_combine(part_o: torch.Tensor, part_lse: torch.Tensor,

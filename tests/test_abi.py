@@ -203,3 +203,23 @@ def test_fused_append_entries_validate_without_gpu(L):
     assert call("paged_decode_attn_bf16_append", _cache()) == 1        # e4m3 pool
     assert "does not match" in L.pafp8_last_error().decode()
     assert call("paged_decode_attn_fp8_append", _cache(), k_new=None, batch=_batch(batch=0)) == 0
+
+
+def _noalloc(L, cache, batch, hq=64, splits=1):
+    return L.paged_decode_attn_fp8_noalloc(ctypes.byref(cache), ctypes.byref(batch), 4096, hq, 0.1,
+                                           splits, 8192, None, None)
+
+
+def test_noalloc_entry_validates_without_gpu(L):
+    """The no-allocation entry point checks its arguments like the workspace
+    call, and refuses, before any HIP call, a split count whose partials
+    exceed its fixed scratch."""
+    assert L.pafp8_noalloc_scratch_bytes() == 16 << 20
+    assert _noalloc(L, _cache(kv_dtype=1), _batch()) == 1
+    assert b"does not match" in L.pafp8_last_error()
+    assert _noalloc(L, _cache(), _batch(), hq=60) == 1
+    big = _batch(batch=64)                                  # 64 x 64 heads x 16 splits x 129 floats
+    assert L.pafp8_decode_workspace_bytes(64, 64, 128, 16) > 16 << 20
+    assert _noalloc(L, _cache(), big, splits=16) == 2
+    assert b"scratch" in L.pafp8_last_error()
+    assert _noalloc(L, _cache(), _batch(batch=0), splits=16) == 0   # nothing to do
