@@ -245,6 +245,27 @@ pafp8_status attn_impl(const pafp8_cache *cache, const pafp8_batch *batch, const
     p.pages_per_split = balanced ? batch->max_pages_per_req : (batch->max_pages_per_req + S - 1) / S;
     p.bal_groups = balanced ? -S : 0;
     p.sm_scale = sm_scale;
+    // Many uniform splits (at least one per wave slot of the GPU: 64
+    // partitions of four 256k-token requests, say) run in wave mode: every
+    // wave takes one or two whole splits of one (request, KV head) and
+    // writes their partial rows itself, so split boundaries cost no barrier.  It needs splits
+    // of whole tiles (64 e4m3 or 32 bf16 tokens) on the MFMA path with pages
+    // of at least a tile; the append taken into the launch keeps the
+    // work-group mode.
+    p.wave_parts = 0;
+    p.part_tiles = 0;
+    if (!balanced && S > 1 && p.group >= 2 && !append) {
+        const int64_t tile = cache->kv_dtype == PAFP8_KV_BF16 ? 32 : 64;
+        const int64_t split_tokens = static_cast<int64_t>(p.pages_per_split) * cache->page_size;
+        const int64_t units = static_cast<int64_t>(batch->batch) * cache->num_kv_heads * S;
+        const int64_t slots = 4 * static_cast<int64_t>(device_cu_count());  // one work-group per CU
+        if (cache->page_size >= tile && split_tokens % tile == 0 && units >= slots) {
+            // a wave takes at most two splits: the rows of the first wait in
+            // registers until the second is done
+            p.wave_parts = units >= 2 * slots ? 2 : 1;
+            p.part_tiles = static_cast<int32_t>(split_tokens / tile);
+        }
+    }
     if (balanced) {
         const size_t R = static_cast<size_t>(batch->batch) + static_cast<size_t>(-S) - 1;  // B + W - 1
         const size_t o_bytes = align16_up(static_cast<size_t>(Hq) * R * cache->head_dim * sizeof(float));

@@ -33,6 +33,8 @@ struct AttnParams {
     int32_t group;            // num_q_heads / num_kv_heads
     int32_t num_splits;       // S (1 in a balanced launch)
     int32_t pages_per_split;  // ceil(max_pages / S)
+    int32_t wave_parts;       // > 0: wave-per-split mode, each wave takes this many splits
+    int32_t part_tiles;       // wave mode: tiles in one split
     int32_t bal_groups;       // W work-groups per KV head in a balanced launch, else 0
     float sm_scale;
 };

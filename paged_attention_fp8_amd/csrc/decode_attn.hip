@@ -59,7 +59,8 @@ struct SplitRange {
     int state;       // 0 = compute, 1 = aborted (0 / -inf), 2 = invalid (NaN)
 };
 
-__device__ __forceinline__ SplitRange split_range(const AttnParams &p, int b, int s)
+// Tokens of splits s .. s + nparts - 1 of request b (clipped to its length).
+__device__ __forceinline__ SplitRange split_range(const AttnParams &p, int b, int s, int nparts = 1)
 {
     SplitRange r{0, 0, 0, 0};
     if (p.req_status != nullptr && p.req_status[b] != 0) {
@@ -74,7 +75,7 @@ __device__ __forceinline__ SplitRange split_range(const AttnParams &p, int b, in
     }
     const int64_t n_pages = (L + (int64_t{1} << p.log2_page) - 1) >> p.log2_page;
     const int64_t p0 = static_cast<int64_t>(s) * p.pages_per_split;
-    int64_t p1 = p0 + p.pages_per_split;
+    int64_t p1 = p0 + static_cast<int64_t>(nparts) * p.pages_per_split;
     if (p1 > n_pages)
         p1 = n_pages;
     if (p0 >= p1)
@@ -638,23 +639,145 @@ __device__ __forceinline__ MergeDst piece_dst(const AttnParams &p, const BalRang
     return MergeDst{p.part_o + row0 * D, p.part_lse + row0, R};
 }
 
-// Request b, KV head g over tokens [rng.t0, rng.t1): each wave's softmax
-// state ends up in sm.  Returns non-zero if a page id lay outside the pool.
-template <bool BF16, int D, bool BIG, bool DUP>
-__device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm, int b, int g,
-                                          const SplitRange &rng)
+// A wave's softmax state into sm (row r of the wave's slot holds head r).
+template <bool BF16, int D, bool DUP>
+__device__ __forceinline__ void mfma_state_to_smem(MfmaState<BF16, D> &st, MergeSmem<D> &sm)
+{
+    using G_ = Geo<BF16, D>;
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    if constexpr (DUP) {
+        // column h + 8 accumulated V times the low part of head h's weights
+#pragma unroll
+        for (int dt = 0; dt < G_::NDT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                st.o[dt][e] += shfl_xor_f(st.o[dt][e], 8);
+    }
+    // the four lanes of a head each hold a quarter of its denominator
+    float l = st.l + shfl_xor_f(st.l, 16);
+    l += shfl_xor_f(l, 32);
+    const int r = lane & 15, lg = lane >> 4;
+    if (lg == 0) {
+        sm.m[wave][r] = st.m;
+        sm.l[wave][r] = l;
+    }
+#pragma unroll
+    for (int dt = 0; dt < G_::NDT; ++dt)
+        *reinterpret_cast<f32x4 *>(&sm.o[wave][r][dt * 16 + lg * 4]) = st.o[dt];
+}
+
+template <bool BF16, int D>
+__device__ __forceinline__ void mfma_state_reset(MfmaState<BF16, D> &st)
+{
+#pragma unroll
+    for (int dt = 0; dt < Geo<BF16, D>::NDT; ++dt)
+        st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m = kNegInf;
+    st.l = 0.f;
+}
+
+// One wave's softmax state, normalised: lane (r, lg) holds out =
+// o * v_scale / l of head r, dims dt*16 + 4*lg .. + 3, and every lane its
+// head's lse = ln(sum exp) (the wave-per-split mode, where no other wave
+// shares the split).  state / bad as in merge_and_write.
+template <bool BF16, int D>
+struct WaveRows {
+    f32x4 o[Geo<BF16, D>::NDT];
+    float lse;
+};
+
+template <bool BF16, int D, bool DUP>
+__device__ __forceinline__ WaveRows<BF16, D> mfma_state_rows(MfmaState<BF16, D> &st, int state, int bad,
+                                                             float v_scale)
+{
+    using G_ = Geo<BF16, D>;
+    if constexpr (DUP) {
+#pragma unroll
+        for (int dt = 0; dt < G_::NDT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                st.o[dt][e] += shfl_xor_f(st.o[dt][e], 8);
+    }
+    float l = st.l + shfl_xor_f(st.l, 16);
+    l += shfl_xor_f(l, 32);
+    float scale = 0.f;
+    WaveRows<BF16, D> w;
+    w.lse = kNegInf;
+    if (state == 0 && st.m != kNegInf) {
+        scale = v_scale / l;
+        w.lse = (st.m + __log2f(l)) * kLn2;
+    }
+    const bool nan_rows = state == 2 || bad;
+    if (nan_rows)
+        w.lse = __builtin_nanf("");
+#pragma unroll
+    for (int dt = 0; dt < G_::NDT; ++dt)
+        w.o[dt] = nan_rows ? f32x4{w.lse, w.lse, w.lse, w.lse} : st.o[dt] * scale;
+    return w;
+}
+
+template <bool BF16, int D>
+__device__ __forceinline__ void store_wave_rows(const WaveRows<BF16, D> &w, int nheads, MergeDst dst)
+{
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, lg = lane >> 4;
+    if (r < nheads) {
+        float *row = dst.o + static_cast<int64_t>(r) * dst.stride * D;
+#pragma unroll
+        for (int dt = 0; dt < Geo<BF16, D>::NDT; ++dt)
+            *reinterpret_cast<f32x4 *>(row + dt * 16 + lg * 4) = w.o[dt];
+        if (lg == 0 && dst.lse != nullptr)
+            dst.lse[static_cast<int64_t>(r) * dst.stride] = w.lse;
+    }
+}
+
+// Request b, KV head g over tokens [rng.t0, rng.t1); dst(j) is where split
+// j's rows go.
+//  * Work-group mode (WAVE false): one split; the four waves take the
+//    range's tiles in turn and merge their states through sm at the end.
+//  * Wave mode (WAVE true): the calling wave alone streams every tile of the
+//    range, which covers nparts <= 2 consecutive splits of part_tiles tiles
+//    each (the request's last split may be shorter); at the split boundary
+//    it normalises the first split's rows into registers and starts afresh,
+//    with the next split's first tile already in flight -- no barrier, no
+//    shared memory.  All rows are stored once the range is done: a store in
+//    mid-stream would hold up the wave's next loads until memory, busy with
+//    every wave's reads, has acknowledged it.
+// A page id outside the pool turns the rows written from then on into NaN.
+template <bool BF16, int D, bool BIG, bool DUP, bool WAVE, class DstFn>
+__device__ __forceinline__ void mfma_range(const AttnParams &p, MergeSmem<D> *sm, int b, int g,
+                                           const SplitRange &rng, int nparts, int part_tiles,
+                                           float v_scale, DstFn dst)
 {
     using G_ = Geo<BF16, D>;
     const int G = p.group;
     const int lane = threadIdx.x & 63;
-    const int wave = uniform(threadIdx.x >> 6);
+    const int wave = WAVE ? 0 : uniform(threadIdx.x >> 6);
+    constexpr int kStep = WAVE ? 1 : kWaves;  // tiles between a wave's consecutive tiles
     MfmaState<BF16, D> st;
-#pragma unroll
-    for (int dt = 0; dt < G_::NDT; ++dt)
-        st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.m = kNegInf;
-    st.l = 0.f;
+    mfma_state_reset(st);
     int bad = 0;
+    int pj = 0;  // next split to write
+    WaveRows<BF16, D> held;  // wave mode: the first of two splits' rows
+    auto flush = [&]() {
+        if constexpr (WAVE) {
+            const WaveRows<BF16, D> rows = mfma_state_rows<BF16, D, DUP>(st, rng.state, bad, v_scale);
+            if (pj + 1 < nparts) {
+                held = rows;
+            } else {
+                if (nparts == 2)
+                    store_wave_rows<BF16, D>(held, G, dst(0));
+                store_wave_rows<BF16, D>(rows, G, dst(pj));
+            }
+        } else {
+            mfma_state_to_smem<BF16, D, DUP>(st, *sm);
+            const int any_bad = __syncthreads_or(bad);
+            merge_and_write<D>(*sm, G, rng.state, any_bad, v_scale, dst(pj));
+        }
+        mfma_state_reset(st);
+        ++pj;
+    };
 
     const int64_t ntok = rng.t1 - rng.t0;
     const int ntiles = rng.state == 0 ? static_cast<int>((ntok + G_::TT - 1) / G_::TT) : 0;
@@ -682,8 +805,11 @@ __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm,
         }
         const float cs = (BF16 ? 1.0f : p.k_scale[g]) * p.sm_scale * kLog2e;
         const page_row_t row = page_row(p, b);
-        const int stride = kWaves * G_::TT;
+        const int stride = kStep * G_::TT;
         const bool lo_lane = c.lane_r >= 8;
+        // wave mode: tiles done, and the count at which the next split opens
+        int done = 0;
+        int next_cross = WAVE && nparts > 1 ? part_tiles : 0x7FFFFFFF;
 
         // Staggered pipeline, one tile buffer per wave: the next tile's K is
         // loaded as soon as Q.K^T has consumed this tile's K, and its V as
@@ -703,7 +829,7 @@ __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm,
             mfma_load_v<BF16, D, BIG>(t, c, T0, pg);
         }
         TilePages pgn = fetch_pages<BIG>(row, T0 + stride, G_::TPG, p.log2_page, rng.p_last);
-        while (i + kWaves < ntiles) {
+        while (i + kStep < ntiles) {
             const TilePages pn = pages_ok(pgn, p.num_pages, bad);
             mfma_qk(t, qop, sacc);
             // keep each load batch where it is: hoisting it above the
@@ -716,8 +842,14 @@ __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm,
             mfma_load_v<BF16, D, BIG>(t, c, T0 + stride, pn);
             __builtin_amdgcn_sched_barrier(0);
             pgn = fetch_pages<BIG>(row, T0 + 2 * stride, G_::TPG, p.log2_page, rng.p_last);
-            i += kWaves;
+            i += kStep;
             T0 += stride;
+            if constexpr (WAVE) {
+                if (++done == next_cross) {  // the next tile opens the next split
+                    flush();
+                    next_cross = pj < nparts - 1 ? next_cross + part_tiles : 0x7FFFFFFF;
+                }
+            }
         }
         mfma_qk(t, qop, sacc);
         if (T0 + G_::TT > rng.t1)
@@ -725,28 +857,8 @@ __device__ __forceinline__ int mfma_range(const AttnParams &p, MergeSmem<D> &sm,
         else
             mfma_softmax_pv<BF16, D, false, DUP>(t, sacc, st, cs, T0, rng.t1, c.lane_g, lo_lane);
     }
-    if constexpr (DUP) {
-        // column h + 8 accumulated V times the low part of head h's weights
-#pragma unroll
-        for (int dt = 0; dt < G_::NDT; ++dt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                st.o[dt][e] += shfl_xor_f(st.o[dt][e], 8);
-    }
-    // the four lanes of a head each hold a quarter of its denominator
-    float l = st.l + shfl_xor_f(st.l, 16);
-    l += shfl_xor_f(l, 32);
-    {
-        const int r = lane & 15, lg = lane >> 4;
-        if (lg == 0) {
-            sm.m[wave][r] = st.m;
-            sm.l[wave][r] = l;
-        }
-#pragma unroll
-        for (int dt = 0; dt < G_::NDT; ++dt)
-            *reinterpret_cast<f32x4 *>(&sm.o[wave][r][dt * 16 + lg * 4]) = st.o[dt];
-    }
-    return bad;
+    while (pj < nparts)  // the last split, and splits past the request's end
+        flush();
 }
 
 template <bool BF16, int D, bool BIG, bool APPEND, bool DUP>
@@ -766,10 +878,31 @@ __global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel
         if (rng.state == 0 && rng.t0 < rng.t1 && rng.t1 == L)
             append_new_token<BF16, D>(p, b, g, L);
     }
-    int bad = mfma_range<BF16, D, BIG, DUP>(p, sm, b, g, rng);
-    bad = __syncthreads_or(bad);
-    merge_and_write<D>(sm, p.group, rng.state, bad, BF16 ? 1.0f : p.v_scale[g],
-                       split_dst<D>(p, b, g, s));
+    mfma_range<BF16, D, BIG, DUP, false>(p, &sm, b, g, rng, 1, 0, BF16 ? 1.0f : p.v_scale[g],
+                                         [&](int) { return split_dst<D>(p, b, g, s); });
+}
+
+// Wave-per-split mode, for launches with at least a split per wave slot of
+// the GPU (many splits of long requests): every wave independently takes
+// wave_parts consecutive splits of one (request, KV head) -- chunk c of that
+// pair -- and writes their partial rows; the combine merges them as usual.
+// Splits of a whole number of tiles only.
+template <bool BF16, int D, bool BIG, bool DUP>
+__global__ __launch_bounds__(kThreads, 2) void decode_attn_mfma_wave_kernel(AttnParams p)
+{
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + uniform(threadIdx.x >> 6);
+    const int64_t nchunks = (p.num_splits + p.wave_parts - 1) / p.wave_parts;
+    if (gw >= static_cast<int64_t>(p.batch) * p.num_kv_heads * nchunks)
+        return;  // the grid's last work-group may hold idle waves
+    const int c = static_cast<int>(gw % nchunks);
+    const int g = static_cast<int>((gw / nchunks) % p.num_kv_heads);
+    const int b = static_cast<int>(gw / nchunks / p.num_kv_heads);
+    const int s0 = c * p.wave_parts;
+    const int nparts = p.num_splits - s0 < p.wave_parts ? p.num_splits - s0 : p.wave_parts;
+    const SplitRange rng = split_range(p, b, s0, nparts);
+    mfma_range<BF16, D, BIG, DUP, true>(p, static_cast<MergeSmem<D> *>(nullptr), b, g, rng, nparts,
+                                        p.part_tiles, BF16 ? 1.0f : p.v_scale[g],
+                                        [&](int j) { return split_dst<D>(p, b, g, s0 + j); });
 }
 
 // Balanced partition: the work-group takes pages [lo, hi) of its KV head's
@@ -792,10 +925,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_bal_mfma_kernel(AttnP
                 if (ps + rq.n <= r.hi)  // the piece ends at the request's last token
                     append_new_token<BF16, D>(p, b, g, rq.L);
             }
-            int bad = mfma_range<BF16, D, BIG, DUP>(p, sm, b, g, rng);
-            bad = __syncthreads_or(bad);
-            merge_and_write<D>(sm, p.group, 0, bad, BF16 ? 1.0f : p.v_scale[g],
-                               piece_dst<D>(p, r, ps, rq, b, g, w));
+            mfma_range<BF16, D, BIG, DUP, false>(p, &sm, b, g, rng, 1, 0, BF16 ? 1.0f : p.v_scale[g],
+                                                 [&](int) { return piece_dst<D>(p, r, ps, rq, b, g, w); });
             __syncthreads();  // sm is written again by the next piece
         }
         ps += rq.n;
@@ -1035,8 +1166,12 @@ template <bool BF16, int D, bool APPEND>
 hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
 {
     const bool bal = p.bal_groups > 0;
-    const int64_t blocks = bal ? static_cast<int64_t>(p.num_kv_heads) * p.bal_groups
-                               : static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_splits;
+    const bool wave_mode = p.wave_parts > 0;
+    int64_t blocks = bal ? static_cast<int64_t>(p.num_kv_heads) * p.bal_groups
+                         : static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_splits;
+    if (wave_mode)
+        blocks = (static_cast<int64_t>(p.batch) * p.num_kv_heads *
+                      ((p.num_splits + p.wave_parts - 1) / p.wave_parts) + kWaves - 1) / kWaves;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
@@ -1045,6 +1180,13 @@ hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
             hipLaunchKernelGGL((decode_attn_bal_vec_kernel<BF16, D, APPEND>), grid, block, 0, stream, p);
         else
             hipLaunchKernelGGL((decode_attn_vec_kernel<BF16, D, APPEND>), grid, block, 0, stream, p);
+    } else if (wave_mode && !APPEND && p.log2_page >= Geo<BF16, D>::LOG2_TT) {
+        if (p.group <= 8)
+            hipLaunchKernelGGL((decode_attn_mfma_wave_kernel<BF16, D, true, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_attn_mfma_wave_kernel<BF16, D, true, false>), grid, block, 0, stream, p);
+    } else if (wave_mode) {
+        return hipErrorInvalidValue;  // the host only picks wave mode for whole-page tiles, no append
     } else if (p.group <= 8) {
         launch_mfma_t<BF16, D, APPEND, true>(p, grid, block, bal, stream);
     } else {

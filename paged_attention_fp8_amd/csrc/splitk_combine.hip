@@ -108,17 +108,17 @@ __device__ __forceinline__ void fill_row(float *o, float *lse, float v, float ls
 // Wave-per-head combine for the attention's own head dims: one wave merges
 // the S partial rows po[S][D] (LSEs pl[S]) of one (request, query head) into
 // o (and *lse unless lse is nullptr); lane (g, c) handles float4 column c of
-// the rows k = g (mod 64 / (D/4)).  The first PF partial rows of every lane
-// are loaded together with the LSEs, so the whole reduction costs one memory
-// round trip when S * D <= 64 * 4 * PF.
-template <int D>
+// the rows k = g (mod 64 / (D/4)).  The first PF partial rows of every lane are
+// loaded together with the LSEs, so the whole reduction costs one memory
+// round trip when S * D <= 64 * 4 * PF (PF = 8 covers 16 splits of 128 dims,
+// PF = 32 covers 64).
+template <int D, int PF>
 __device__ __forceinline__ void combine_rows(const float *__restrict__ pl, const float *__restrict__ po,
                                              int S, bool aborted, float *__restrict__ o,
                                              float *__restrict__ lse)
 {
     constexpr int NC = D / 4;    // float4 columns of a row
     constexpr int NG = 64 / NC;  // row groups in a wave
-    constexpr int PF = 8;        // partial rows per lane loaded up front
     const int lane = threadIdx.x & 63;
     const int col = lane % NC, grp = lane / NC;
     po += col * 4;
@@ -188,7 +188,7 @@ __device__ __forceinline__ void combine_rows(const float *__restrict__ pl, const
 }
 
 // split-K partials: rows [B][Hq][S]
-template <int D>
+template <int D, int PF>
 __global__ __launch_bounds__(kThreads) void splitk_combine_wave_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_lse, int BH, int Hq, int S,
     const int32_t *__restrict__ req_status, float *__restrict__ out, float *__restrict__ lse_out)
@@ -197,9 +197,9 @@ __global__ __launch_bounds__(kThreads) void splitk_combine_wave_kernel(
     if (bh >= BH)
         return;
     const bool aborted = req_status != nullptr && req_status[bh / Hq] != 0;
-    combine_rows<D>(part_lse + static_cast<int64_t>(bh) * S, part_o + static_cast<int64_t>(bh) * S * D,
-                    S, aborted, out + static_cast<int64_t>(bh) * D,
-                    lse_out != nullptr ? lse_out + bh : nullptr);
+    const int64_t row0 = static_cast<int64_t>(bh) * S;
+    combine_rows<D, PF>(part_lse + row0, part_o + row0 * D, S, aborted,
+                        out + static_cast<int64_t>(bh) * D, lse_out != nullptr ? lse_out + bh : nullptr);
 }
 
 // Balanced-partition partials (decode_attn.hip): request b's pieces are rows
@@ -236,7 +236,22 @@ __global__ __launch_bounds__(kThreads) void bal_combine_wave_kernel(
     if (w0 == w1)
         return;
     const int64_t row0 = static_cast<int64_t>(h) * R + b + w0;
-    combine_rows<D>(part_lse + row0, part_o + row0 * D, static_cast<int>(w1 - w0 + 1), false, o, lse);
+    combine_rows<D, 8>(part_lse + row0, part_o + row0 * D, static_cast<int>(w1 - w0 + 1), false, o, lse);
+}
+
+template <int D>
+void launch_combine_wave(const float *part_o, const float *part_lse, int BH, int Hq, int S,
+                         const int32_t *req_status, float *out, float *lse, hipStream_t stream)
+{
+    // up to 16 splits: 8 rows per lane up front; more: 32 (64 splits of
+    // 128 dims in one round trip)
+    const dim3 grid(static_cast<unsigned>((BH + kWaves - 1) / kWaves)), block(kThreads);
+    if (S <= 16)
+        hipLaunchKernelGGL((splitk_combine_wave_kernel<D, 8>), grid, block, 0, stream, part_o, part_lse,
+                           BH, Hq, S, req_status, out, lse);
+    else
+        hipLaunchKernelGGL((splitk_combine_wave_kernel<D, 32>), grid, block, 0, stream, part_o, part_lse,
+                           BH, Hq, S, req_status, out, lse);
 }
 
 }  // namespace
@@ -249,21 +264,15 @@ hipError_t launch_splitk_combine(const float *part_o, const float *part_lse, int
     const int64_t bh = static_cast<int64_t>(batch) * num_q_heads;
     if (bh > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
-    if (head_dim == 64 || head_dim == 128) {
-        const unsigned blocks = static_cast<unsigned>((bh + kWaves - 1) / kWaves);
-        if (head_dim == 64)
-            hipLaunchKernelGGL(splitk_combine_wave_kernel<64>, dim3(blocks), dim3(kThreads), 0, stream,
-                               part_o, part_lse, static_cast<int>(bh), num_q_heads, num_splits,
-                               req_status, out, lse);
-        else
-            hipLaunchKernelGGL(splitk_combine_wave_kernel<128>, dim3(blocks), dim3(kThreads), 0, stream,
-                               part_o, part_lse, static_cast<int>(bh), num_q_heads, num_splits,
-                               req_status, out, lse);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(splitk_combine_kernel, dim3(static_cast<unsigned>(bh)), dim3(kThreads), 0,
-                       stream, part_o, part_lse, num_q_heads, num_splits, head_dim, req_status, out,
-                       lse);
+    const int BH = static_cast<int>(bh);
+    if (head_dim == 64)
+        launch_combine_wave<64>(part_o, part_lse, BH, num_q_heads, num_splits, req_status, out, lse, stream);
+    else if (head_dim == 128)
+        launch_combine_wave<128>(part_o, part_lse, BH, num_q_heads, num_splits, req_status, out, lse, stream);
+    else
+        hipLaunchKernelGGL(splitk_combine_kernel, dim3(static_cast<unsigned>(bh)), dim3(kThreads), 0,
+                           stream, part_o, part_lse, num_q_heads, num_splits, head_dim, req_status, out,
+                           lse);
     return hipGetLastError();
 }
 
