@@ -49,7 +49,6 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 COUNTERS_SUMMARY = os.path.join(ROOT, "profiles", "decode_attn_e4m3_gqa8_16k_b64_counters.md")
-ATTN_KERNEL = "decode_attn_mfma_kernel<false, 128"
 COPY_BYTES = 1 << 30
 FLUSH_BYTES = 1 << 30
 SEED = 1003
@@ -78,25 +77,13 @@ def parse_args():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", default=COUNTERS_SUMMARY,
-                    help="counter summary written by --summarize-counters")
-    ap.add_argument("--summarize-counters", nargs=4, default=None,
-                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="turn four rocprofv3 --pmc runs into the counter summary and exit")
+                    help="counter summary of the headline kernel (read for roofline.traffic)")
+    ap.add_argument("--summarize-counters", default=None, metavar="PRESET",
+                    help="turn the rocprofv3 --pmc runs of one counter preset into its summary "
+                         "under profiles/ and exit: " + ", ".join(COUNTER_PRESETS))
+    ap.add_argument("--pmc-dir", default=os.path.join("gpurun_out", "pmc"),
+                    help="where the --pmc runs of --summarize-counters are")
     return ap.parse_args()
-
-
-# the sources the counted attention launch is built and configured from
-ATTN_SOURCES = ("decode_attn.hip", "pafp8_device.hpp", "attn_params.hpp")
-
-
-def source_hash() -> str:
-    """Hash of the attention kernel's sources: counter figures taken on other
-    sources are stale."""
-    h = hashlib.sha256()
-    for name in ATTN_SOURCES:
-        with open(os.path.join(ROOT, "paged_attention_fp8_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(lens, Hq, Hkv, D, P, kv_elem_bytes, checked=True):
@@ -556,49 +543,147 @@ def _pmc_values(directory, counter, kernel_substr):
     return vals
 
 
-def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel,
-    scaled by what the same counters read for a plain 1 GiB device copy."""
-    f = _pmc_values(fetch_dir, "FETCH_SIZE", ATTN_KERNEL)
-    w = _pmc_values(write_dir, "WRITE_SIZE", ATTN_KERNEL)
-    cf = _pmc_values(copy_fetch_dir, "FETCH_SIZE", "copy")
-    cw = _pmc_values(copy_write_dir, "WRITE_SIZE", "copy")
+# Counter presets: one per kernel the bench reports.  Each names the bench
+# arguments that run the kernel's workload, the kernel (a substring of its
+# full name), the sources it is built from, and its algorithmic bytes per
+# launch, computed on the host from the seeded workload definition.
+def _attn_workload_bytes(w, seed, kv_elem_bytes, checked=True):
+    from paged_attention_fp8_amd import inputs as I
+    lens = I.context_lengths(w, seed)
+    stale = set(I.stale_requests(w, seed, len(lens)))
+    live = [0 if b in stale else int(L) for b, L in enumerate(lens)]
+    return algorithmic_bytes(live, w.q_heads, w.kv_heads, w.head_dim, w.page_size, kv_elem_bytes,
+                             checked)
+
+
+def _int4_bytes(M, N=28672, K=8192):
+    return N * K // 2 + (K // 128) * N * 2 + M * K * 2 + M * N * 4
+
+
+def _handoff_bytes(B=8, T=8192, Hkv=8, D=128, P=64):
+    elems = B * T * Hkv * D
+    return 2 * elems * (2 + 1) + B * (T // P) * 4 + 2 * B * 4 + 2 * Hkv * 4
+
+
+def _preset_bytes(name):
+    from paged_attention_fp8_amd import inputs as I
+    if name == "decode_attn_e4m3_gqa8_16k_b64":
+        return _attn_workload_bytes(I.sweep_workload(64, 1), SEED, 1)
+    if name == "decode_attn_wave_e4m3_gqa8_256k_b4_s64":
+        return _attn_workload_bytes(I.scaled(I.WORKLOADS["gqa8_256k_b4"], stale_requests=0), SEED, 1)
+    if name == "splitk_combine_gqa8_256k_b4_s64":
+        B, Hq, S, D = 4, 64, 64, 128
+        return B * Hq * S * (D + 1) * 4 + B * Hq * (D + 1) * 4 + B * 4
+    if name == "decode_attn_small_pages_e4m3_gqa4_4k":
+        return _attn_workload_bytes(I.WORKLOADS["gqa4_4k_outliers"], SEED, 1)
+    if name == "decode_attn_bal_e4m3_ragged_32k":
+        return _attn_workload_bytes(I.WORKLOADS["gqa8_ragged_32k"], SEED, 1)
+    if name == "kv_fill_e4m3_handoff_8k_b8":
+        return _handoff_bytes()
+    if name == "int4_gemv_row_28672x8192_m1":
+        return _int4_bytes(1)
+    if name == "int4_gemv_28672x8192_m64":
+        return _int4_bytes(64)
+    raise KeyError(name)
+
+
+_ATTN = ("decode_attn.hip", "pafp8_device.hpp", "attn_params.hpp")
+COUNTER_PRESETS = {
+    "decode_attn_e4m3_gqa8_16k_b64": dict(
+        what="e4m3 paged decode attention, 64 requests x 16384 tokens (the headline launch)",
+        args="--steps 5 --warmup 2 --no-cpu-baseline --no-extras",
+        kernel="decode_attn_mfma_kernel<false, 128, true, false, true>", sources=_ATTN),
+    "decode_attn_wave_e4m3_gqa8_256k_b4_s64": dict(
+        what="e4m3 attention in wave-per-split mode, 4 requests x 262144 tokens, 64 splits "
+             "(median launch: the clean batch; the stale-request batch reads 3/4 of it)",
+        args="--only long_context --steps 3 --warmup 1",
+        kernel="decode_attn_mfma_wave_kernel<false, 128, true, true>", sources=_ATTN),
+    "splitk_combine_gqa8_256k_b4_s64": dict(
+        what="split-K combine of 64 splits, 4 requests x 64 query heads x 128 dims",
+        args="--only long_context --steps 3 --warmup 1",
+        kernel="splitk_combine_wave_kernel<128, 32>", sources=("splitk_combine.hip", "pafp8_device.hpp")),
+    "decode_attn_small_pages_e4m3_gqa4_4k": dict(
+        what="e4m3 attention over 16-token pages, 8 requests x 4096 tokens, GQA 32/8, 4 splits",
+        args="--only gqa4_4k --steps 3 --warmup 1",
+        kernel="decode_attn_mfma_kernel<false, 128, false, false, true>", sources=_ATTN),
+    "decode_attn_bal_e4m3_ragged_32k": dict(
+        what="e4m3 attention, balanced partition, 32 ragged requests of 1k-32k tokens",
+        args="--only fp8_vs_bf16 --steps 3 --warmup 1",
+        kernel="decode_attn_bal_mfma_kernel<false, 128, true, false, true>", sources=_ATTN),
+    "kv_fill_e4m3_handoff_8k_b8": dict(
+        what="kv_quant_fill of 8 prompts x 8192 bf16 tokens into e4m3 pages",
+        args="--only prefill_handoff --steps 3 --warmup 1",
+        kernel="kv_fill_kernel<false, 128>",
+        sources=("kv_write.hip", "pafp8_quant.hpp", "pafp8_append.hpp", "pafp8_device.hpp")),
+    "int4_gemv_row_28672x8192_m1": dict(
+        what="INT4 weight-streaming GEMV, one row of x, 28672 x 8192 weights",
+        args="--only int4_decode_gemv --steps 3 --warmup 1",
+        kernel="int4_gemv_row_kernel", sources=("int4_gemv.hip", "pafp8_device.hpp")),
+    "int4_gemv_28672x8192_m64": dict(
+        what="INT4 weight-streaming GEMV, 64 rows of x, 28672 x 8192 weights",
+        args="--only int4_decode_gemv --steps 3 --warmup 1",
+        kernel="int4_gemv_kernel<4, 8, false>", sources=("int4_gemv.hip", "pafp8_device.hpp")),
+}
+
+
+def preset_hash(sources) -> str:
+    """Hash of a kernel's sources: counter figures taken on other sources are stale."""
+    h = hashlib.sha256()
+    for name in sources:
+        with open(os.path.join(ROOT, "paged_attention_fp8_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_summary_path(preset):
+    return os.path.join(ROOT, "profiles", f"{preset}_counters.md")
+
+
+def summarize_counters(preset, pmc_dir, out_path=None):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one preset's kernel, each
+    scaled by what the same counter reads for a plain 1 GiB device copy, with
+    the kernel's algorithmic bytes beside them."""
+    cfg = COUNTER_PRESETS[preset]
+    d = lambda tag: os.path.join(pmc_dir, tag)
+    f = _pmc_values(d(f"{preset}_fetch"), "FETCH_SIZE", cfg["kernel"])
+    w = _pmc_values(d(f"{preset}_write"), "WRITE_SIZE", cfg["kernel"])
+    cf = _pmc_values(d("copy_fetch"), "FETCH_SIZE", "copy")
+    cw = _pmc_values(d("copy_write"), "WRITE_SIZE", "copy")
     if not (f and w and cf and cw):
-        raise SystemExit(f"missing counter rows: fetch {len(f)} write {len(w)} copy {len(cf)}/{len(cw)}")
+        raise SystemExit(f"{preset}: missing counter rows: fetch {len(f)} write {len(w)} "
+                         f"copy {len(cf)}/{len(cw)}")
     # the copy moves COPY_BYTES each way; its largest dispatches are the copies
     cf_kib, cw_kib = max(cf), max(cw)
     kf = COPY_BYTES / (cf_kib * 1024.0)
     kw = COPY_BYTES / (cw_kib * 1024.0)
     fetch = statistics.median(f) * 1024.0 * kf
     write = statistics.median(w) * 1024.0 * kw
-    lines = [
-        "# HBM traffic counters: e4m3 paged decode attention, 64 requests x 16384 tokens",
-        "",
-        "Commands (MI355X, repository root; one counter per run):",
-        "",
-        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- \\",
-        "        python bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extras",
-        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- \\",
-        "        python bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extras",
-        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copy_fetch -o run -- \\",
-        "        python bench.py --copy-calibration",
-        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_write -o run -- \\",
-        "        python bench.py --copy-calibration",
-        "    python bench.py --summarize-counters gpurun_out/pmc_fetch gpurun_out/pmc_write \\",
-        "        gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write",
-        "",
-        f"attention dispatches: {len(f)} (FETCH_SIZE), {len(w)} (WRITE_SIZE)",
-        f"attention FETCH_SIZE median: {statistics.median(f):.1f} KiB per dispatch",
-        f"attention WRITE_SIZE median: {statistics.median(w):.1f} KiB per dispatch",
-        f"copy calibration: 1 GiB copy reads FETCH_SIZE {cf_kib:.1f} KiB, WRITE_SIZE {cw_kib:.1f} KiB",
-        f"scale factors (known bytes / counter bytes): fetch {kf:.4f}, write {kw:.4f}",
-        f"traffic_bytes_per_launch: {fetch + write:.0f}",
-        f"fetch_bytes_per_launch: {fetch:.0f}",
-        f"write_bytes_per_launch: {write:.0f}",
-        f"source_hash: {source_hash()}",
-        "",
-    ]
-    with open(COUNTERS_SUMMARY, "w") as fh:
+    alg = _preset_bytes(preset)
+    run = lambda c, tag, a: [f"    rocprofv3 --pmc {c} --output-format csv -d {d(tag)} -o run -- \\",
+                             f"        python bench.py {a}"]
+    lines = [f"# HBM traffic counters: {cfg['what']}", "",
+             "Commands (MI355X, repository root; one counter per run):", ""]
+    lines += run("FETCH_SIZE", f"{preset}_fetch", cfg["args"])
+    lines += run("WRITE_SIZE", f"{preset}_write", cfg["args"])
+    lines += run("FETCH_SIZE", "copy_fetch", "--copy-calibration")
+    lines += run("WRITE_SIZE", "copy_write", "--copy-calibration")
+    lines += [f"    python bench.py --summarize-counters {preset} --pmc-dir {pmc_dir}", "",
+              f"kernel: {cfg['kernel']}",
+              f"dispatches: {len(f)} (FETCH_SIZE), {len(w)} (WRITE_SIZE)",
+              f"FETCH_SIZE median: {statistics.median(f):.1f} KiB per dispatch "
+              f"(min {min(f):.1f}, max {max(f):.1f})",
+              f"WRITE_SIZE median: {statistics.median(w):.1f} KiB per dispatch "
+              f"(min {min(w):.1f}, max {max(w):.1f})",
+              f"copy calibration: 1 GiB copy reads FETCH_SIZE {cf_kib:.1f} KiB, WRITE_SIZE {cw_kib:.1f} KiB",
+              f"scale factors (known bytes / counter bytes): fetch {kf:.4f}, write {kw:.4f}",
+              f"traffic_bytes_per_launch: {fetch + write:.0f}",
+              f"fetch_bytes_per_launch: {fetch:.0f}",
+              f"write_bytes_per_launch: {write:.0f}",
+              f"algorithmic_bytes_per_launch: {alg}",
+              f"traffic_over_algorithmic: {(fetch + write) / alg:.4f}",
+              f"source_hash: {preset_hash(cfg['sources'])}", ""]
+    out_path = out_path or counter_summary_path(preset)
+    with open(out_path, "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
 
@@ -614,7 +699,7 @@ def read_traffic(summary_path):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != source_hash():
+    if vals.get("source_hash") != preset_hash(_ATTN):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -654,7 +739,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(args.summarize_counters, args.pmc_dir)
         return
     import torch
     if args.copy_calibration:

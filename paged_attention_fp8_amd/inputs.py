@@ -281,6 +281,14 @@ class DecodeInputs:
         return self.k_tokens[b][:-1], self.v_tokens[b][:-1]
 
 
+def stale_requests(w: Workload, seed: int, batch: int) -> List[int]:
+    """The requests of a batch that get a stale tag (sorted)."""
+    if not w.stale_requests:
+        return []
+    pick = rng(seed, 5).choice(batch, size=min(w.stale_requests, batch), replace=False)
+    return sorted(int(x) for x in pick)
+
+
 def context_lengths(w: Workload, seed: int) -> np.ndarray:
     if w.min_len == w.max_len:
         return np.full(w.batch, w.max_len, dtype=np.int32)
@@ -313,13 +321,10 @@ def make_decode_inputs(w: Workload, seed: int, lengths: Optional[Sequence[int]] 
             v_amax[h] = max(v_amax[h], va)
         ks.append(k)
         vs.append(v)
-    stale = []
-    if w.stale_requests:
-        pick = rng(seed, 5).choice(B, size=min(w.stale_requests, B), replace=False)
-        for b in sorted(int(x) for x in pick):
-            i = int(rng(seed, 6, b).integers(0, pages_needed(lens[b], P)))
-            make_stale(pool, batch, b, i)
-            stale.append(b)
+    stale = stale_requests(w, seed, B)
+    for b in stale:
+        i = int(rng(seed, 6, b).integers(0, pages_needed(lens[b], P)))
+        make_stale(pool, batch, b, i)
     return DecodeInputs(w, seed, q, ks, vs, fp8_scale_from_amax(k_amax),
                         fp8_scale_from_amax(v_amax), pool, batch, stale)
 
@@ -453,12 +458,9 @@ def make_device_decode_inputs(w: Workload, seed: int, device="cuda",
         v_amax = torch.maximum(v_amax, va)
     if qf is not None:
         q = qf.to(torch.bfloat16)
-    stale = []
-    if w.stale_requests:
-        pick = rng(seed, 5).choice(B, size=min(w.stale_requests, B), replace=False)
-        for b in sorted(int(x) for x in pick):
-            i = int(rng(seed, 6, b).integers(0, pages_needed(lens[b], P)))
-            make_stale(pool, batch, b, i)
-            stale.append(b)
+    stale = stale_requests(w, seed, B)
+    for b in stale:
+        i = int(rng(seed, 6, b).integers(0, pages_needed(lens[b], P)))
+        make_stale(pool, batch, b, i)
     return DeviceDecodeInputs(w, seed, q, k, v, fp8_scale_from_amax(k_amax.cpu().numpy()),
                               fp8_scale_from_amax(v_amax.cpu().numpy()), pool, batch, stale)

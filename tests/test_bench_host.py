@@ -46,26 +46,43 @@ def _counter_dir(path, rows):
             w.writerow({"Kernel_Name": kernel, "Counter_Name": counter, "Counter_Value": value})
 
 
-def test_counter_summary_scales_by_the_copy(tmp_path, monkeypatch):
-    """FETCH_SIZE and WRITE_SIZE (KiB) of the attention launches, each scaled
-    by known bytes / counted bytes of a 1 GiB copy; the median launch counts."""
-    attn = bench.ATTN_KERNEL + ", true>(pafp8::AttnParams)"
-    _counter_dir(tmp_path / "f", [(attn, "FETCH_SIZE", v) for v in (1000.0, 1100.0, 1050.0)]
+def test_counter_summary_scales_by_the_copy(tmp_path):
+    """FETCH_SIZE and WRITE_SIZE (KiB) of one preset's kernel, each scaled by
+    known bytes / counted bytes of a 1 GiB copy; the median launch counts;
+    other kernels' rows are ignored; the summary states the algorithmic bytes."""
+    preset = "decode_attn_e4m3_gqa8_16k_b64"
+    attn = "void pafp8::(anonymous namespace)::" + bench.COUNTER_PRESETS[preset]["kernel"] + "(pafp8::AttnParams)"
+    pmc = tmp_path / "pmc"
+    _counter_dir(pmc / f"{preset}_fetch", [(attn, "FETCH_SIZE", v) for v in (1000.0, 1100.0, 1050.0)]
                  + [("other_kernel", "FETCH_SIZE", 9e9)])
-    _counter_dir(tmp_path / "w", [(attn, "WRITE_SIZE", v) for v in (10.0, 12.0, 11.0)])
+    _counter_dir(pmc / f"{preset}_write", [(attn, "WRITE_SIZE", v) for v in (10.0, 12.0, 11.0)])
     gib_kib = (1 << 30) / 1024.0
-    _counter_dir(tmp_path / "cf", [("copyBuffer", "FETCH_SIZE", gib_kib / 2), ("copyBuffer", "FETCH_SIZE", 4.0)])
-    _counter_dir(tmp_path / "cw", [("copyBuffer", "WRITE_SIZE", gib_kib)])
+    _counter_dir(pmc / "copy_fetch", [("copyBuffer", "FETCH_SIZE", gib_kib / 2), ("copyBuffer", "FETCH_SIZE", 4.0)])
+    _counter_dir(pmc / "copy_write", [("copyBuffer", "WRITE_SIZE", gib_kib)])
     out = tmp_path / "summary.md"
-    monkeypatch.setattr(bench, "COUNTERS_SUMMARY", str(out))
-    bench.summarize_counters(*(str(tmp_path / d) for d in ("f", "w", "cf", "cw")))
+    bench.summarize_counters(preset, str(pmc), str(out))
     vals = dict(line.split(":", 1) for line in out.read_text().splitlines()
                 if ":" in line and not line.startswith(" "))
     # fetch counts half the copy's bytes -> factor 2; write counts them all -> factor 1
     assert float(vals["fetch_bytes_per_launch"]) == 1050.0 * 1024 * 2
     assert float(vals["write_bytes_per_launch"]) == 11.0 * 1024
     assert float(vals["traffic_bytes_per_launch"]) == 1050.0 * 1024 * 2 + 11.0 * 1024
+    assert int(vals["algorithmic_bytes_per_launch"]) == 2150711872
     assert bench.read_traffic(str(out)) == 1050.0 * 1024 * 2 + 11.0 * 1024
     # figures taken on other sources are not used
     out.write_text(out.read_text().replace(vals["source_hash"].strip(), "0" * 16))
     assert bench.read_traffic(str(out)) is None
+
+
+def test_counter_presets_name_their_bytes():
+    """Every preset has algorithmic bytes from its workload definition (host
+    only): the INT4 and hand-off figures written out, the others positive."""
+    assert bench._preset_bytes("int4_gemv_28672x8192_m64") == \
+        28672 * 8192 // 2 + 64 * 28672 * 2 + 64 * 8192 * 2 + 64 * 28672 * 4
+    assert bench._preset_bytes("kv_fill_e4m3_handoff_8k_b8") == \
+        2 * 8 * 8192 * 8 * 128 * 3 + 8 * 128 * 4 + 2 * 8 * 4 + 2 * 8 * 4
+    for name in bench.COUNTER_PRESETS:
+        assert bench._preset_bytes(name) > 0, name
+    # the long-context preset counts the clean batch of four 256k-token requests
+    assert bench._preset_bytes("decode_attn_wave_e4m3_gqa8_256k_b4_s64") == \
+        bench.algorithmic_bytes([262144] * 4, 64, 8, 128, 64, 1)
