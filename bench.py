@@ -421,7 +421,9 @@ def int4_decode(args, dev):
     del ws, ss
     torch.cuda.empty_cache()
     return {"workload": "8 int4 weight matrices 28672 x 8192 (bf16 scale per 128 inputs), "
-                        "bf16 activations, fp32 output", "kernel": "int4_gemv_kernel", "points": res}
+                        "bf16 activations, fp32 output",
+            "kernel": "int4_gemv_row_kernel (1 row), int4_gemv_kernel (2-32 rows), "
+                      "int4_gemv_wide_kernel (33-64 rows)", "points": res}
 
 
 def fp8_vs_bf16(args, dev):
@@ -622,7 +624,7 @@ COUNTER_PRESETS = {
     "int4_gemv_28672x8192_m64": dict(
         what="INT4 weight-streaming GEMV, 64 rows of x, 28672 x 8192 weights",
         args="--only int4_decode_gemv --steps 3 --warmup 1",
-        kernel="int4_gemv_kernel<4, 8, false>", sources=("int4_gemv.hip", "pafp8_device.hpp")),
+        kernel="int4_gemv_wide_kernel<2>", sources=("int4_gemv.hip", "pafp8_device.hpp")),
 }
 
 

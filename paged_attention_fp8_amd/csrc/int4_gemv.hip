@@ -36,16 +36,54 @@ namespace {
 constexpr int kGemvWaves = 4;
 constexpr int kGemvThreads = 64 * kGemvWaves;
 constexpr int kGroup = 128;        // input features per scale
+constexpr int kStreamLoad = 2;     // buffer load policy: non-temporal (weights are read once)
 
-// 8 int4 weights (one dword, low nibble first) -> 8 bf16 of q/16, exact
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+// a wave-uniform address kept in scalar registers (a buffer resource built
+// from it otherwise lands in vector registers and every load through it
+// becomes a loop over the distinct values)
+__device__ __forceinline__ void *uniform_ptr(const void *p)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+    const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+    return reinterpret_cast<void *>(lo | (hi << 32));
+}
+
+// v_cvt_off_f32_i4 (q/16 of the low nibble of its operand) reading byte B
+// of v: written out because the compiler folds (w >> 4) >> 8i into one
+// shift and then cannot use the byte select
+template <int B>
+__device__ __forceinline__ float cvt_off_byte(uint32_t v)
+{
+    float f;
+    if constexpr (B == 0)
+        f = __builtin_amdgcn_cvt_off_f32_i4(v);
+    else if constexpr (B == 1)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(f) : "v"(v));
+    else if constexpr (B == 2)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(f) : "v"(v));
+    else
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(f) : "v"(v));
+    return f;
+}
+
+// 8 int4 weights (one dword, low nibble first) -> 8 bf16 of q/16, exact.
+// Nibble 2i is the low half of byte i of w, nibble 2i + 1 that of byte i of
+// w >> 4: one shift, eight conversions, four packs.
 __device__ __forceinline__ bf16x8 int4x8_to_bf16_div16(uint32_t w)
 {
+    const uint32_t hi = w >> 4;
     f32x2 f[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[i][0] = __builtin_amdgcn_cvt_off_f32_i4(w >> (8 * i));
-        f[i][1] = __builtin_amdgcn_cvt_off_f32_i4(w >> (8 * i + 4));
-    }
+    f[0][0] = cvt_off_byte<0>(w);
+    f[0][1] = cvt_off_byte<0>(hi);
+    f[1][0] = cvt_off_byte<1>(w);
+    f[1][1] = cvt_off_byte<1>(hi);
+    f[2][0] = cvt_off_byte<2>(w);
+    f[2][1] = cvt_off_byte<2>(hi);
+    f[3][0] = cvt_off_byte<3>(w);
+    f[3][1] = cvt_off_byte<3>(hi);
     bf16x8 r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -206,6 +244,158 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
         }
 }
 
+// Up to 64 rows of x on 32x32 output tiles (v_mfma_f32_32x32x16_bf16): each
+// x operand a lane reads from LDS feeds 32 weight rows, half the LDS traffic
+// per weight of the 16x16 tiles above.  The packed layout is the same: for
+// k-step s of a group (features 16s .. 16s + 16) the B operand of lane
+// L = 32h + 16t + r is row r of the wave's tile t at features 16s + 8h .. + 8,
+// i.e. dword s/2 of the 16-byte piece at position 16h + r (s even) or
+// 32 + 16h + r (s odd) of that tile's block: two 16-byte loads per lane and
+// group cover the wave's two 1 KiB blocks.  Weights expand as q/16
+// (v_cvt_off_f32_i4) and the factor 16 goes into the scale.
+// A work-group of 4 waves owns 64 output rows (4 tiles): wave w takes the
+// tile pair w & 1 over the half w >> 1 of K; the two halves' x of a step sit
+// side by side in LDS, and the halves' sums meet in LDS at the end.
+template <int MT>   // 32-row tiles of x: 1 (up to 32 rows) or 2 (up to 64)
+__global__ __launch_bounds__(kGemvThreads, 2) void int4_gemv_wide_kernel(
+    const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ w,
+    const uint16_t *__restrict__ scales, int N, int K, float *__restrict__ y)
+{
+    constexpr int PF = 4;                        // groups of weights in flight per wave
+    constexpr int XS = kGroup + 8;               // LDS row stride (bf16), 16 bytes of padding
+    constexpr int XR = 32 * MT;                  // rows of x staged
+    constexpr int XP = 2 * XR * (kGroup / 8) / kGemvThreads;   // 16-byte x pieces per thread per step
+    __shared__ __align__(16) uint16_t xs[2][2][XR * XS];       // [buffer][K half][row][feature]
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int tid = threadIdx.x;
+    const int pair = wave & 1, half = wave >> 1;
+    const int G = K / kGroup, GH = G / 2;        // groups per K half (a multiple of PF)
+    const int r = lane & 15, t = (lane >> 4) & 1, h = lane >> 5;
+    const int n_tiles = N / 16;
+    const int nt = blockIdx.x * kGemvWaves + 2 * pair + t;   // this lane's 16-row weight tile
+    const bool live = nt < n_tiles;
+    const int g0 = half * GH;                    // this wave's first group
+
+    // Buffer loads: a wave-uniform base in the resource, a per-lane offset
+    // fixed for the whole loop and the group's offset in a scalar register,
+    // so stepping through K costs no vector address arithmetic.  A tile past
+    // N reads its wave's first tile (clamped into range) and is not stored.
+    const int tile0 = uniform(min(blockIdx.x * kGemvWaves + 2 * pair, n_tiles - 1));
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(w + static_cast<int64_t>(tile0) * G * 1024), 0, 0x7FFFFFFF, 0x00020000);
+    const int wvo = (live ? nt - tile0 : 0) * G * 1024 + (16 * h + r) * 16;
+    const __amdgpu_buffer_rsrc_t srs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(scales), 0, 0x7FFFFFFF, 0x00020000);
+    const int svo = ((live ? nt : tile0) * 16 + r) * 2;
+    const __amdgpu_buffer_rsrc_t xrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x), 0, 0x7FFFFFFF, 0x00020000);
+
+    f32x16 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            acc[mt][v] = 0.f;
+
+    // x of step i: rows [0, XR) of groups i (half 0) and GH + i (half 1).
+    // Rows >= M repeat row M - 1: an output row depends on its own row of x
+    // alone, and rows >= M are never stored.
+    int xvo[XP], xlds[XP];
+#pragma unroll
+    for (int it = 0; it < XP; ++it) {
+        const int idx = tid + it * kGemvThreads;
+        const int hh = idx / (XR * 16), m = (idx / 16) % XR, c8 = idx % 16;
+        const int mr = m < M ? m : M - 1;
+        xvo[it] = (mr * K + hh * GH * kGroup + c8 * 8) * 2;
+        xlds[it] = hh * XR * XS + m * XS + c8 * 8;
+    }
+    u32x4 xr[XP];
+    auto load_x = [&](int i) {
+#pragma unroll
+        for (int it = 0; it < XP; ++it)
+            xr[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[it], i * kGroup * 2, 0));
+    };
+    auto store_x = [&](int buf) {
+#pragma unroll
+        for (int it = 0; it < XP; ++it)
+            *reinterpret_cast<u32x4 *>(&xs[buf][0][xlds[it]]) = xr[it];
+    };
+
+    u32x4 wlo[PF], whi[PF];   // positions 16h + r (even k-steps) and 32 + 16h + r (odd)
+    uint32_t sr[PF];
+    auto load_w = [&](int u, int g) {
+        wlo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo, g * 1024, kStreamLoad));
+        whi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo + 512, g * 1024, kStreamLoad));
+        sr[u] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo, g * N * 2, 0);
+    };
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+        load_w(u, g0 + u);
+    load_x(0);
+    store_x(0);
+    __syncthreads();
+
+    for (int i0 = 0; i0 < GH; i0 += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int i = i0 + u;
+            load_x(i + 1 < GH ? i + 1 : GH - 1);
+            // keep these loads ahead of the step's weight loads: the LDS
+            // store at the step's end then waits for them alone
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x4 wa = wlo[u], wc = whi[u];
+            const float s16 = 16.0f * __uint_as_float(sr[u] << 16);
+            load_w(u, g0 + (i + PF < GH ? i + PF : GH - 1));
+            const uint16_t *xa = &xs[i & 1][half][(lane & 31) * XS + 8 * h];
+            f32x16 part[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    part[mt][v] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const bf16x8 b = int4x8_to_bf16_div16((s & 1) ? wc[s >> 1] : wa[s >> 1]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xa + mt * 32 * XS + 16 * s);
+                    part[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, part[mt], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] += s16 * part[mt];
+            // every wave is done with buffer (i + 1) & 1 since the last
+            // barrier; after the last step this store is dead but keeps the
+            // x loads unconditional
+            store_x((i + 1) & 1);
+            __syncthreads();
+        }
+    }
+    // the K halves meet: waves 2, 3 hand their sums to waves 0, 1
+    float *red = reinterpret_cast<float *>(&xs[0][0][0]);   // 2 x 64 x 16 * MT floats
+    if (half == 1) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                red[((pair * MT + mt) * 16 + v) * 64 + lane] = acc[mt][v];
+    }
+    __syncthreads();
+    if (half == 1 || !live)
+        return;
+    // acc[mt][v] = y[32mt + 8(v/4) + 4h + v%4][16nt + r]
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int m = mt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (m < M)
+                y[static_cast<int64_t>(m) * N + nt * 16 + r] = acc[mt][v] + red[((pair * MT + mt) * 16 + v) * 64 + lane];
+        }
+}
+
 // One row of x.  The weights expand as in the PLUS136 path (bf16 pairs
 // (136 + q_i, 136 + q_{i+4}), x staged in the same pairing) and x is
 // broadcast to all 16 rows of the MFMA's A operand, so every output row of
@@ -339,10 +529,18 @@ hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const ui
     else                                                                                           \
         hipLaunchKernelGGL((int4_gemv_kernel<MT_, 4, (MT_ <= 2)>), grid, dim3(kGemvThreads), 0, stream, \
                            x, M, w, scales, N, K, y);
+    // 33-64 rows on 32x32 tiles (K a multiple of 1024: whole prefetch rings
+    // in each half of K;
+    // and 32-bit buffer offsets into x and the scales)
+    const bool wide = (K / kGroup / 2) % 4 == 0 && static_cast<int64_t>(K) * 64 * 2 < INT32_MAX &&
+                      static_cast<int64_t>(K / kGroup + 1) * N * 2 < INT32_MAX;
     if (mt == 1) {
         PAFP8_GEMV(1)
     } else if (mt == 2) {
         PAFP8_GEMV(2)
+    } else if (wide) {
+        hipLaunchKernelGGL((int4_gemv_wide_kernel<2>), grid, dim3(kGemvThreads), 0, stream, x, M, w, scales,
+                           N, K, y);
     } else if (mt == 3) {
         PAFP8_GEMV(3)
     } else {
