@@ -422,8 +422,8 @@ def int4_decode(args, dev):
     torch.cuda.empty_cache()
     return {"workload": "8 int4 weight matrices 28672 x 8192 (bf16 scale per 128 inputs), "
                         "bf16 activations, fp32 output",
-            "kernel": "int4_gemv_row_kernel (1 row), int4_gemv_kernel (2-32 rows), "
-                      "int4_gemv_wide_kernel (33-64 rows)", "points": res}
+            "kernel": "int4_gemv_row_kernel (1 row), int4_gemv_kernel (2-16 rows), "
+                      "int4_gemv_wide_kernel (17-64 rows)", "points": res}
 
 
 def fp8_vs_bf16(args, dev):

@@ -253,11 +253,12 @@ pafp8_status int4_pack_weights(const uint8_t *w_rowmajor, int32_t N, int32_t K, 
  *   y         device fp32 [M][N] (output)
  * Requires N % 16 == 0 and K % 512 == 0; any M >= 0 (64 rows of x per
  * launch).  Products are exact and summed in fp32, per group and then over
- * the K / 128 groups; in launches of at most 32 rows the sums run over
- * x * (136 + q) and 136 * sum x is taken back out.  To first order
+ * the K / 128 groups; in launches of at most 16 rows, and of 17 to 32 rows
+ * when K is not a multiple of 1024, the sums run over x * (136 + q) and
+ * 136 * sum x is taken back out.  To first order
  *     |y[m][n] - exact| <= (K / 128 + 160) * 2^-24 * sum_k |x[m][k]| (|q[n][k]| + c) s,
- * c = 272 for rows of a launch of at most 32 rows (M <= 32, or the last
- * launch when M = 64 t + r with r <= 32), c = 0 otherwise. */
+ * c = 272 for the rows of such a launch (M rows, or the last launch's
+ * r = M mod 64 rows), c = 0 otherwise. */
 pafp8_status int4_gemv(const uint16_t *x, int32_t M, const uint8_t *w_packed, const uint16_t *scales,
                        int32_t N, int32_t K, float *y, hipStream_t stream);
 

@@ -17,14 +17,18 @@
 // order, low nibble first), which is exactly lane L's B operand of the j-th
 // v_mfma_f32_16x16x32_bf16 over the block.
 //
-// Two rows of x or more: a work-group of 4 waves owns 64 output rows (one
-// 16-row tile per wave) over all of K.  Per group of 128 features the
-// work-group stages x[0:16*MT][group] in LDS; each wave expands its 1 KiB
-// block to bf16, runs 4 MFMAs per 16-row tile of x and adds s times the
-// group's partial sums into its fp32 accumulators.  Up to 32 rows the
-// expansion is 136 + q (a shift and one logic op per pair) with the offset
-// taken back out by MFMAs against -136; from 33 rows on v_cvt_off_f32_i4
-// gives q/16 exactly and the factor 16 goes into the scale.
+// 2 to 16 rows of x (and up to 64 when K is not a multiple of 1024): a
+// work-group of 4 waves owns 64 output rows (one 16-row tile per wave) over
+// all of K (int4_gemv_kernel).  Per group of 128 features the work-group
+// stages x[0:16*MT][group] in LDS; each wave expands its 1 KiB block to
+// bf16, runs 4 MFMAs per 16-row tile of x and adds s times the group's
+// partial sums into its fp32 accumulators.  Up to 32 rows the expansion is
+// 136 + q (a shift and one logic op per pair) with the offset taken back
+// out by MFMAs against -136; from 33 rows on v_cvt_off_f32_i4 gives q/16
+// exactly and the factor 16 goes into the scale.
+// 17 to 64 rows with K a multiple of 1024: 32x32 MFMA tiles, a work-group
+// of 8 waves per 128 output rows, x loaded straight into LDS
+// (int4_gemv_wide_kernel).
 // One row of x: a work-group per 16-row tile whose waves split K, with x
 // broadcast to the MFMA's 16 rows (int4_gemv_row_kernel).
 #include "pafp8_device.hpp"
@@ -244,156 +248,220 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
         }
 }
 
-// Up to 64 rows of x on 32x32 output tiles (v_mfma_f32_32x32x16_bf16): each
-// x operand a lane reads from LDS feeds 32 weight rows, half the LDS traffic
-// per weight of the 16x16 tiles above.  The packed layout is the same: for
-// k-step s of a group (features 16s .. 16s + 16) the B operand of lane
-// L = 32h + 16t + r is row r of the wave's tile t at features 16s + 8h .. + 8,
-// i.e. dword s/2 of the 16-byte piece at position 16h + r (s even) or
-// 32 + 16h + r (s odd) of that tile's block: two 16-byte loads per lane and
-// group cover the wave's two 1 KiB blocks.  Weights expand as q/16
-// (v_cvt_off_f32_i4) and the factor 16 goes into the scale.
-// A work-group of 4 waves owns 64 output rows (4 tiles): wave w takes the
-// tile pair w & 1 over the half w >> 1 of K; the two halves' x of a step sit
-// side by side in LDS, and the halves' sums meet in LDS at the end.
+// 33 to 64 rows of x on 32x32 output tiles (v_mfma_f32_32x32x16_bf16).  The
+// packed layout is the same as above: for k-step s of a group (features
+// 16s .. 16s + 16) the B operand of lane L = 32h + 16t + r is row r of tile t
+// of a tile pair at features 16s + 8h .. + 8, i.e. dword s/2 of the 16-byte
+// piece at position 16h + r (s even) or 32 + 16h + r (s odd) of that tile's
+// block.  Weights expand as q/16 (v_cvt_off_f32_i4) and the factor 16 goes
+// into the scale.
+// A work-group of 8 waves owns 128 output rows (8 tiles) over all of K:
+// wave w takes the 4 tiles of quad w & 1 (two tile pairs) over the quarter
+// w >> 1 of K, so each x operand it reads from LDS feeds 64 weight rows, and
+// each group of x staged in LDS serves 128.  The quarters' sums meet in LDS
+// at the end.
+// x goes from memory straight into LDS (buffer loads with the LDS
+// destination, 1 KiB per instruction), with no pass through registers.  An
+// instruction fills 4 rows of 256 bytes; the 16-byte piece p of row R holds
+// x's piece p ^ (R & 15), so the 32 rows one operand read touches spread
+// over all banks.
+constexpr int kWideWaves = 8;
+constexpr int kWideThreads = 64 * kWideWaves;
+
 template <int MT>   // 32-row tiles of x: 1 (up to 32 rows) or 2 (up to 64)
-__global__ __launch_bounds__(kGemvThreads, 2) void int4_gemv_wide_kernel(
-    const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ w,
-    const uint16_t *__restrict__ scales, int N, int K, float *__restrict__ y)
+__global__ __launch_bounds__(kWideThreads, 1) void int4_gemv_wide_kernel(
+    const uint16_t *__restrict__ x, int M, const uint8_t *w, const uint16_t *scales, int N, int K,
+    float *__restrict__ y)
 {
-    constexpr int PF = 4;                        // groups of weights in flight per wave
-    constexpr int XS = kGroup + 8;               // LDS row stride (bf16), 16 bytes of padding
-    constexpr int XR = 32 * MT;                  // rows of x staged
-    constexpr int XP = 2 * XR * (kGroup / 8) / kGemvThreads;   // 16-byte x pieces per thread per step
-    __shared__ __align__(16) uint16_t xs[2][2][XR * XS];       // [buffer][K half][row][feature]
+    constexpr int PF = 2;                          // groups of weights in flight per wave
+    constexpr int XR = 32 * MT;                    // rows of x staged
+    constexpr int QTR_BYTES = XR * kGroup * 2;     // one K quarter of a step
+    constexpr int BUF_BYTES = 4 * QTR_BYTES;       // one step: all four quarters
+    constexpr int CW = BUF_BYTES / 1024 / kWideWaves;   // 1 KiB LDS loads per wave per step
+    constexpr int LPS = 3 * 2;                     // weight and scale loads per step (2 tile pairs)
+    __shared__ __align__(1024) unsigned char xs[2 * BUF_BYTES];   // [buffer][K quarter][row][256 B]
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
-    const int tid = threadIdx.x;
-    const int pair = wave & 1, half = wave >> 1;
-    const int G = K / kGroup, GH = G / 2;        // groups per K half (a multiple of PF)
+    const int quad = wave & 1, qtr = wave >> 1;
+    const int G = K / kGroup, GQ = G / 4;        // groups per K quarter (a multiple of PF)
     const int r = lane & 15, t = (lane >> 4) & 1, h = lane >> 5;
     const int n_tiles = N / 16;
-    const int nt = blockIdx.x * kGemvWaves + 2 * pair + t;   // this lane's 16-row weight tile
-    const bool live = nt < n_tiles;
-    const int g0 = half * GH;                    // this wave's first group
+    const int g0 = qtr * GQ;                     // this wave's first group
 
-    // Buffer loads: a wave-uniform base in the resource, a per-lane offset
+    // Buffer loads: a wave-uniform base in the resource, per-lane offsets
     // fixed for the whole loop and the group's offset in a scalar register,
-    // so stepping through K costs no vector address arithmetic.  A tile past
-    // N reads its wave's first tile (clamped into range) and is not stored.
-    const int tile0 = uniform(min(blockIdx.x * kGemvWaves + 2 * pair, n_tiles - 1));
+    // so stepping through K costs no vector address arithmetic.  Tiles past
+    // N read the wave's first tile (clamped into range) and are not stored.
+    // Weights and scales are not declared __restrict__: loads from
+    // restricted read-only memory may be moved across the inline-asm
+    // barriers below, whose waits count them.
+    const int tile0 = uniform(min(blockIdx.x * 8 + 4 * quad, n_tiles - 1));
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(w + static_cast<int64_t>(tile0) * G * 1024), 0, 0x7FFFFFFF, 0x00020000);
-    const int wvo = (live ? nt - tile0 : 0) * G * 1024 + (16 * h + r) * 16;
     const __amdgpu_buffer_rsrc_t srs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(scales), 0, 0x7FFFFFFF, 0x00020000);
-    const int svo = ((live ? nt : tile0) * 16 + r) * 2;
     const __amdgpu_buffer_rsrc_t xrs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x), 0, 0x7FFFFFFF, 0x00020000);
-
-    f32x16 acc[MT];
+    int nt[2], wvo[2], svo[2];   // per tile pair: this lane's tile, weight and scale offsets
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            acc[mt][v] = 0.f;
-
-    // x of step i: rows [0, XR) of groups i (half 0) and GH + i (half 1).
-    // Rows >= M repeat row M - 1: an output row depends on its own row of x
-    // alone, and rows >= M are never stored.
-    int xvo[XP], xlds[XP];
-#pragma unroll
-    for (int it = 0; it < XP; ++it) {
-        const int idx = tid + it * kGemvThreads;
-        const int hh = idx / (XR * 16), m = (idx / 16) % XR, c8 = idx % 16;
-        const int mr = m < M ? m : M - 1;
-        xvo[it] = (mr * K + hh * GH * kGroup + c8 * 8) * 2;
-        xlds[it] = hh * XR * XS + m * XS + c8 * 8;
+    for (int tp = 0; tp < 2; ++tp) {
+        nt[tp] = blockIdx.x * 8 + 4 * quad + 2 * tp + t;
+        const int tl = nt[tp] < n_tiles ? nt[tp] : tile0;
+        wvo[tp] = (tl - tile0) * G * 1024 + (16 * h + r) * 16;
+        svo[tp] = (tl * 16 + r) * 2;
     }
-    u32x4 xr[XP];
-    auto load_x = [&](int i) {
-#pragma unroll
-        for (int it = 0; it < XP; ++it)
-            xr[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[it], i * kGroup * 2, 0));
-    };
-    auto store_x = [&](int buf) {
-#pragma unroll
-        for (int it = 0; it < XP; ++it)
-            *reinterpret_cast<u32x4 *>(&xs[buf][0][xlds[it]]) = xr[it];
-    };
 
-    u32x4 wlo[PF], whi[PF];   // positions 16h + r (even k-steps) and 32 + 16h + r (odd)
-    uint32_t sr[PF];
-    auto load_w = [&](int u, int g) {
-        wlo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo, g * 1024, kStreamLoad));
-        whi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo + 512, g * 1024, kStreamLoad));
-        sr[u] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo, g * N * 2, 0);
-    };
+    f32x16 acc[2][MT];
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
-        load_w(u, g0 + u);
-    load_x(0);
-    store_x(0);
-    __syncthreads();
-
-    for (int i0 = 0; i0 < GH; i0 += PF) {
-#pragma unroll
-        for (int u = 0; u < PF; ++u) {
-            const int i = i0 + u;
-            load_x(i + 1 < GH ? i + 1 : GH - 1);
-            // keep these loads ahead of the step's weight loads: the LDS
-            // store at the step's end then waits for them alone
-            __builtin_amdgcn_sched_barrier(0);
-            const u32x4 wa = wlo[u], wc = whi[u];
-            const float s16 = 16.0f * __uint_as_float(sr[u] << 16);
-            load_w(u, g0 + (i + PF < GH ? i + PF : GH - 1));
-            const uint16_t *xa = &xs[i & 1][half][(lane & 31) * XS + 8 * h];
-            f32x16 part[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    part[mt][v] = 0.f;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const bf16x8 b = int4x8_to_bf16_div16((s & 1) ? wc[s >> 1] : wa[s >> 1]);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xa + mt * 32 * XS + 16 * s);
-                    part[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, part[mt], 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[mt] += s16 * part[mt];
-            // every wave is done with buffer (i + 1) & 1 since the last
-            // barrier; after the last step this store is dead but keeps the
-            // x loads unconditional
-            store_x((i + 1) & 1);
-            __syncthreads();
-        }
-    }
-    // the K halves meet: waves 2, 3 hand their sums to waves 0, 1
-    float *red = reinterpret_cast<float *>(&xs[0][0][0]);   // 2 x 64 x 16 * MT floats
-    if (half == 1) {
+    for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-                red[((pair * MT + mt) * 16 + v) * 64 + lane] = acc[mt][v];
+                acc[tp][mt][v] = 0.f;
+
+    // x of step i: rows [0, XR) of groups qq * GQ + i, qq = 0..3.  LDS load j
+    // of this wave fills 1 KiB block c = CW * wave + j of the step's buffer:
+    // quarter c / (XR / 4), rows 4 (c % (XR / 4)) + lane / 16.  Rows >= M
+    // repeat row M - 1: an output row depends on its own row of x alone, and
+    // rows >= M are never stored.
+    int xvo[CW];
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+        const int c = CW * wave + j;
+        const int qq = c / (XR / 4), row = 4 * (c % (XR / 4)) + (lane >> 4);
+        const int mr = row < M ? row : M - 1;
+        xvo[j] = (mr * K + qq * GQ * kGroup + (((lane & 15) ^ (row & 15)) * 8)) * 2;
+    }
+    // (the offsets are passed as unsigned: given an int, the host pass
+    // silently drops the kernel's launch stub)
+    auto load_x = [&](int i, int buf) {
+#pragma unroll
+        for (int j = 0; j < CW; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xrs, (__attribute__((address_space(3))) void *)(xs + buf * BUF_BYTES + (CW * wave + j) * 1024), 16,
+                static_cast<unsigned>(xvo[j]), static_cast<unsigned>(i * kGroup * 2), 0, 0);
+    };
+    // this lane's operand of k-step s (tile mt adds 32 rows = 8 KiB)
+    int xrd[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        xrd[s] = qtr * QTR_BYTES + (lane & 31) * 256 + (((2 * s + h) ^ (lane & 15)) * 16);
+
+    u32x4 wlo[PF][2], whi[PF][2];   // positions 16h + r (even k-steps) and 32 + 16h + r (odd)
+    uint32_t sr[PF][2];
+    auto load_w = [&](int u, int g) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            wlo[u][tp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo[tp], g * 1024, kStreamLoad));
+            whi[u][tp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo[tp] + 512, g * 1024, kStreamLoad));
+            sr[u][tp] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo[tp], g * N * 2, 0);
+        }
+    };
+    load_x(0, 0);
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+        load_w(u, g0 + u);
+    // x of step 0 in LDS (only the weight loads issued after it may still be
+    // in flight), then every wave's.  The scheduling barriers keep the
+    // compiler from moving memory operations across the waits.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LPS * PF) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int i0 = 0; i0 < GQ; i0 += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int i = i0 + u;
+            // buffer (i + 1) & 1 was last read in step i - 1, before the
+            // barrier that ended it; after the last step this load is dead
+            // but keeps the loop uniform
+            load_x(i + 1 < GQ ? i + 1 : GQ - 1, (u + 1) & 1);
+            // the step's weight loads must follow these: the wait at the
+            // step's end counts on it
+            __builtin_amdgcn_sched_barrier(0);
+            u32x4 wa[2], wc[2];
+            float s16[2];
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+                wa[tp] = wlo[u][tp];
+                wc[tp] = whi[u][tp];
+                s16[tp] = 16.0f * __uint_as_float(sr[u][tp] << 16);
+            }
+            load_w(u, g0 + (i + PF < GQ ? i + PF : GQ - 1));
+            const unsigned char *xb = xs + (u & 1) * BUF_BYTES;
+            f32x16 part[2][MT];
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        part[tp][mt][v] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                bf16x8 a[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    a[mt] = *reinterpret_cast<const bf16x8 *>(xb + xrd[s] + mt * 32 * 256);
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp) {
+                    const bf16x8 b = int4x8_to_bf16_div16((s & 1) ? wc[tp][s >> 1] : wa[tp][s >> 1]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        part[tp][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b, part[tp][mt], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[tp][mt] += s16[tp] * part[tp][mt];
+            // this wave's x loads of step i + 1 have landed (only the weight
+            // loads after them may be outstanding) and its reads of buffer
+            // i & 1 are done; the barrier makes that true of all waves
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS) : "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // no LDS load may still be in flight where the sums meet
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // the K quarters meet: quarters 1..3 hand their sums to quarter 0
+    float *red = reinterpret_cast<float *>(xs);   // [quad][quarter - 1][tp][mt][v][lane]
+    constexpr int RW = 2 * MT * 16 * 64;          // floats per wave
+    if (qtr > 0) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    red[(quad * 3 + qtr - 1) * RW + ((tp * MT + mt) * 16 + v) * 64 + lane] = acc[tp][mt][v];
     }
     __syncthreads();
-    if (half == 1 || !live)
+    if (qtr > 0)
         return;
-    // acc[mt][v] = y[32mt + 8(v/4) + 4h + v%4][16nt + r]
+    // acc[tp][mt][v] = y[32mt + 8(v/4) + 4h + v%4][16 nt[tp] + r]
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int tp = 0; tp < 2; ++tp) {
+        if (nt[tp] >= n_tiles)
+            continue;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int m = mt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (m < M)
-                y[static_cast<int64_t>(m) * N + nt * 16 + r] = acc[mt][v] + red[((pair * MT + mt) * 16 + v) * 64 + lane];
-        }
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = mt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int o = ((tp * MT + mt) * 16 + v) * 64 + lane;
+                if (m < M)
+                    y[static_cast<int64_t>(m) * N + nt[tp] * 16 + r] =
+                        acc[tp][mt][v] + red[(quad * 3) * RW + o] + red[(quad * 3 + 1) * RW + o] +
+                        red[(quad * 3 + 2) * RW + o];
+            }
+    }
 }
 
 // One row of x.  The weights expand as in the PLUS136 path (bf16 pairs
@@ -529,18 +597,20 @@ hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const ui
     else                                                                                           \
         hipLaunchKernelGGL((int4_gemv_kernel<MT_, 4, (MT_ <= 2)>), grid, dim3(kGemvThreads), 0, stream, \
                            x, M, w, scales, N, K, y);
-    // 33-64 rows on 32x32 tiles (K a multiple of 1024: whole prefetch rings
-    // in each half of K;
-    // and 32-bit buffer offsets into x and the scales)
-    const bool wide = (K / kGroup / 2) % 4 == 0 && static_cast<int64_t>(K) * 64 * 2 < INT32_MAX &&
+    // 17-64 rows on 32x32 tiles (K a multiple of 1024: whole prefetch rings
+    // in each quarter of K; and 32-bit buffer offsets into x and the scales)
+    const bool wide = (K / kGroup / 4) % 2 == 0 && static_cast<int64_t>(K) * 64 * 2 < INT32_MAX &&
                       static_cast<int64_t>(K / kGroup + 1) * N * 2 < INT32_MAX;
     if (mt == 1) {
         PAFP8_GEMV(1)
+    } else if (mt == 2 && wide) {
+        hipLaunchKernelGGL((int4_gemv_wide_kernel<1>), dim3((n_tiles + 7) / 8), dim3(kWideThreads), 0, stream, x,
+                           M, w, scales, N, K, y);
     } else if (mt == 2) {
         PAFP8_GEMV(2)
     } else if (wide) {
-        hipLaunchKernelGGL((int4_gemv_wide_kernel<2>), grid, dim3(kGemvThreads), 0, stream, x, M, w, scales,
-                           N, K, y);
+        hipLaunchKernelGGL((int4_gemv_wide_kernel<2>), dim3((n_tiles + 7) / 8), dim3(kWideThreads), 0, stream, x,
+                           M, w, scales, N, K, y);
     } else if (mt == 3) {
         PAFP8_GEMV(3)
     } else {
