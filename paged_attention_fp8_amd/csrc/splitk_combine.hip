@@ -187,6 +187,116 @@ __device__ __forceinline__ void combine_rows(const float *__restrict__ pl, const
         *lse = LSE;
 }
 
+// Many splits (16 < S <= 256): a work-group per (request, query head), its
+// wave w taking the consecutive splits [w C, (w + 1) C), C = ceil(S / 4), so
+// that each lane holds a quarter of the rows it would alone.  The waves'
+// maxima, then their sums of exp(lse_s - max), meet in LDS; each wave then
+// weighs its own rows and wave 0 adds the four partial rows in wave order.
+template <int D>
+__global__ __launch_bounds__(kThreads) void splitk_combine_wg_kernel(
+    const float *__restrict__ part_o, const float *__restrict__ part_lse, int Hq, int S,
+    const int32_t *__restrict__ req_status, float *__restrict__ out, float *__restrict__ lse_out)
+{
+    constexpr int NC = D / 4;    // float4 columns of a row
+    constexpr int NG = 64 / NC;  // row groups in a wave
+    constexpr int PF = 8;        // rows per lane loaded up front
+    __shared__ float sm_m[kWaves], sm_sum[kWaves];
+    __shared__ int sm_nan[kWaves];
+    __shared__ f32x4 sm_acc[kWaves][NC];
+    const int bh = blockIdx.x;
+    const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int col = lane % NC, grp = lane / NC;
+    const int C = (S + kWaves - 1) / kWaves;
+    const int k0 = wave * C;
+    const int n = S - k0 < C ? (S - k0 > 0 ? S - k0 : 0) : C;   // this wave's splits (<= 64)
+    const float *pl = part_lse + static_cast<int64_t>(bh) * S + k0;
+    const float *po = part_o + (static_cast<int64_t>(bh) * S + k0) * D + col * 4;
+    f32x4 pre[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        const int k = grp + i * NG;
+        pre[i] = k < n ? *reinterpret_cast<const f32x4 *>(po + static_cast<int64_t>(k) * D)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float l0 = lane < n ? pl[lane] : kNegInf;
+    const float Mw = wave_max(l0);
+    const bool nan_w = __builtin_amdgcn_ballot_w64(l0 != l0) != 0;
+    if (lane == 0) {
+        sm_m[wave] = Mw;
+        sm_nan[wave] = nan_w;
+    }
+    __syncthreads();
+    float M = sm_m[0];
+    bool has_nan = sm_nan[0] != 0;
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+        M = __builtin_fmaxf(M, sm_m[w]);
+        has_nan |= sm_nan[w] != 0;
+    }
+    const bool aborted = req_status != nullptr && req_status[bh / Hq] != 0;
+    float *o = out + static_cast<int64_t>(bh) * D;
+    float *lse = lse_out != nullptr ? lse_out + bh : nullptr;
+    if (aborted || has_nan || M == kNegInf) {
+        if (wave == 0) {
+            const float fill = (has_nan && !aborted) ? __builtin_nanf("") : 0.f;
+            fill_row<D>(o, lse, fill, (has_nan && !aborted) ? fill : kNegInf);
+        }
+        return;
+    }
+    const float sw = wave_sum(lane < n ? __expf(l0 - M) : 0.f);
+    if (lane == 0)
+        sm_sum[wave] = sw;
+    __syncthreads();
+    float sum = sm_sum[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        sum += sm_sum[w];
+    const float LSE = M + __logf(sum);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        const int k = grp + i * NG;
+        const float lk = __shfl(l0, k & 63, 64);  // every lane takes part
+        if (k < n && lk != kNegInf)               // empty split: contributes nothing
+            acc += __expf(lk - LSE) * pre[i];
+    }
+    // rows past the first PF per lane, PF at a time (all loads of a batch
+    // go out together; the LSEs come from memory, since lanes leave this
+    // loop at different trips and a shuffle may not read an idle lane)
+    for (int kb = grp + PF * NG; kb < n; kb += PF * NG) {
+        f32x4 rows[PF];
+        float lks[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            const int k = kb + i * NG < n ? kb + i * NG : n - 1;   // clamped: no conditional loads
+            rows[i] = *reinterpret_cast<const f32x4 *>(po + static_cast<int64_t>(k) * D);
+            lks[i] = pl[k];
+        }
+#pragma unroll
+        for (int i = 0; i < PF; ++i)
+            if (kb + i * NG < n && lks[i] != kNegInf)
+                acc += __expf(lks[i] - LSE) * rows[i];
+    }
+#pragma unroll
+    for (int m = NC; m < 64; m <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc[e] += shfl_xor_f(acc[e], m);
+    }
+    if (grp == 0)
+        sm_acc[wave][col] = acc;
+    __syncthreads();
+    if (wave == 0 && lane < NC) {
+        f32x4 t = sm_acc[0][lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            t += sm_acc[w][lane];
+        *reinterpret_cast<f32x4 *>(o + lane * 4) = t;
+    }
+    if (threadIdx.x == 0 && lse != nullptr)
+        *lse = LSE;
+}
+
 // split-K partials: rows [B][Hq][S]
 template <int D, int PF>
 __global__ __launch_bounds__(kThreads) void splitk_combine_wave_kernel(
@@ -243,12 +353,16 @@ template <int D>
 void launch_combine_wave(const float *part_o, const float *part_lse, int BH, int Hq, int S,
                          const int32_t *req_status, float *out, float *lse, hipStream_t stream)
 {
-    // up to 16 splits: 8 rows per lane up front; more: 32 (64 splits of
-    // 128 dims in one round trip)
+    // up to 16 splits: a wave per (request, head), 8 rows per lane up
+    // front; 17 to 256: a work-group per (request, head), the splits in four
+    // parts; more: a wave per (request, head), 32 rows per lane at a time
     const dim3 grid(static_cast<unsigned>((BH + kWaves - 1) / kWaves)), block(kThreads);
     if (S <= 16)
         hipLaunchKernelGGL((splitk_combine_wave_kernel<D, 8>), grid, block, 0, stream, part_o, part_lse,
                            BH, Hq, S, req_status, out, lse);
+    else if (S <= 4 * 64)
+        hipLaunchKernelGGL((splitk_combine_wg_kernel<D>), dim3(static_cast<unsigned>(BH)), block, 0, stream,
+                           part_o, part_lse, Hq, S, req_status, out, lse);
     else
         hipLaunchKernelGGL((splitk_combine_wave_kernel<D, 32>), grid, block, 0, stream, part_o, part_lse,
                            BH, Hq, S, req_status, out, lse);

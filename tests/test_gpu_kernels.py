@@ -335,7 +335,8 @@ def test_tag_realloc_repeated_pages():
 
 # --- combine --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("S,D", [(1, 128), (7, 64), (17, 64), (64, 128), (130, 128), (5, 96), (70, 256)])
+@pytest.mark.parametrize("S,D", [(1, 128), (7, 64), (16, 128), (17, 64), (33, 64), (64, 128), (130, 128),
+                                 (256, 128), (257, 64), (5, 96), (70, 256)])
 def test_combine_matches_oracle(S, D):
     say(f"combine: S={S} D={D}")
     g = np.random.default_rng(S * 1000 + D)
