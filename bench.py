@@ -59,6 +59,27 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+# The driver clears device memory that is allocated or released, in the
+# background: for a few seconds after a multi-GiB pool comes or goes, kernels
+# share HBM with that clearing (measured here: after a 2 GiB release the next
+# attention calls run ~4% slower, and within 5 s they are back to normal).
+# Every timed section therefore starts once the device has been quiet for
+# SETTLE_S seconds since the last segment was allocated or freed.
+SETTLE_S = 5.0
+_settled_at = None
+
+
+def settle():
+    import torch
+    global _settled_at
+    torch.cuda.synchronize()
+    st = torch.cuda.memory_stats()
+    mark = (st.get("segment.all.allocated", 0), st.get("segment.all.freed", 0))
+    if mark != _settled_at:
+        time.sleep(SETTLE_S)
+        _settled_at = mark
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,12 +140,14 @@ class Point:
         self.bytes = algorithmic_bytes(live, Hq, self.w.kv_heads, D, self.w.page_size, elem)
 
     def run(self, steps, warmup, splits, check=True, events=True, flush=False, fused=False,
-            append_in_attention=False):
+            append_in_attention=False, prepared=False):
         """Time `steps` decode steps.  flush: before every step, read
         FLUSH_BYTES of other device memory so that no step finds the previous
         one's KV bytes in the last-level caches (the 256 MB MALL holds a
         whole batch of up to 8 requests); step times then come from HIP
-        events around each step instead of the wall clock."""
+        events around each step instead of the wall clock.  prepared (with
+        append_in_attention): the check and the attention go through
+        PreparedCalls, marshalled once before the loop."""
         import torch
         ops, H, st = self.ops, self.H, self.step
         B, Hq, D = st.batch.batch, self.w.q_heads, self.w.head_dim
@@ -145,6 +168,16 @@ class Point:
         sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
         junk = (torch.zeros(FLUSH_BYTES // 8, dtype=torch.int64, device=dev) if flush else None)
+        if prepared:
+            if not append_in_attention:
+                raise ValueError("prepared runs take the append inside the attention launch")
+            stream = torch.cuda.current_stream(dev).cuda_stream
+            chk = (ops.prepare_page_tag_check(st.batch, self.w.page_size, st.page_tags,
+                                              st.expected_tags, status) if check else None)
+            att = ops.prepare_paged_decode_attn(st.cache, st.batch.with_status(status if check else None),
+                                                st.q, self.sm, S, ws, out, lse, k_new=st.k_new,
+                                                v_new=st.v_new)
+        settle()
 
         def one(i=None):
             if junk is not None:
@@ -152,6 +185,17 @@ class Point:
             if i is not None and flush:
                 sev[i][0].record()
             stat = None
+            if prepared:
+                if chk is not None:
+                    chk.run(stream)
+                if i is not None and events:
+                    ev[i][0].record()
+                att.run(stream)
+                if i is not None and events:
+                    ev[i][1].record()
+                if i is not None and flush:
+                    sev[i][1].record()
+                return
             if append_in_attention:   # the append inside the attention launch
                 if check:
                     stat = ops.page_tag_check(st.batch, self.w.page_size, st.page_tags,
@@ -319,6 +363,7 @@ def handoff(args, dev):
     k, v = inp.k_tokens[:, :T].contiguous(), inp.v_tokens[:, :T].contiguous()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    settle()
     for _ in range(args.warmup):
         ops.kv_quant_fill(cache, batch, start, count, k, v)
     for a, b in ev:
@@ -359,6 +404,7 @@ def decode_loop(args, dev):
                              SEED, scale, scale)
         for rid, d in enumerate(dec):
             loop.submit(DL.Request(rid, 16384 - int(d), int(d)))
+        settle()
         stats = []
         t0 = time.perf_counter()
         while (loop.queue or any(r is not None for r in loop.slots)) and len(stats) < 4000:
@@ -401,6 +447,7 @@ def int4_decode(args, dev):
     for M in (1, 8, 16, 32, 64):
         x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        settle()
         for _ in range(args.warmup):
             for i in range(layers):
                 ops.int4_gemv(x, ws[i], ss[i], N, K, out=y)
@@ -826,6 +873,7 @@ def main():
         r1s = one.run(args.steps, args.warmup, 0)
         r1f = one.run(args.steps, args.warmup, 0, append_in_attention=True)
         r1c = one.run(args.steps, args.warmup, 0, fused=True)
+        r1p = one.run(args.steps, args.warmup, 0, append_in_attention=True, prepared=True, events=False)
         result["append_in_attention"] = {
             "step": "tag check + attention with the append in its launch, against tag check + "
                     "append + attention (and, at one request, the check inside the append launch)",
@@ -833,9 +881,12 @@ def main():
                     "tokens_per_s": B / (ra["ms_per_step"] * 1e-3)},
             "b1": {"ms_per_step": r1f["ms_per_step"], "separate_ms_per_step": r1s["ms_per_step"],
                    "checked_append_ms_per_step": r1c["ms_per_step"],
+                   # the same step through prepared calls (argument checks
+                   # and marshalling done once; still eager launches)
+                   "prepared_ms_per_step": r1p["ms_per_step"],
                    "tokens_per_s": 1 / (r1f["ms_per_step"] * 1e-3), "splits": r1f["splits"]},
         }
-        del ra, one, r1s, r1f, r1c
+        del ra, one, r1s, r1f, r1c, r1p
         q = Point(32, ops.KV_BF16, dev)
         rb = q.run(args.steps, args.warmup, args.splits)
         bms = statistics.mean(rb["attn_ms"])

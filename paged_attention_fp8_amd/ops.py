@@ -126,6 +126,27 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+class PreparedCall:
+    """One entry-point call with its arguments checked and marshalled once:
+    run() only issues it on a stream (the current stream of the call's device
+    unless a stream handle is given).  The tensors it was prepared with must
+    stay alive with the same shapes; their contents may change between runs
+    (a decode loop rewrites q, lengths and tables in place).  For loops
+    where the per-call argument checks would cost more than the kernels."""
+
+    def __init__(self, fn, args, what, device, keep, result):
+        self._fn, self._args, self._what, self._dev = fn, tuple(args), what, device
+        self._keep = keep          # ctypes structs the args point at
+        self.result = result
+
+    def run(self, stream: Optional[int] = None):
+        st = _stream(self._dev) if stream is None else stream
+        status = self._fn(*self._args, st)
+        if status != 0:
+            _check(status, self._what)
+        return self.result
+
+
 # ----------------------------------------------------------------------------
 # the two objects of the ABI
 # ----------------------------------------------------------------------------
@@ -226,9 +247,8 @@ class DecodeBatch:
 # entry points
 # ----------------------------------------------------------------------------
 
-def page_tag_check(batch: DecodeBatch, page_size: int, page_tags: torch.Tensor,
-                   expected_tags: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Per-request status (0 = OK, else PAFP8_REQ_* flags)."""
+def _tag_check_call(batch: DecodeBatch, page_size: int, page_tags: torch.Tensor,
+                    expected_tags: torch.Tensor, out: Optional[torch.Tensor]) -> PreparedCall:
     dev = batch.page_table.device
     bs = batch._struct(dev)
     # tags are 32-bit patterns; int32 and uint32 tensors are both accepted
@@ -238,10 +258,22 @@ def page_tag_check(batch: DecodeBatch, page_size: int, page_tags: torch.Tensor,
     if out is None:
         out = torch.empty(batch.batch, dtype=torch.int32, device=dev)
     _need(out, "req_status_out", torch.int32, (batch.batch,), dev)
-    _check(lib().page_tag_check(ctypes.byref(bs), page_size, page_tags.data_ptr(),
-                                page_tags.numel(), expected_tags.data_ptr(), out.data_ptr(),
-                                _stream(dev)), "page_tag_check")
-    return out
+    return PreparedCall(lib().page_tag_check,
+                        (ctypes.byref(bs), page_size, page_tags.data_ptr(), page_tags.numel(),
+                         expected_tags.data_ptr(), out.data_ptr()),
+                        "page_tag_check", dev, (bs, batch, page_tags, expected_tags), out)
+
+
+def page_tag_check(batch: DecodeBatch, page_size: int, page_tags: torch.Tensor,
+                   expected_tags: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-request status (0 = OK, else PAFP8_REQ_* flags)."""
+    return _tag_check_call(batch, page_size, page_tags, expected_tags, out).run()
+
+
+def prepare_page_tag_check(batch: DecodeBatch, page_size: int, page_tags: torch.Tensor,
+                           expected_tags: torch.Tensor, out: torch.Tensor) -> PreparedCall:
+    """page_tag_check as a PreparedCall writing `out`."""
+    return _tag_check_call(batch, page_size, page_tags, expected_tags, out)
 
 
 def _kv_src(t, name, shape, dev):
@@ -347,19 +379,10 @@ def default_balanced_groups(num_kv_heads: int, num_cus: int = 0) -> int:
 BALANCED = "balanced"
 
 
-def paged_decode_attn(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor, sm_scale: float,
-                      num_splits=0, workspace: Optional[torch.Tensor] = None,
-                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                      return_lse: bool = True, k_new: Optional[torch.Tensor] = None,
-                      v_new: Optional[torch.Tensor] = None):
-    """Decode attention over the paged cache; dispatches to
-    paged_decode_attn_fp8 or paged_decode_attn_bf16 by the pool's dtype, or,
-    given this step's k_new and v_new (bf16 [B][Hkv][D]), to their _append
-    forms, which write that token in the same launch.
-    num_splits: S >= 1 uniform splits, 0 the library's default, -W (or
-    BALANCED for pafp8_default_balanced_groups) the balanced partition over W
-    work-groups per KV head.
-    Returns (out fp32 [B][Hq][D], lse fp32 [B][Hq] or None)."""
+def _attn_call(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor, sm_scale: float,
+               num_splits, workspace: Optional[torch.Tensor], out: Optional[torch.Tensor],
+               lse: Optional[torch.Tensor], return_lse: bool, k_new: Optional[torch.Tensor],
+               v_new: Optional[torch.Tensor]) -> PreparedCall:
     dev = cache.device
     cs, bs = cache._struct(), batch._struct(dev)
     if q.dim() != 3:
@@ -389,21 +412,49 @@ def paged_decode_attn(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor, 
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if (k_new is None) != (v_new is None):
         raise ValueError("give both k_new and v_new, or neither")
+    keep = (cs, bs, cache, batch, q, workspace, k_new, v_new)
+    head = (ctypes.byref(cs), ctypes.byref(bs), q.data_ptr(), Hq, float(sm_scale), num_splits,
+            ws_ptr, ws_bytes)
     if k_new is not None:
         shape = (B, cache.num_kv_heads, cache.head_dim)
         _kv_src(k_new, "k_new", shape, dev)
         _kv_src(v_new, "v_new", shape, dev)
         fn = (lib().paged_decode_attn_bf16_append if cache.kv_dtype == KV_BF16
               else lib().paged_decode_attn_fp8_append)
-        _check(fn(ctypes.byref(cs), ctypes.byref(bs), q.data_ptr(), Hq, float(sm_scale), num_splits,
-                  ws_ptr, ws_bytes, k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(), _ptr(lse),
-                  _stream(dev)), "paged_decode_attn (append)")
-        return out, lse
+        return PreparedCall(fn, head + (k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(), _ptr(lse)),
+                            "paged_decode_attn (append)", dev, keep, (out, lse))
     fn = lib().paged_decode_attn_bf16 if cache.kv_dtype == KV_BF16 else lib().paged_decode_attn_fp8
-    _check(fn(ctypes.byref(cs), ctypes.byref(bs), q.data_ptr(), Hq, float(sm_scale), num_splits,
-              ws_ptr, ws_bytes, out.data_ptr(), _ptr(lse), _stream(dev)),
-           "paged_decode_attn")
-    return out, lse
+    return PreparedCall(fn, head + (out.data_ptr(), _ptr(lse)), "paged_decode_attn", dev, keep,
+                        (out, lse))
+
+
+def paged_decode_attn(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor, sm_scale: float,
+                      num_splits=0, workspace: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      return_lse: bool = True, k_new: Optional[torch.Tensor] = None,
+                      v_new: Optional[torch.Tensor] = None):
+    """Decode attention over the paged cache; dispatches to
+    paged_decode_attn_fp8 or paged_decode_attn_bf16 by the pool's dtype, or,
+    given this step's k_new and v_new (bf16 [B][Hkv][D]), to their _append
+    forms, which write that token in the same launch.
+    num_splits: S >= 1 uniform splits, 0 the library's default, -W (or
+    BALANCED for pafp8_default_balanced_groups) the balanced partition over W
+    work-groups per KV head.
+    Returns (out fp32 [B][Hq][D], lse fp32 [B][Hq] or None)."""
+    return _attn_call(cache, batch, q, sm_scale, num_splits, workspace, out, lse, return_lse,
+                      k_new, v_new).run()
+
+
+def prepare_paged_decode_attn(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor,
+                              sm_scale: float, num_splits=0,
+                              workspace: Optional[torch.Tensor] = None,
+                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                              return_lse: bool = True, k_new: Optional[torch.Tensor] = None,
+                              v_new: Optional[torch.Tensor] = None) -> PreparedCall:
+    """paged_decode_attn as a PreparedCall (same arguments); run() returns
+    (out, lse).  A workspace it allocates is kept with it."""
+    return _attn_call(cache, batch, q, sm_scale, num_splits, workspace, out, lse, return_lse,
+                      k_new, v_new)
 
 
 def paged_decode_attn_noalloc(cache: PagedKVCache, batch: DecodeBatch, q: torch.Tensor,
