@@ -650,7 +650,7 @@ COUNTER_PRESETS = {
     "splitk_combine_gqa8_256k_b4_s64": dict(
         what="split-K combine of 64 splits, 4 requests x 64 query heads x 128 dims",
         args="--only long_context --steps 3 --warmup 1",
-        kernel="splitk_combine_wave_kernel<128, 32>", sources=("splitk_combine.hip", "pafp8_device.hpp")),
+        kernel="splitk_combine_wg_kernel<128>", sources=("splitk_combine.hip", "pafp8_device.hpp")),
     "decode_attn_small_pages_e4m3_gqa4_4k": dict(
         what="e4m3 attention over 16-token pages, 8 requests x 4096 tokens, GQA 32/8, 4 splits",
         args="--only gqa4_4k --steps 3 --warmup 1",
