@@ -40,6 +40,7 @@ namespace {
 constexpr int kGemvWaves = 4;
 constexpr int kGemvThreads = 64 * kGemvWaves;
 constexpr int kGroup = 128;        // input features per scale
+constexpr int kXcds = 8;           // MI355X: work-groups are dealt to 8 XCDs in turn
 constexpr int kStreamLoad = 2;     // buffer load policy: non-temporal (weights are read once)
 
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
@@ -485,7 +486,13 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_row_kernel(
     __shared__ float red[kGemvWaves][16];
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
-    const int nt = blockIdx.x;
+    // XCD-aware tiles: work-groups go to the 8 XCDs in turn, so XCD x gets
+    // the consecutive tiles [x * per, (x + 1) * per) -- the four tiles whose
+    // scales share a 128-byte line are fetched into one L2, not four
+    const int n_tiles = N / 16, per = (n_tiles + kXcds - 1) / kXcds;
+    const int nt = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    if (nt >= n_tiles)
+        return;
     const int G = K / kGroup;
     const int C = G / XC;                                   // chunks of K
     const int c0 = wave * C / kGemvWaves, c1 = (wave + 1) * C / kGemvWaves;
@@ -586,7 +593,8 @@ hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const ui
     const int mt = (M + 15) / 16;
     const bool pf8 = (K / kGroup) % 8 == 0;   // K % 512 == 0 gives a multiple of 4
     if (M == 1) {
-        hipLaunchKernelGGL(int4_gemv_row_kernel, dim3(n_tiles), dim3(kGemvThreads), 0, stream, x, w,
+        const int per = (n_tiles + kXcds - 1) / kXcds;
+        hipLaunchKernelGGL(int4_gemv_row_kernel, dim3(per * kXcds), dim3(kGemvThreads), 0, stream, x, w,
                            scales, N, K, y);
         return hipGetLastError();
     }
