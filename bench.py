@@ -104,6 +104,11 @@ def parse_args():
                          "under profiles/ and exit: " + ", ".join(COUNTER_PRESETS))
     ap.add_argument("--pmc-dir", default=os.path.join("gpurun_out", "pmc"),
                     help="where the --pmc runs of --summarize-counters are")
+    ap.add_argument("--summarize-kernel-stats", default=None, metavar="NAME",
+                    help="turn a rocprofv3 --kernel-trace --stats run (--stats-dir) into "
+                         "profiles/NAME_kernel_stats.md and exit: " + ", ".join(STATS_PRESETS))
+    ap.add_argument("--stats-dir", default=os.path.join("gpurun_out", "prof"),
+                    help="where the --kernel-trace --stats run of --summarize-kernel-stats is")
     return ap.parse_args()
 
 
@@ -737,6 +742,66 @@ def summarize_counters(preset, pmc_dir, out_path=None):
     print("\n".join(lines))
 
 
+# Kernel-trace summaries: the bench arguments profiled and what the summary is of.
+STATS_PRESETS = {
+    "decode_attn_e4m3_gqa8_16k_b64": dict(
+        what="e4m3 paged decode attention, 64 requests x 16384 tokens (the headline step: "
+             "page_tag_check + kv_quant_append + paged_decode_attn_fp8)",
+        args="--steps 20 --warmup 5 --no-cpu-baseline --no-extras",
+        headline="decode_attn_mfma_kernel<false, 128, true, false, true>"),
+    "path_extras": dict(
+        what="every kernel of the library under the full bench run (headline, bf16 twin, "
+             "concurrency sweep, 4k small pages, long context, hand-off, decode loop, INT4, ragged)",
+        args="--steps 20 --warmup 5 --no-cpu-baseline", headline=None),
+}
+
+
+def summarize_kernel_stats(name, stats_dir, out_path=None):
+    """The library's kernels from a rocprofv3 --kernel-trace --stats run: calls
+    and durations, and for the headline preset the attention launch's
+    algorithmic bytes over its average duration."""
+    import csv
+    cfg = STATS_PRESETS[name]
+    paths = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_stats.csv under {stats_dir}")
+    rows = []
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if "pafp8::" in r["Name"]:
+                    rows.append(r)
+    def short(n):   # "void pafp8::(anonymous namespace)::k<...>(args)" -> "k<...>"
+        n = n.replace("pafp8::(anonymous namespace)::", "").replace("void ", "", 1)
+        return n.split("(")[0]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# rocprofv3 kernel statistics: {cfg['what']}", "",
+             "Command (MI355X, repository root):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d {stats_dir} -o run -- \\",
+             f"        python bench.py {cfg['args']}",
+             f"    python bench.py --summarize-kernel-stats {name} --stats-dir {stats_dir}", "",
+             "Calls include warm-up and cache-building launches.", "",
+             "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} |")
+    if cfg["headline"]:
+        h = [r for r in rows if cfg["headline"] in r["Name"]]
+        if h:
+            avg = float(h[0]["AverageNs"])
+            alg = _preset_bytes("decode_attn_e4m3_gqa8_16k_b64")
+            lines += ["", f"headline kernel: {cfg['headline']}",
+                      f"average_duration_ns: {avg:.0f}",
+                      f"algorithmic_bytes_per_launch: {alg}",
+                      f"achieved_GBps: {alg / avg:.1f}",
+                      f"frac_of_8TBps: {alg / avg / PEAK_HBM_GBS:.4f}"]
+    lines.append("")
+    out_path = out_path or os.path.join(ROOT, "profiles", f"{name}_kernel_stats.md")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def read_traffic(summary_path):
     """HBM bytes per attention launch from the committed counter summary, or
     None when there is none or it was taken on other kernel sources."""
@@ -787,6 +852,9 @@ def main():
               "is the per-GPU throughput",
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_kernel_stats:
+        summarize_kernel_stats(args.summarize_kernel_stats, args.stats_dir)
+        return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.pmc_dir)
         return
