@@ -86,3 +86,28 @@ def test_counter_presets_name_their_bytes():
     # the long-context preset counts the clean batch of four 256k-token requests
     assert bench._preset_bytes("decode_attn_wave_e4m3_gqa8_256k_b4_s64") == \
         bench.algorithmic_bytes([262144] * 4, 64, 8, 128, 64, 1)
+
+
+def test_kernel_stats_summary(tmp_path):
+    """The kernel-trace summary keeps the library's kernels only, names them
+    without namespace and arguments, and divides the headline's algorithmic
+    bytes by its average duration."""
+    d = tmp_path / "stats" / "host"
+    d.mkdir(parents=True)
+    with open(d / "run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs",
+                    "StdDev"])
+        w.writerow(["void pafp8::(anonymous namespace)::decode_attn_mfma_kernel<false, 128, true, false, "
+                    "true>(pafp8::AttnParams)", 25, 8000000, 320000, 90, 310000, 330000, 1])
+        w.writerow(["void pafp8::(anonymous namespace)::tag_check_kernel(int, int)", 25, 100000, 4000, 1,
+                    3000, 5000, 1])
+        w.writerow(["at::native::reduce_kernel<512, 1>(...)", 3, 600000, 200000, 9, 1, 2, 0])
+    out = tmp_path / "summary.md"
+    bench.summarize_kernel_stats("decode_attn_e4m3_gqa8_16k_b64", str(tmp_path / "stats"), str(out))
+    text = out.read_text()
+    assert "| decode_attn_mfma_kernel<false, 128, true, false, true> | 25 | 320000 |" in text
+    assert "| tag_check_kernel | 25 | 4000 |" in text
+    assert "reduce_kernel" not in text
+    alg = bench._preset_bytes("decode_attn_e4m3_gqa8_16k_b64")
+    assert f"achieved_GBps: {alg / 320000:.1f}" in text
