@@ -142,7 +142,7 @@ def test_balanced_edge_requests():
 
 
 def test_balanced_against_uniform_splits_and_deterministic():
-    """Same attention as the uniform split path up to the fp16 rounding of P
+    """Same attention as the uniform split path up to the rounding of P
     against different running maxima (bound as in the split-invariance test),
     and bitwise repeatable."""
     w = CASES[4]
@@ -151,7 +151,7 @@ def test_balanced_against_uniform_splits_and_deterministic():
     ops.kv_quant_append(step.cache, step.batch, step.k_new, step.v_new)
     base = [t.cpu().numpy() for t in ops.paged_decode_attn(step.cache, step.batch, step.q, 0.09, 1)]
     vmax = 448.0 * float(inp.v_scale.max())
-    bound = 2.0 ** -10 * vmax + 1e-5
+    bound = 2.0 ** -14 * vmax + 1e-6
     for groups in (2, 7, 64):
         a = [t.cpu().numpy() for t in ops.paged_decode_attn(step.cache, step.batch, step.q, 0.09, -groups)]
         b = [t.cpu().numpy() for t in ops.paged_decode_attn(step.cache, step.batch, step.q, 0.09, -groups)]
@@ -200,11 +200,13 @@ def test_determinism_and_split_invariance():
         b = [t.cpu().numpy() for t in b]
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), f"S={S} not deterministic"
         runs[S] = a
-    # different splits round P to fp16 against different running maxima: each
-    # run's P carries a relative error <= 2^-11, so two runs differ by at most
-    # 2^-10 * max|v| (plus fp32 accumulation noise)
+    # different splits split P into bf16 high + low parts against different
+    # running maxima: each run's P carries a relative error <= 2^-16, so two
+    # runs differ by at most 2^-15 * max|v|, plus fp32 summation in another
+    # order (a few 2^-24 per step); 2^-14 * max|v| covers both, far inside
+    # the parity tolerance
     vmax = 448.0 * float(inp.v_scale.max())
-    bound = 2.0 ** -10 * vmax + 1e-5
+    bound = 2.0 ** -14 * vmax + 1e-6
     for S in (2, 5, 24):
         diff = np.abs(runs[S][0] - runs[1][0]).max()
         say(f"  split {S} vs 1: max |diff| = {diff:.3e} (bound {bound:.3e})")
