@@ -468,10 +468,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void int4_gemv_wide_kernel(
 // One row of x.  The weights expand as in the PLUS136 path (bf16 pairs
 // (136 + q_i, 136 + q_{i+4}), x staged in the same pairing) and x is
 // broadcast to all 16 rows of the MFMA's A operand, so every output row of
-// the MFMA is y's row and lanes 0..15 read it off; a second MFMA of the same
-// x against a constant -136 takes the offset back out.  Against dot-product
-// instructions on the VALU this halves the VALU work per weight, and the
-// matrix cores, otherwise idle, absorb the rest.
+// the MFMA is y's row and lanes 0..15 read it off.  The offset, 136 times
+// the group's sum of x, is one scalar per group, taken out as the group's
+// partial sum joins the accumulator.  Against dot-product instructions on
+// the VALU this halves the VALU work per weight.
 //
 // A work-group owns one 16-row tile; its four waves take consecutive quarters
 // of K (in chunks of 4 groups), each with its own prefetch ring and its own
@@ -498,7 +498,6 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_row_kernel(
     const int c0 = wave * C / kGemvWaves, c1 = (wave + 1) * C / kGemvWaves;
     const int c = lane & 15, kq = lane >> 4;
     const int g_first = c0 * XC, g_last = c1 * XC - 1;      // this wave's groups (none if c0 == c1)
-    const bf16x8 neg136 = __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
 
     u32x4 xr;
     auto load_x = [&](int ch) {
@@ -511,6 +510,22 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_row_kernel(
         v[2] = __builtin_amdgcn_perm(xr[3], xr[1], 0x05040100u);   // 2, 6
         v[3] = __builtin_amdgcn_perm(xr[3], xr[1], 0x07060302u);   // 3, 7
         *reinterpret_cast<u32x4 *>(&xs[wave][buf][lane * 4]) = v;
+    };
+    // The expansion's offset, 136 times the sum of x over a group, is the same
+    // for every output row (x has one row): one scalar per group of the
+    // staged chunk, from the 16 lanes 16u .. 16u + 15 that hold group u.
+    float cx[XC];
+    auto offsets = [&]() {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            t += bf16_lo(xr[e]) + bf16_hi(xr[e]);
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1)
+            t += shfl_xor_f(t, m);
+#pragma unroll
+        for (int u = 0; u < XC; ++u)
+            cx[u] = -136.0f * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 16 * u));
     };
 
     float tot = 0.f;
@@ -526,6 +541,7 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_row_kernel(
         }
         load_x(c0);
         store_x(0);
+        offsets();
         for (int ch = c0; ch < c1; ++ch) {
             const int buf = (ch - c0) & 1;
             load_x(ch + 1 < c1 ? ch + 1 : ch);   // unconditional: clamped into this wave's range
@@ -547,12 +563,12 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_row_kernel(
                     const bf16x8 a = __builtin_bit_cast(
                         bf16x8, *reinterpret_cast<const u32x4 *>(&xs[wave][buf][(u * 16 + 4 * j + kq) * 4]));
                     part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, int4x8_to_bf16_plus136(wq[j]), part, 0, 0, 0);
-                    part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, neg136, part, 0, 0, 0);
                 }
-                tot = __builtin_fmaf(s, part[0], tot);   // part[i]: output row 4kq + i, column c
+                tot = __builtin_fmaf(s, part[0] + cx[u], tot);   // part[i]: output row 4kq + i, column c
             }
             // the wave's own LDS: its DS operations run in order, no barrier
             store_x(buf ^ 1);
+            offsets();
         }
     }
     if (kq == 0)
