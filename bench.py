@@ -532,6 +532,68 @@ def _attn_point(pt, rr):
             "splits": rr["splits"], "algorithmic_bytes": pt.bytes}
 
 
+class ReadCeiling:
+    """What the memory system delivers for a point's byte count: the
+    library's bare non-temporal read (ops.stream_read) of the same number of
+    bytes, each launch after the same 1 GiB flush and timed with the same HIP
+    events as the attention; the best of a few work-group counts is kept.
+    No kernel that must read those bytes once can beat it under this timing,
+    so attn_us / read_us says how much of the attention's time is more than
+    the read itself."""
+    CAPACITY = 5 << 29          # 2.5 GiB; the largest point reads 2.15 GB
+    GRIDS = (256, 512, 1024)
+
+    def __init__(self, dev):
+        import torch
+        from paged_attention_fp8_amd import ops
+        self.ops = ops
+        self.buf = torch.full((self.CAPACITY,), 0x5A, dtype=torch.uint8, device=dev)
+        self.junk = torch.zeros(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
+        self.sink = torch.empty(max(self.GRIDS) * ops.STREAM_READ_THREADS, dtype=torch.int32,
+                                device=dev)
+        self.done = {}
+
+    def __call__(self, nbytes, steps):
+        import torch
+        n = min(nbytes, self.CAPACITY) // self.ops.STREAM_READ_TILE * self.ops.STREAM_READ_TILE
+        if n not in self.done:
+            view = self.buf[:n]
+            best = None
+            for g in self.GRIDS:
+                self.ops.stream_read(view, g, self.sink)
+                settle()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(steps)]
+                for a, b in ev:
+                    self.junk.max()
+                    a.record()
+                    self.ops.stream_read(view, g, self.sink)
+                    b.record()
+                torch.cuda.synchronize()
+                us = 1e3 * statistics.mean(a.elapsed_time(b) for a, b in ev)
+                if best is None or us < best[0]:
+                    best = (us, g)
+            self.done[n] = {"read_us": best[0], "read_work_groups": best[1], "read_bytes": n,
+                            "read_frac": n / (best[0] * 1e-6) / 1e9 / PEAK_HBM_GBS}
+        return dict(self.done[n])
+
+
+_read_ceilings = {}
+
+
+def read_ceiling(dev, nbytes, steps):
+    """ReadCeiling figures for nbytes, with attn_us to be set beside them."""
+    if dev not in _read_ceilings:
+        _read_ceilings[dev] = ReadCeiling(dev)
+    return _read_ceilings[dev](nbytes, steps)
+
+
+def _with_ceiling(entry, dev, nbytes, steps):
+    entry.update(read_ceiling(dev, nbytes, steps))
+    entry["attn_over_read"] = entry["attn_us"] / entry["read_us"]
+    return entry
+
+
 def concurrency_sweep(args, dev, head=None):
     """The concurrency table of the pages' KV-cache section: 1, 8, 16, 32 and
     64 requests of 16,384 tokens (GQA 64/8, head_dim 128, 64-token pages) in
@@ -556,8 +618,10 @@ def concurrency_sweep(args, dev, head=None):
                     points.append(entry)
                     continue
             entry.update(_attn_point(pt, pt.run(args.steps, args.warmup, 0, flush=True)))
+            _with_ceiling(entry, dev, pt.bytes, args.steps)
             points.append(entry)
-            log(f"sweep {name} B={b}: {entry['attn_us']:.1f} us, {100 * entry['attn_frac']:.1f}%")
+            log(f"sweep {name} B={b}: {entry['attn_us']:.1f} us, {100 * entry['attn_frac']:.1f}%; "
+                f"bare read {entry['read_us']:.1f} us, {100 * entry['read_frac']:.1f}%")
             if pt is not head:
                 del pt
                 torch.cuda.empty_cache()
@@ -578,7 +642,9 @@ def gqa4_4k(args, dev):
     for kv_dtype, name in ((ops.KV_FP8_E4M3, "e4m3"), (ops.KV_BF16, "bf16")):
         pt = Point(w.batch, kv_dtype, dev, workload=w)
         res[name] = _attn_point(pt, pt.run(args.steps, args.warmup, 0, flush=True))
-        log(f"gqa4_4k {name}: {res[name]['attn_us']:.1f} us, {100 * res[name]['attn_frac']:.1f}%")
+        _with_ceiling(res[name], dev, pt.bytes, args.steps)
+        log(f"gqa4_4k {name}: {res[name]['attn_us']:.1f} us, {100 * res[name]['attn_frac']:.1f}%; "
+            f"bare read {res[name]['read_us']:.1f} us, {100 * res[name]['read_frac']:.1f}%")
         del pt
         torch.cuda.empty_cache()
     return res

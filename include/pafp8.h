@@ -396,6 +396,27 @@ pafp8_status splitk_combine(const float *part_o, const float *part_lse, int32_t 
                             hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * pafp8_stream_read -- a measurement aid, not a step of the decode path.  The
+ * KV-cache section of "Smaller, faster, safer: running Kimi and GLM at scale"
+ * treats decode attention as bound by the bytes it reads; this call reads
+ * `bytes` of device memory once, with the loads the attention kernels use for
+ * K/V (16 bytes per lane, non-temporal, a wave's next 16 KiB tile in flight
+ * while it consumes the current one), and does nothing else.  Its time is
+ * what the memory system delivers for that many bytes, against which an
+ * HBM-bound kernel of the same size is set beside the published peak.
+ *   src        device, 16-byte aligned, `bytes` readable (not modified)
+ *   bytes      a non-negative multiple of 16384
+ *   work_groups number of 256-thread work-groups (>= 1); they split the
+ *              buffer into equal ranges of 16 KiB tiles
+ *   sink       device uint32 [sink_words], sink_words >= work_groups * 256:
+ *              each thread writes the XOR of the 32-bit words it read, so the
+ *              XOR over sink[0 .. work_groups * 256) is the XOR over src
+ * PAFP8_EINVAL on a bad size or pointer, with nothing launched.
+ * ------------------------------------------------------------------------- */
+pafp8_status pafp8_stream_read(const void *src, int64_t bytes, int32_t work_groups,
+                               uint32_t *sink, int64_t sink_words, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * The device e4m3 codec the kernels use, exposed for conformance testing.
  * pafp8_e4m3_encode: codes[i] = e4m3(x[i]) (rounding as kv_quant_append).
  * pafp8_e4m3_decode: for each code, the value as produced by each of the

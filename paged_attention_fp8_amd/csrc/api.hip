@@ -639,6 +639,26 @@ pafp8_status pafp8_e4m3_decode(const uint8_t *codes, float *out_f32, float *out_
                       "pafp8_e4m3_decode launch");
 }
 
+pafp8_status pafp8_stream_read(const void *src, int64_t bytes, int32_t work_groups,
+                               uint32_t *sink, int64_t sink_words, hipStream_t stream)
+{
+    if (bytes < 0 || bytes % pafp8::kStreamReadTile != 0)
+        return fail(PAFP8_EINVAL, "bytes = %lld is not a non-negative multiple of %lld",
+                    static_cast<long long>(bytes), static_cast<long long>(pafp8::kStreamReadTile));
+    if (work_groups < 1)
+        return fail(PAFP8_EINVAL, "work_groups = %d < 1", work_groups);
+    if (sink_words < static_cast<int64_t>(work_groups) * pafp8::kStreamReadThreads)
+        return fail(PAFP8_EINVAL, "sink holds %lld words; work_groups * %d = %lld needed",
+                    static_cast<long long>(sink_words), pafp8::kStreamReadThreads,
+                    static_cast<long long>(work_groups) * pafp8::kStreamReadThreads);
+    if (sink == nullptr || (bytes > 0 && src == nullptr))
+        return fail(PAFP8_EINVAL, "src or sink is NULL");
+    if (!aligned16(src))
+        return fail(PAFP8_EINVAL, "src must be 16-byte aligned");
+    return hip_status(pafp8::launch_stream_read(src, bytes, work_groups, sink, stream),
+                      "pafp8_stream_read launch");
+}
+
 const char *pafp8_status_string(pafp8_status status)
 {
     switch (status) {

@@ -72,6 +72,13 @@ hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const ui
                             int N, int K, float *y, hipStream_t stream);
 hipError_t launch_int4_pack(const uint8_t *src, uint8_t *dst, int N, int K, hipStream_t stream);
 
+// Measurement: a bare read of bytes (a multiple of kStreamReadTile) by
+// work_groups work-groups of 256 threads; sink holds work_groups * 256 words.
+constexpr int64_t kStreamReadTile = 16384;
+constexpr int kStreamReadThreads = 256;
+hipError_t launch_stream_read(const void *src, int64_t bytes, int work_groups, uint32_t *sink,
+                              hipStream_t stream);
+
 hipError_t launch_e4m3_encode(const float *x, uint8_t *codes, int64_t n, hipStream_t stream);
 hipError_t launch_e4m3_decode(const uint8_t *codes, float *f32, float *via_f16, float *via_bf16,
                               int64_t n, hipStream_t stream);

@@ -1,0 +1,71 @@
+// stream_read.hip -- a bare streaming read of device memory, for measurement.
+// It reads every byte once with the loads the attention kernels use for KV
+// (16 bytes per lane, non-temporal), keeping a wave's next 16 KiB tile in
+// flight while it consumes the current one, and does nothing else.  Its time
+// is what the memory system delivers for that many bytes under the same
+// timing, so an HBM-bound kernel's time can be set beside it as well as
+// beside the published peak.
+#include "pafp8_device.hpp"
+#include "pafp8_internal.hpp"
+
+namespace pafp8 {
+namespace {
+
+constexpr int kReadWaves = 4;
+constexpr int kReadLoads = 16;   // 16-byte loads per lane per tile: 16 KiB per wave
+static_assert(kReadLoads * 64 * 16 == kStreamReadTile, "tile size");
+static_assert(kReadWaves * 64 == kStreamReadThreads, "work-group size");
+
+// Work-group g takes tiles [g * per_group, (g + 1) * per_group) of the
+// buffer; its waves take every kReadWaves-th of them.  Each thread stores the
+// XOR of the 32-bit words it read, so the XOR over sink equals the XOR over
+// the buffer.
+__global__ __launch_bounds__(kReadWaves * 64) void stream_read_kernel(const uint8_t *src,
+                                                                       int64_t tiles,
+                                                                       int64_t per_group,
+                                                                       uint32_t *sink)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * per_group;
+    const int64_t end = first + per_group < tiles ? first + per_group : tiles;
+    uint32_t acc = 0;
+    u32x4 cur[kReadLoads], nxt[kReadLoads];
+    auto load = [&](u32x4 *r, int64_t t) {
+        const uint8_t *base = src + t * (kReadLoads * 1024) + lane * 16;
+#pragma unroll
+        for (int k = 0; k < kReadLoads; ++k)
+            r[k] = load16_stream(base + k * 1024);
+    };
+    auto fold = [&](const u32x4 *r) {
+#pragma unroll
+        for (int k = 0; k < kReadLoads; ++k)
+            acc ^= r[k][0] ^ r[k][1] ^ r[k][2] ^ r[k][3];
+    };
+    int64_t t = first + wave;
+    if (t < end)
+        load(cur, t);
+    for (; t < end; t += 2 * kReadWaves) {
+        if (t + kReadWaves < end)
+            load(nxt, t + kReadWaves);
+        fold(cur);
+        if (t + 2 * kReadWaves < end)
+            load(cur, t + 2 * kReadWaves);
+        if (t + kReadWaves < end)
+            fold(nxt);
+    }
+    sink[static_cast<int64_t>(blockIdx.x) * (kReadWaves * 64) + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void *src, int64_t bytes, int work_groups, uint32_t *sink,
+                              hipStream_t stream)
+{
+    const int64_t tiles = bytes / kStreamReadTile;
+    const int64_t per = (tiles + work_groups - 1) / work_groups;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(work_groups), dim3(kReadWaves * 64), 0, stream,
+                       static_cast<const uint8_t *>(src), tiles, per, sink);
+    return hipGetLastError();
+}
+
+}  // namespace pafp8

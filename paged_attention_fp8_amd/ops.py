@@ -66,6 +66,7 @@ _SIGNATURES = {
     "paged_decode_attn_fp8_noalloc": (_I32, [_CP, _BP, _V, _I32, _F, _I32, _V, _V, _V]),
     "pafp8_noalloc_scratch_bytes": (_SZ, []),
     "splitk_combine": (_I32, [_V, _V, _I32, _I32, _I32, _I32, _V, _V, _V, _V]),
+    "pafp8_stream_read": (_I32, [_V, _I64, _I32, _V, _I64, _V]),
     "pafp8_e4m3_encode": (_I32, [_V, _V, _I64, _V]),
     "pafp8_e4m3_decode": (_I32, [_V, _V, _V, _V, _I64, _V]),
     "pafp8_status_string": (ctypes.c_char_p, [_I32]),
@@ -512,6 +513,26 @@ def splitk_combine(part_o: torch.Tensor, part_lse: torch.Tensor,
                                 _ptr(req_status), out.data_ptr(), lse.data_ptr(), _stream(dev)),
            "splitk_combine")
     return out, lse
+
+
+STREAM_READ_TILE = 16384
+STREAM_READ_THREADS = 256
+
+
+def stream_read(buf: torch.Tensor, work_groups: int = 256,
+                sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Measurement aid: one bare non-temporal read of all of buf's bytes
+    (a multiple of 16 KiB) by work_groups work-groups; returns the sink of
+    per-thread XORs (int32 [work_groups * 256]), whose XOR is buf's."""
+    if buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(work_groups * STREAM_READ_THREADS, dtype=torch.int32, device=buf.device)
+    _need(sink, "sink", torch.int32, None, buf.device)
+    _check(lib().pafp8_stream_read(buf.data_ptr(), nbytes, work_groups, sink.data_ptr(),
+                                   sink.numel(), _stream(buf.device)), "pafp8_stream_read")
+    return sink
 
 
 def e4m3_encode(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

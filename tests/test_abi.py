@@ -177,6 +177,15 @@ def test_other_entry_points_validate_without_gpu(L):
     assert L.int4_pack_weights(None, 16, 512, 64, None) == 1
     assert L.int4_pack_weights(66, 16, 512, 64, None) == 1              # source not 4-byte aligned
     assert L.pafp8_e4m3_encode(None, None, -1, None) == 1
+    # the bare read (a measurement aid): size, sink, pointers, alignment
+    assert L.pafp8_stream_read(64, 16384 + 16, 1, 64, 256, None) == 1   # not whole 16 KiB tiles
+    assert L.pafp8_stream_read(64, -16384, 1, 64, 256, None) == 1
+    assert L.pafp8_stream_read(64, 16384, 0, 64, 256, None) == 1        # no work-groups
+    assert L.pafp8_stream_read(64, 16384, 2, 64, 511, None) == 1        # sink one word short
+    assert b"512" in L.pafp8_last_error()
+    assert L.pafp8_stream_read(None, 16384, 1, 64, 256, None) == 1
+    assert L.pafp8_stream_read(64, 16384, 1, None, 256, None) == 1
+    assert L.pafp8_stream_read(72, 16384, 1, 64, 256, None) == 1        # src not 16-byte aligned
     # empty work is OK and launches nothing
     assert L.pafp8_e4m3_encode(None, None, 0, None) == 0
     assert _attn(L, _cache(), _batch(batch=0)) == 0
