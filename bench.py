@@ -334,6 +334,8 @@ def long_context(args, dev):
         "default_splits_attn_us": 1e3 * dms,
         "default_splits_attn_frac": pc.bytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
+    res.update(read_ceiling(dev, pc.bytes, args.steps))
+    res["attn_over_read"] = res["attn_us"] / res["read_us"]
     del pc, rc, rn, rd
     torch.cuda.empty_cache()
     ps = Point(w.batch, ops.KV_FP8_E4M3, dev, workload=w)
@@ -381,9 +383,13 @@ def handoff(args, dev):
     nbytes = 2 * elems * (2 + 1) + B * (T // w.page_size) * 4 + 2 * B * 4 + 2 * w.kv_heads * 4
     del cache, inp, k, v
     torch.cuda.empty_cache()
-    return {"workload": "8 prompts x 8192 bf16 tokens, 8 KV heads, head_dim 128, 64-token pages -> e4m3",
-            "kernel": "kv_fill_kernel<e4m3, 128>", "us": 1e3 * ms, "algorithmic_bytes": nbytes,
-            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    res = {"workload": "8 prompts x 8192 bf16 tokens, 8 KV heads, head_dim 128, 64-token pages -> e4m3",
+           "kernel": "kv_fill_kernel<e4m3, 128>", "us": 1e3 * ms, "algorithmic_bytes": nbytes,
+           "GBps": nbytes / (ms * 1e-3) / 1e9, "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    # the bare stream of the same shape: read the 2-byte source, write half
+    res.update(_read_write_ceiling(_ceiling(dev), 2 * elems * 2, 2, args.steps, args.warmup))
+    res["over_read_write"] = res["us"] / res["read_write_us"]
+    return res
 
 
 def decode_loop(args, dev):
@@ -472,8 +478,14 @@ def int4_decode(args, dev):
                     "TFLOPs": 2.0 * M * N * K / (ms * 1e-3) / 1e12})
     del ws, ss
     torch.cuda.empty_cache()
+    # the bare read of one matrix's weights and scales, 8 disjoint copies
+    # back to back, timed like the GEMVs
+    wbytes = N * K // 2 + (K // 128) * N * 2
+    ceil = _ceiling(dev).back_to_back(wbytes, layers, args.steps)
+    for r in res:
+        r["over_read"] = r["us_per_matrix"] / ceil["read_us"]
     return {"workload": "8 int4 weight matrices 28672 x 8192 (bf16 scale per 128 inputs), "
-                        "bf16 activations, fp32 output",
+                        "bf16 activations, fp32 output", "read_ceiling": ceil,
             "kernel": "int4_gemv_row_kernel (1 row), int4_gemv_kernel (2-16 rows), "
                       "int4_gemv_wide_kernel (17-64 rows)", "points": res}
 
@@ -499,6 +511,7 @@ def fp8_vs_bf16(args, dev):
             ms = statistics.mean(r["attn_ms"])
             res = {"attn_us": 1e3 * ms, "attn_GBps": pt.bytes / (ms * 1e-3) / 1e9,
                    "attn_frac": pt.bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "splits": r["splits"]}
+            _with_ceiling(res, dev, pt.bytes, args.steps)
             if mode == 0:
                 runs[name] = dict(res, out=r["out"].clone(), lse=r["lse"].clone())
             else:
@@ -577,15 +590,79 @@ class ReadCeiling:
                             "read_frac": n / (best[0] * 1e-6) / 1e9 / PEAK_HBM_GBS}
         return dict(self.done[n])
 
+    def back_to_back(self, nbytes, count, steps):
+        """count bare reads of nbytes each over disjoint slices of the
+        buffer, launched back to back and timed together (no flush: the
+        slices together exceed the MALL), per-launch mean; best grid."""
+        import torch
+        t = self.ops.STREAM_READ_TILE
+        n = nbytes // t * t
+        if n * count > self.CAPACITY:
+            raise ValueError("back_to_back: %d x %d bytes exceed the buffer" % (count, n))
+        views = [self.buf[i * n:(i + 1) * n] for i in range(count)]
+        best = None
+        for g in self.GRIDS:
+            for v in views:
+                self.ops.stream_read(v, g, self.sink)
+            settle()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for a, b in ev:
+                a.record()
+                for v in views:
+                    self.ops.stream_read(v, g, self.sink)
+                b.record()
+            torch.cuda.synchronize()
+            us = 1e3 * statistics.mean(a.elapsed_time(b) for a, b in ev) / count
+            if best is None or us < best[0]:
+                best = (us, g)
+        return {"read_us": best[0], "read_work_groups": best[1], "read_bytes": n,
+                "read_frac": n / (best[0] * 1e-6) / 1e9 / PEAK_HBM_GBS}
+
+
+def _read_write_ceiling(rc, src_bytes, ratio, steps, warmup):
+    """The bare read of src_bytes with a write of src_bytes / ratio
+    (ops.stream_read_write), launched and timed like the hand-off: back to
+    back, HIP events per launch, no flush; best grid."""
+    import torch
+    t = rc.ops.STREAM_READ_TILE
+    n = src_bytes // t * t
+    src, dst = rc.buf[:n], rc.buf[rc.CAPACITY - n // ratio:]
+    if n + n // ratio > rc.CAPACITY:
+        raise ValueError("read_write: %d bytes exceed the buffer" % n)
+    best = None
+    for g in rc.GRIDS:
+        rc.ops.stream_read_write(src, dst, g)
+        settle()
+        for _ in range(warmup):
+            rc.ops.stream_read_write(src, dst, g)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record()
+            rc.ops.stream_read_write(src, dst, g)
+            b.record()
+        torch.cuda.synchronize()
+        us = 1e3 * statistics.mean(a.elapsed_time(b) for a, b in ev)
+        if best is None or us < best[0]:
+            best = (us, g)
+    moved = n + n // ratio
+    return {"read_write_us": best[0], "read_write_work_groups": best[1], "read_bytes": n,
+            "write_bytes": n // ratio, "read_write_frac": moved / (best[0] * 1e-6) / 1e9 / PEAK_HBM_GBS}
+
 
 _read_ceilings = {}
 
 
-def read_ceiling(dev, nbytes, steps):
-    """ReadCeiling figures for nbytes, with attn_us to be set beside them."""
+def _ceiling(dev):
     if dev not in _read_ceilings:
         _read_ceilings[dev] = ReadCeiling(dev)
-    return _read_ceilings[dev](nbytes, steps)
+    return _read_ceilings[dev]
+
+
+def read_ceiling(dev, nbytes, steps):
+    """ReadCeiling figures for nbytes, with attn_us to be set beside them."""
+    return _ceiling(dev)(nbytes, steps)
 
 
 def _with_ceiling(entry, dev, nbytes, steps):

@@ -416,6 +416,19 @@ pafp8_status splitk_combine(const float *part_o, const float *part_lse, int32_t 
 pafp8_status pafp8_stream_read(const void *src, int64_t bytes, int32_t work_groups,
                                uint32_t *sink, int64_t sink_words, hipStream_t stream);
 
+/* pafp8_stream_read_write -- the same read of src_bytes, and a write of
+ * dst_bytes = src_bytes / R (R = 1, 2 or 4) to dst with plain 16-byte stores:
+ * the bare stream behind a kernel that reads and writes in that ratio (the
+ * prefill-to-decode quantiser reads 2 bytes and writes 1 per element).
+ * Lane l's k-th store for 16 KiB tile t goes to dst offset
+ * t * 16384 / R + k * 1024 + 16 l and is the XOR of the 16-byte words it read
+ * at tile offsets (kR + q) * 1024 + 16 l, q < R.
+ *   src  device, 16-byte aligned, src_bytes a non-negative multiple of 16384
+ *   dst  device, 16-byte aligned, dst_bytes written (0 when src_bytes is 0)
+ * PAFP8_EINVAL on a bad size, ratio or pointer, with nothing launched. */
+pafp8_status pafp8_stream_read_write(const void *src, int64_t src_bytes, void *dst, int64_t dst_bytes,
+                                     int32_t work_groups, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * The device e4m3 codec the kernels use, exposed for conformance testing.
  * pafp8_e4m3_encode: codes[i] = e4m3(x[i]) (rounding as kv_quant_append).

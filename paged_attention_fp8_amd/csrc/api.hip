@@ -659,6 +659,30 @@ pafp8_status pafp8_stream_read(const void *src, int64_t bytes, int32_t work_grou
                       "pafp8_stream_read launch");
 }
 
+pafp8_status pafp8_stream_read_write(const void *src, int64_t src_bytes, void *dst, int64_t dst_bytes,
+                                     int32_t work_groups, hipStream_t stream)
+{
+    if (src_bytes < 0 || src_bytes % pafp8::kStreamReadTile != 0)
+        return fail(PAFP8_EINVAL, "src_bytes = %lld is not a non-negative multiple of %lld",
+                    static_cast<long long>(src_bytes), static_cast<long long>(pafp8::kStreamReadTile));
+    const int ratio = dst_bytes > 0 && src_bytes % dst_bytes == 0 ? static_cast<int>(src_bytes / dst_bytes) : 0;
+    if (src_bytes > 0 && ratio != 1 && ratio != 2 && ratio != 4)
+        return fail(PAFP8_EINVAL, "dst_bytes = %lld: src_bytes must be 1, 2 or 4 times it",
+                    static_cast<long long>(dst_bytes));
+    if (src_bytes == 0 && dst_bytes != 0)
+        return fail(PAFP8_EINVAL, "dst_bytes = %lld with src_bytes = 0", static_cast<long long>(dst_bytes));
+    if (work_groups < 1)
+        return fail(PAFP8_EINVAL, "work_groups = %d < 1", work_groups);
+    if (src_bytes == 0)
+        return ok();
+    if (src == nullptr || dst == nullptr)
+        return fail(PAFP8_EINVAL, "src or dst is NULL");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(PAFP8_EINVAL, "src and dst must be 16-byte aligned");
+    return hip_status(pafp8::launch_stream_read_write(src, src_bytes, dst, ratio, work_groups, stream),
+                      "pafp8_stream_read_write launch");
+}
+
 const char *pafp8_status_string(pafp8_status status)
 {
     switch (status) {

@@ -78,6 +78,9 @@ constexpr int64_t kStreamReadTile = 16384;
 constexpr int kStreamReadThreads = 256;
 hipError_t launch_stream_read(const void *src, int64_t bytes, int work_groups, uint32_t *sink,
                               hipStream_t stream);
+// ... and write src_bytes / ratio bytes to dst (ratio 1, 2 or 4)
+hipError_t launch_stream_read_write(const void *src, int64_t src_bytes, void *dst, int ratio,
+                                    int work_groups, hipStream_t stream);
 
 hipError_t launch_e4m3_encode(const float *x, uint8_t *codes, int64_t n, hipStream_t stream);
 hipError_t launch_e4m3_decode(const uint8_t *codes, float *f32, float *via_f16, float *via_bf16,

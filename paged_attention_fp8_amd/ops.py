@@ -67,6 +67,7 @@ _SIGNATURES = {
     "pafp8_noalloc_scratch_bytes": (_SZ, []),
     "splitk_combine": (_I32, [_V, _V, _I32, _I32, _I32, _I32, _V, _V, _V, _V]),
     "pafp8_stream_read": (_I32, [_V, _I64, _I32, _V, _I64, _V]),
+    "pafp8_stream_read_write": (_I32, [_V, _I64, _V, _I64, _I32, _V]),
     "pafp8_e4m3_encode": (_I32, [_V, _V, _I64, _V]),
     "pafp8_e4m3_decode": (_I32, [_V, _V, _V, _V, _I64, _V]),
     "pafp8_status_string": (ctypes.c_char_p, [_I32]),
@@ -533,6 +534,19 @@ def stream_read(buf: torch.Tensor, work_groups: int = 256,
     _check(lib().pafp8_stream_read(buf.data_ptr(), nbytes, work_groups, sink.data_ptr(),
                                    sink.numel(), _stream(buf.device)), "pafp8_stream_read")
     return sink
+
+
+def stream_read_write(src: torch.Tensor, dst: torch.Tensor, work_groups: int = 256) -> torch.Tensor:
+    """Measurement aid: one bare read of all of src's bytes (a multiple of
+    16 KiB) and a write of all of dst's (1/1, 1/2 or 1/4 of src's) by
+    work_groups work-groups; returns dst."""
+    for t, n in ((src, "src"), (dst, "dst")):
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous device tensor")
+    _check(lib().pafp8_stream_read_write(src.data_ptr(), src.numel() * src.element_size(), dst.data_ptr(),
+                                         dst.numel() * dst.element_size(), work_groups,
+                                         _stream(src.device)), "pafp8_stream_read_write")
+    return dst
 
 
 def e4m3_encode(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

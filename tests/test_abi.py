@@ -186,6 +186,15 @@ def test_other_entry_points_validate_without_gpu(L):
     assert L.pafp8_stream_read(None, 16384, 1, 64, 256, None) == 1
     assert L.pafp8_stream_read(64, 16384, 1, None, 256, None) == 1
     assert L.pafp8_stream_read(72, 16384, 1, 64, 256, None) == 1        # src not 16-byte aligned
+    assert L.pafp8_stream_read_write(64, 16384, 64, 16384 // 3, 1, None) == 1   # ratio not 1, 2, 4
+    assert L.pafp8_stream_read_write(64, 16384, 64, 16384 // 8, 1, None) == 1
+    assert L.pafp8_stream_read_write(64, 16384 + 16, 64, 8200, 1, None) == 1
+    assert L.pafp8_stream_read_write(64, 16384, 64, 0, 1, None) == 1
+    assert L.pafp8_stream_read_write(64, 0, 64, 16, 1, None) == 1
+    assert L.pafp8_stream_read_write(64, 16384, 64, 8192, 0, None) == 1
+    assert L.pafp8_stream_read_write(64, 16384, None, 8192, 1, None) == 1
+    assert L.pafp8_stream_read_write(64, 16384, 72, 8192, 1, None) == 1       # dst not 16-byte aligned
+    assert L.pafp8_stream_read_write(None, 0, None, 0, 1, None) == 0           # nothing to do
     # empty work is OK and launches nothing
     assert L.pafp8_e4m3_encode(None, None, 0, None) == 0
     assert _attn(L, _cache(), _batch(batch=0)) == 0
