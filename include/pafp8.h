@@ -268,7 +268,8 @@ pafp8_status int4_gemv(const uint16_t *x, int32_t M, const uint8_t *w_packed, co
  * pages; each chunk produces a partial (o, lse) in the workspace and
  * splitk_combine merges them.  pafp8_default_num_splits picks S so that
  * batch * num_kv_heads * S is about one work-group per CU, with splits of at
- * least 1024 tokens (num_cus <= 0: query the current device).
+ * least 512 tokens and none for max_pages_per_req * page_size < 2048 tokens
+ * (num_cus <= 0: query the current device).
  *
  * Balanced partition, num_splits = -W (1 <= W <= 65536): for each KV head the
  * pages of all live requests, in request order, form one sequence of T pages

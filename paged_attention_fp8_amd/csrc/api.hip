@@ -465,14 +465,15 @@ int32_t pafp8_default_num_splits(int32_t batch, int32_t num_kv_heads, int32_t ma
         num_cus = device_cu_count();
     // about one work-group per CU (measured best from 4 to 64 requests of
     // 16k-256k tokens on MI355X: more, shorter splits add combine traffic and
-    // per-split start-up), without splits shorter than 1024 tokens (one
-    // request of 16k tokens: 16 splits took 16 us, 32 splits 20 us)
+    // per-split start-up), without splits shorter than 512 tokens, and no
+    // split at all below 2048 tokens.  One request on MI355X, e4m3 (bf16):
+    // 16k tokens 16.9 us at 16 splits, 16.6 at 32 (21.9, 20.7); 4k tokens 15.6
+    // at 4, 13.5 at 8 (19.9, 15.6); 1k tokens 11.9 whole, 13.0 in two halves
+    // (the combine launch costs more than the halves save).
     const int64_t units = static_cast<int64_t>(batch) * num_kv_heads;
     int64_t S = (num_cus + units - 1) / units;
     const int64_t tokens = static_cast<int64_t>(max_pages_per_req) * page_size;
-    int64_t s_max = tokens / 1024;
-    if (s_max < 1)
-        s_max = 1;
+    int64_t s_max = tokens >= 2048 ? tokens / 512 : 1;
     if (S > s_max)
         S = s_max;
     if (S > max_pages_per_req)

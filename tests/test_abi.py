@@ -82,11 +82,14 @@ def test_default_split_choice(L):
     assert L.pafp8_default_num_splits(16, 8, 256, 64, 256) == 2
     assert L.pafp8_default_num_splits(8, 8, 256, 64, 256) == 4
     assert L.pafp8_default_num_splits(4, 8, 4096, 64, 256) == 8
-    # no split shorter than 1024 tokens
-    assert L.pafp8_default_num_splits(1, 8, 256, 64, 256) == 16
+    # no split shorter than 512 tokens, and none below 2048 tokens
+    assert L.pafp8_default_num_splits(1, 8, 256, 64, 256) == 32
+    assert L.pafp8_default_num_splits(1, 8, 64, 64, 256) == 8
+    assert L.pafp8_default_num_splits(1, 8, 32, 64, 256) == 4
     assert L.pafp8_default_num_splits(1, 4, 16, 16, 256) == 1
-    assert L.pafp8_default_num_splits(2, 8, 64, 16, 256) == 1
-    assert L.pafp8_default_num_splits(2, 8, 128, 16, 256) == 2
+    assert L.pafp8_default_num_splits(2, 8, 64, 16, 256) == 1       # 1024 tokens: whole
+    assert L.pafp8_default_num_splits(1, 8, 31, 64, 256) == 1       # 1984 tokens: whole
+    assert L.pafp8_default_num_splits(2, 8, 128, 16, 256) == 4      # 2048 tokens: 512 each
 
 
 def _cache(**kw):
