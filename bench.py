@@ -28,7 +28,10 @@ hand-off (kv_quant_fill of 8 prompts of 8,192 tokens), a continuous decode
 loop with admission under the same 2 GiB budget (e4m3 vs bf16), INT4 weight
 streaming (int4_gemv over 940 MB of int4 weights at 1-64 rows), and the
 ragged batch (32 requests of 1k-32k tokens) on e4m3 and bf16 caches from one
-bf16 source.  --only runs named extras alone (for profiling one workload).
+bf16 source.  Beside each HBM-bound point stands the bare stream of its bytes
+(pafp8_stream_read, or pafp8_stream_read_write for the hand-off), launched and
+timed the same way: what the memory system delivers at that size.  --only
+runs named extras alone (for profiling one workload).
 cpu_baseline times the CPU oracle on a bounded sample of the same batch.
 """
 from __future__ import annotations
