@@ -230,16 +230,9 @@ struct MfmaCtx {
 
 // 16-byte KV loads.  Every K and V line a tile touches is consumed whole by
 // the wave's own load steps, so the loads stream past the caches.
-#ifndef PAFP8_KV_STREAM
-#define PAFP8_KV_STREAM 1
-#endif
-template <bool STREAM>
 __device__ __forceinline__ u32x4 load16_kv(const void *p)
 {
-    if constexpr (STREAM)
-        return load16_stream(p);
-    else
-        return load16(p);
+    return load16_stream(p);
 }
 
 // Pool block layout (per page and KV head; see include/pafp8.h): blocks are
@@ -265,7 +258,7 @@ __device__ __forceinline__ void mfma_load_k(MfmaTile<BF16, D> &t, const MfmaCtx<
         for (int j = 0; j < G_::NJ; ++j)
 #pragma unroll
             for (int l = 0; l < G_::KL; ++l)
-                t.k[j][l] = load16_kv<PAFP8_KV_STREAM != 0>(kp + (j * G_::KL + l) * 1024);
+                t.k[j][l] = load16_kv(kp + (j * G_::KL + l) * 1024);
     } else {
         // the page is the segment; lane group r/4 reads token group s of its page
         const int P = 1 << c.log2_page;
@@ -278,7 +271,7 @@ __device__ __forceinline__ void mfma_load_k(MfmaTile<BF16, D> &t, const MfmaCtx<
         for (int j = 0; j < G_::NJ; ++j)
 #pragma unroll
             for (int l = 0; l < G_::KL; ++l)
-                t.k[j][l] = load16_kv<PAFP8_KV_STREAM != 0>(kp + ((j * G_::KL + l) * 256 << log2_ns));
+                t.k[j][l] = load16_kv(kp + ((j * G_::KL + l) * 256 << log2_ns));
     }
 }
 
@@ -294,7 +287,7 @@ __device__ __forceinline__ void mfma_load_v(MfmaTile<BF16, D> &t, const MfmaCtx<
                             seg * (G_::TT * D * G_::E) + (c.lane_r * G_::TT + c.lane_g * G_::TPG) * G_::E;
 #pragma unroll
         for (int dt = 0; dt < G_::NDT; ++dt)
-            t.v[dt] = load16_kv<PAFP8_KV_STREAM != 0>(vp + dt * 16 * G_::TT * G_::E);
+            t.v[dt] = load16_kv(vp + dt * 16 * G_::TT * G_::E);
     } else {
         const int P = 1 << c.log2_page;
         const int vslot = static_cast<int>((T0 + c.lane_g * G_::TPG) & (P - 1));
@@ -302,7 +295,7 @@ __device__ __forceinline__ void mfma_load_v(MfmaTile<BF16, D> &t, const MfmaCtx<
                             ((c.lane_r << c.log2_page) + vslot) * G_::E;
 #pragma unroll
         for (int dt = 0; dt < G_::NDT; ++dt)
-            t.v[dt] = load16_kv<PAFP8_KV_STREAM != 0>(vp + ((dt * 16 * G_::E) << c.log2_page));
+            t.v[dt] = load16_kv(vp + ((dt * 16 * G_::E) << c.log2_page));
     }
 }
 

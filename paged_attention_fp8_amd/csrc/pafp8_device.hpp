@@ -101,17 +101,10 @@ __device__ __forceinline__ u32x4 load16(const void *p)
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
-// KV data is read exactly once per call: stream it past the caches.
-#ifndef PAFP8_KV_NT_LOADS
-#define PAFP8_KV_NT_LOADS 1
-#endif
+// Data read exactly once per call (KV, weights): stream it past the caches.
 __device__ __forceinline__ u32x4 load16_stream(const void *p)
 {
-#if PAFP8_KV_NT_LOADS
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-#else
-    return *reinterpret_cast<const u32x4 *>(p);
-#endif
 }
 
 __device__ __forceinline__ void store16(void *p, u32x4 v)
