@@ -22,6 +22,7 @@ requests and one), the bf16 twin (32 requests: the same KV bytes), and the
 extras -- the concurrency sweep of the pages' decode table (1/8/16/32/64
 requests, e4m3 and bf16, each step after a 1 GiB read of other memory so
 that no point runs out of the MALL), the 4k-token / 16-token-page workload,
+one query head per KV head (the vector kernel),
 the long-context point (4 requests of 262,144 tokens in 64 splits: check
 overhead, and the batch with one stale request), the prefill-to-decode
 hand-off (kv_quant_fill of 8 prompts of 8,192 tokens), a continuous decode
@@ -730,6 +731,28 @@ def gqa4_4k(args, dev):
     return res
 
 
+def mha_g1(args, dev):
+    """One query head per KV head (the vector kernel, no matrix cores): 8
+    requests of 16,384 tokens, 32 heads, head_dim 128, 64-token pages,
+    e4m3 and bf16, library-default splits, flushed caches, each beside the
+    bare read of its bytes."""
+    import torch
+    from paged_attention_fp8_amd import inputs as I
+    from paged_attention_fp8_amd import ops
+    w = I.Workload("mha_g1_16k_b8", 8, 32, 32, 128, 64, 16384, 16384, pool_factor=1.0)
+    res = {"workload": "mha_g1_16k_b8: 8 requests x 16384 tokens, 32 query heads = 32 KV heads, head_dim 128, "
+                       "64-token pages, flushed caches"}
+    for kv_dtype, name in ((ops.KV_FP8_E4M3, "e4m3"), (ops.KV_BF16, "bf16")):
+        pt = Point(w.batch, kv_dtype, dev, workload=w)
+        res[name] = _attn_point(pt, pt.run(args.steps, args.warmup, 0, flush=True))
+        _with_ceiling(res[name], dev, pt.bytes, args.steps)
+        log(f"mha_g1 {name}: {res[name]['attn_us']:.1f} us, {100 * res[name]['attn_frac']:.1f}%; "
+            f"bare read {res[name]['read_us']:.1f} us, {100 * res[name]['read_frac']:.1f}%")
+        del pt
+        torch.cuda.empty_cache()
+    return res
+
+
 def _pmc_values(directory, counter, kernel_substr):
     """Per-dispatch values of one counter for kernels whose name contains
     kernel_substr, from a rocprofv3 --pmc csv run directory."""
@@ -982,6 +1005,7 @@ def copy_calibration():
 EXTRAS = {
     "concurrency_sweep": concurrency_sweep,
     "gqa4_4k": gqa4_4k,
+    "mha_g1": mha_g1,
     "long_context": long_context,
     "prefill_handoff": handoff,
     "decode_loop": decode_loop,

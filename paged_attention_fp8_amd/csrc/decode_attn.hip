@@ -999,28 +999,34 @@ __device__ __forceinline__ int vec_range(const AttnParams &p, VecSmem<D> &sm, in
     // segment of the block layout: min(page, 64 bytes / element) tokens
     const int log2_seg = p.log2_page < (BF16 ? 5 : 6) ? p.log2_page : (BF16 ? 5 : 6);
 
-    for (int i = wave; i < ntiles; i += kWaves) {
-        const int64_t T0 = rng.t0 + static_cast<int64_t>(i) * V_::TT;
-        const TilePages pg = pages_ok(fetch_pages(row, T0, 16, p.log2_page, rng.p_last),
-                                      p.num_pages, bad);
+    // A wave's tiles are i = wave, wave + kWaves, ...  On e4m3 pools the next
+    // tile's loads go out before the current tile's arithmetic.  Past the
+    // last tile that prefetch reads the current tile again (just fetched, so
+    // it comes from the caches): loads stay unconditional, which keeps the
+    // compiler's wait counts exact across the loop.  A bf16 tile holds twice
+    // the registers; two of them cost more occupancy than the overlap gains
+    // (measured), so bf16 pools take one tile at a time.
+    struct Tile {
+        u32x4 k[V_::KL];
+        u32x4 v[V_::ROWS][4][V_::VL];
+    };
+    const int q = lane >> 4;
+    constexpr int LOG2_TG = BF16 ? 3 : 4;     // tokens per K token group: 16 / e
+    constexpr int KLc = V_::KL / 4;           // chunks per quarter row
+    const int log2_ns = log2_seg - LOG2_TG;
+    auto issue = [&](int64_t T0, const TilePages &pg, Tile &t) {
         // K row of token T0 + lane: token TG*sub + 4j + a of its segment keeps
         // chunk qc*KLc + l at chunk ((j*KLc + l)*4 + qc)*(4*NS) + 4*sub + a
-        const int q = lane >> 4;
         const int kslot = static_cast<int>((T0 + q * 16) & (P - 1)) + (lane & 15);
-        constexpr int LOG2_TG = BF16 ? 3 : 4;     // tokens per K token group: 16 / e
-        constexpr int KLc = V_::KL / 4;           // chunks per quarter row
-        const int log2_ns = log2_seg - LOG2_TG;
         const int ku = kslot & ((1 << log2_seg) - 1);
         const int kw = ku & ((1 << LOG2_TG) - 1);
         const uint8_t *kp = k_head + static_cast<int64_t>(select4(q, pg)) * page_bytes +
                             (kslot >> log2_seg) * ((D * V_::E) << log2_seg) +
                             ((((kw >> 2) * KLc * 4) << (2 + log2_ns)) + ((ku >> LOG2_TG) << 2) + (kw & 3)) * 16;
-        u32x4 kr[V_::KL];
 #pragma unroll
         for (int e = 0; e < V_::KL; ++e)
-            kr[e] = load16_stream(kp + ((((e % KLc) * 4 + e / KLc) << (2 + log2_ns)) * 16));
+            t.k[e] = load16_stream(kp + ((((e % KLc) * 4 + e / KLc) << (2 + log2_ns)) * 16));
         // V: rows lane + 64*r, four 16-token runs; a segment is [D][tokens]
-        u32x4 vr[V_::ROWS][4][V_::VL];
 #pragma unroll
         for (int r = 0; r < V_::ROWS; ++r)
 #pragma unroll
@@ -1031,14 +1037,16 @@ __device__ __forceinline__ int vec_range(const AttnParams &p, VecSmem<D> &sm, in
                                      (vslot & ((1 << log2_seg) - 1))) * V_::E;
 #pragma unroll
                 for (int e = 0; e < V_::VL; ++e)
-                    vr[r][qq][e] = load16_stream(vp + 16 * e);
+                    t.v[r][qq][e] = load16_stream(vp + 16 * e);
             }
+    };
+    auto consume = [&](int64_t T0, const Tile &t) {
         // score of token T0 + lane
-        float sc = 0.f;
         constexpr int PER = BF16 ? 8 : 16;  // elements per 16-byte load
+        float sc = 0.f;
 #pragma unroll
         for (int e = 0; e < V_::KL; ++e)
-            sc = dot16<BF16>(kr[e], &sm.q[e * PER], sc);
+            sc = dot16<BF16>(t.k[e], &sm.q[e * PER], sc);
         const bool valid = T0 + lane < rng.t1;
         sc = valid ? sc : kNegInf;
         const float mx = wave_max(sc);
@@ -1058,7 +1066,7 @@ __device__ __forceinline__ int vec_range(const AttnParams &p, VecSmem<D> &sm, in
                 const int nv = nv64 <= 0 ? 0 : (nv64 >= 16 ? 16 : static_cast<int>(nv64));
 #pragma unroll
                 for (int e = 0; e < V_::VL; ++e) {
-                    u32x4 w = vr[r][qq][e];
+                    u32x4 w = t.v[r][qq][e];
                     if (nv < 16)
                         w = keep_bytes(w, BF16 ? (nv - 8 * e) * 2 : nv);
                     const float *ps = &sm.p[wave][qq * 16 + e * PER];
@@ -1076,6 +1084,40 @@ __device__ __forceinline__ int vec_range(const AttnParams &p, VecSmem<D> &sm, in
             acc[r] = a;
         }
         __builtin_amdgcn_wave_barrier();
+    };
+
+    if constexpr (BF16) {
+        for (int i = wave; i < ntiles; i += kWaves) {
+            const int64_t T0 = rng.t0 + static_cast<int64_t>(i) * V_::TT;
+            const TilePages pg = pages_ok(fetch_pages(row, T0, 16, p.log2_page, rng.p_last), p.num_pages, bad);
+            Tile t;
+            issue(T0, pg, t);
+            consume(T0, t);
+        }
+    } else if (wave < ntiles) {
+        const int64_t stride = static_cast<int64_t>(kWaves) * V_::TT;
+        int i = wave;
+        int64_t T0 = rng.t0 + static_cast<int64_t>(i) * V_::TT;
+        TilePages pg = pages_ok(fetch_pages(row, T0, 16, p.log2_page, rng.p_last), p.num_pages, bad);
+        TilePages pgn = fetch_pages(row, T0 + stride, 16, p.log2_page, rng.p_last);
+        Tile ta, tb;
+        issue(T0, pg, ta);
+        // one step: tile i is in `cur`; the next (or tile i again) into `nxt`
+        auto step = [&](Tile &cur, Tile &nxt) {
+            const bool more = i + kWaves < ntiles;
+            TilePages pn = pg;
+            if (more)
+                pn = pages_ok(pgn, p.num_pages, bad);
+            pgn = fetch_pages(row, T0 + 2 * stride, 16, p.log2_page, rng.p_last);
+            issue(more ? T0 + stride : T0, pn, nxt);
+            consume(T0, cur);
+            i += kWaves;
+            T0 += stride;
+            pg = pn;
+            return more;
+        };
+        while (step(ta, tb) && step(tb, ta)) {
+        }
     }
     l = wave_sum(l);
     if (lane == 0) {
