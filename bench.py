@@ -22,7 +22,7 @@ requests and one), the bf16 twin (32 requests: the same KV bytes), and the
 extras -- the concurrency sweep of the pages' decode table (1/8/16/32/64
 requests, e4m3 and bf16, each step after a 1 GiB read of other memory so
 that no point runs out of the MALL), the 4k-token / 16-token-page workload,
-one query head per KV head (the vector kernel),
+one query head per KV head (8 x 16k tokens, 32 heads),
 the long-context point (4 requests of 262,144 tokens in 64 splits: check
 overhead, and the batch with one stale request), the prefill-to-decode
 hand-off (kv_quant_fill of 8 prompts of 8,192 tokens), a continuous decode
@@ -732,7 +732,7 @@ def gqa4_4k(args, dev):
 
 
 def mha_g1(args, dev):
-    """One query head per KV head (the vector kernel, no matrix cores): 8
+    """One query head per KV head (one live MFMA column of the group): 8
     requests of 16,384 tokens, 32 heads, head_dim 128, 64-token pages,
     e4m3 and bf16, library-default splits, flushed caches, each beside the
     bare read of its bytes."""

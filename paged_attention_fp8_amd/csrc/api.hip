@@ -248,13 +248,13 @@ pafp8_status attn_impl(const pafp8_cache *cache, const pafp8_batch *batch, const
     // Many uniform splits (at least one per wave slot of the GPU: 64
     // partitions of four 256k-token requests, say) run in wave mode: every
     // wave takes one or two whole splits of one (request, KV head) and
-    // writes their partial rows itself, so split boundaries cost no barrier.  It needs splits
-    // of whole tiles (64 e4m3 or 32 bf16 tokens) on the MFMA path with pages
-    // of at least a tile; the append taken into the launch keeps the
-    // work-group mode.
+    // writes their partial rows itself, so split boundaries cost no barrier.
+    // It needs splits of whole tiles (64 e4m3 or 32 bf16 tokens) and pages of
+    // at least a tile; the append taken into the launch keeps the work-group
+    // mode.
     p.wave_parts = 0;
     p.part_tiles = 0;
-    if (!balanced && S > 1 && p.group >= 2 && !append) {
+    if (!balanced && S > 1 && !append) {
         const int64_t tile = cache->kv_dtype == PAFP8_KV_BF16 ? 32 : 64;
         const int64_t split_tokens = static_cast<int64_t>(p.pages_per_split) * cache->page_size;
         const int64_t units = static_cast<int64_t>(batch->batch) * cache->num_kv_heads * S;

@@ -23,8 +23,8 @@
 //    loads go out as soon as Q.K^T has consumed this tile's K, its V loads as
 //    soon as P.V has consumed this tile's V; page ids arrive through scalar
 //    loads a tile ahead, so they never queue behind the vector loads;
-//  * G >= 2 (grouped query heads): Q.K^T and P.V run on 16x16x32 MFMAs and
-//    the whole query group shares one K/V tile held in registers.  Q.K^T takes
+//  * Q.K^T and P.V run on 16x16x32 MFMAs and the whole query group shares
+//    one K/V tile held in registers.  Q.K^T takes
 //    the tile's tokens as rows and the group's heads as columns (K decoded
 //    exactly to bf16; Q is bf16 already); P.V takes head dims as rows (V
 //    exact in bf16, P split into a bf16 high and low part; with at most 8
@@ -35,8 +35,10 @@
 //    feeds to the next MFMA, and the head a lane owns never changes: the
 //    online softmax needs two cross-lane max exchanges per tile and no other
 //    data movement;
-//  * G == 1: there is no contraction to speak of, so a vector path does the
-//    dot products with FMAs (lane = token for Q.K, lane = head dim for P.V);
+//  * one query head per KV head (G == 1) takes the same MFMA kernels with
+//    one live column: the matrix cores have the idle columns to spare, and
+//    the tile's conversions and loads are what they are at any G, whereas
+//    the same dot products on FMAs kept the VALU too busy to stream;
 //  * every kernel has an APPEND instantiation that also writes the step's new
 //    token (the append taken into the attention launch).
 // Arithmetic: scores and outputs accumulate in fp32, softmax in the exp2
@@ -195,7 +197,7 @@ __device__ __forceinline__ u32x4 keep_bytes(u32x4 w, int n)
 }
 
 // ===========================================================================
-// MFMA path (G >= 2)
+// MFMA path (every query group size, 1 to 16)
 // ===========================================================================
 template <bool BF16, int D>
 struct Geo {
@@ -926,261 +928,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_bal_mfma_kernel(AttnP
     }
 }
 
-// ===========================================================================
-// vector path (G == 1)
-// ===========================================================================
-template <bool BF16, int D>
-struct VecGeo {
-    static constexpr int E = BF16 ? 2 : 1;
-    static constexpr int TT = 64;                 // tokens per wave tile, lane = token
-    static constexpr int KL = D * E / 16;         // 16-byte loads per K row
-    static constexpr int ROWS = D / 64;           // V rows (head dims) per lane
-    static constexpr int VL = 16 * E / 16;        // 16-byte loads per 16-token V run
-};
-
-// 16 bytes -> 16 (fp8) or 8 (bf16) floats, dot with q[base..] from LDS
-template <bool BF16>
-__device__ __forceinline__ float dot16(u32x4 w, const float *__restrict__ qs, float acc)
-{
-    if constexpr (BF16) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc = __builtin_fmaf(bf16_lo(w[e]), qs[2 * e], acc);
-            acc = __builtin_fmaf(bf16_hi(w[e]), qs[2 * e + 1], acc);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const f32x2 a = e4m3x2_to_f32x2<false>(w[e]);
-            const f32x2 b = e4m3x2_to_f32x2<true>(w[e]);
-            acc = __builtin_fmaf(a[0], qs[4 * e], acc);
-            acc = __builtin_fmaf(a[1], qs[4 * e + 1], acc);
-            acc = __builtin_fmaf(b[0], qs[4 * e + 2], acc);
-            acc = __builtin_fmaf(b[1], qs[4 * e + 3], acc);
-        }
-    }
-    return acc;
-}
-
-template <int D>
-struct VecSmem {
-    MergeSmem<D> merge;
-    float q[D];
-    float p[kWaves][64];
-};
-
-template <bool BF16, int D>
-__device__ __forceinline__ int vec_range(const AttnParams &p, VecSmem<D> &sm, int b, int g,
-                                         const SplitRange &rng)
-{
-    using V_ = VecGeo<BF16, D>;
-    const int lane = threadIdx.x & 63;
-    const int wave = uniform(threadIdx.x >> 6);
-
-    for (int d = threadIdx.x; d < D; d += kThreads)
-        sm.q[d] = __uint_as_float(static_cast<uint32_t>(p.q[(static_cast<int64_t>(b) * p.num_q_heads + g) * D + d]) << 16);
-    __syncthreads();
-
-    float acc[V_::ROWS];
-#pragma unroll
-    for (int r = 0; r < V_::ROWS; ++r)
-        acc[r] = 0.f;
-    float m = kNegInf, l = 0.f;
-    int bad = 0;
-    const int64_t ntok = rng.t1 - rng.t0;
-    const int ntiles = rng.state == 0 ? static_cast<int>((ntok + V_::TT - 1) / V_::TT) : 0;
-    const float cs = (BF16 ? 1.0f : p.k_scale[g]) * p.sm_scale * kLog2e;
-    const int P = 1 << p.log2_page;
-    const int64_t head_bytes = static_cast<int64_t>(P) * D * V_::E;
-    const int64_t page_bytes = head_bytes * p.num_kv_heads;
-    const uint8_t *k_head = p.k_pool + g * head_bytes;
-    const uint8_t *v_head = p.v_pool + g * head_bytes;
-    const page_row_t row = page_row(p, b);
-    // segment of the block layout: min(page, 64 bytes / element) tokens
-    const int log2_seg = p.log2_page < (BF16 ? 5 : 6) ? p.log2_page : (BF16 ? 5 : 6);
-
-    // A wave's tiles are i = wave, wave + kWaves, ...  On e4m3 pools the next
-    // tile's loads go out before the current tile's arithmetic.  Past the
-    // last tile that prefetch reads the current tile again (just fetched, so
-    // it comes from the caches): loads stay unconditional, which keeps the
-    // compiler's wait counts exact across the loop.  A bf16 tile holds twice
-    // the registers; two of them cost more occupancy than the overlap gains
-    // (measured), so bf16 pools take one tile at a time.
-    struct Tile {
-        u32x4 k[V_::KL];
-        u32x4 v[V_::ROWS][4][V_::VL];
-    };
-    const int q = lane >> 4;
-    constexpr int LOG2_TG = BF16 ? 3 : 4;     // tokens per K token group: 16 / e
-    constexpr int KLc = V_::KL / 4;           // chunks per quarter row
-    const int log2_ns = log2_seg - LOG2_TG;
-    auto issue = [&](int64_t T0, const TilePages &pg, Tile &t) {
-        // K row of token T0 + lane: token TG*sub + 4j + a of its segment keeps
-        // chunk qc*KLc + l at chunk ((j*KLc + l)*4 + qc)*(4*NS) + 4*sub + a
-        const int kslot = static_cast<int>((T0 + q * 16) & (P - 1)) + (lane & 15);
-        const int ku = kslot & ((1 << log2_seg) - 1);
-        const int kw = ku & ((1 << LOG2_TG) - 1);
-        const uint8_t *kp = k_head + static_cast<int64_t>(select4(q, pg)) * page_bytes +
-                            (kslot >> log2_seg) * ((D * V_::E) << log2_seg) +
-                            ((((kw >> 2) * KLc * 4) << (2 + log2_ns)) + ((ku >> LOG2_TG) << 2) + (kw & 3)) * 16;
-#pragma unroll
-        for (int e = 0; e < V_::KL; ++e)
-            t.k[e] = load16_stream(kp + ((((e % KLc) * 4 + e / KLc) << (2 + log2_ns)) * 16));
-        // V: rows lane + 64*r, four 16-token runs; a segment is [D][tokens]
-#pragma unroll
-        for (int r = 0; r < V_::ROWS; ++r)
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int vslot = static_cast<int>((T0 + qq * 16) & (P - 1));
-                const uint8_t *vp = v_head + static_cast<int64_t>(pg.pid[qq]) * page_bytes +
-                                    ((((vslot >> log2_seg) * D + lane + 64 * r) << log2_seg) +
-                                     (vslot & ((1 << log2_seg) - 1))) * V_::E;
-#pragma unroll
-                for (int e = 0; e < V_::VL; ++e)
-                    t.v[r][qq][e] = load16_stream(vp + 16 * e);
-            }
-    };
-    auto consume = [&](int64_t T0, const Tile &t) {
-        // score of token T0 + lane
-        constexpr int PER = BF16 ? 8 : 16;  // elements per 16-byte load
-        float sc = 0.f;
-#pragma unroll
-        for (int e = 0; e < V_::KL; ++e)
-            sc = dot16<BF16>(t.k[e], &sm.q[e * PER], sc);
-        const bool valid = T0 + lane < rng.t1;
-        sc = valid ? sc : kNegInf;
-        const float mx = wave_max(sc);
-        const float m_new = __builtin_fmaxf(m, mx * cs);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc, cs, -m_new));
-        l = l * alpha + pv;
-        m = m_new;
-        sm.p[wave][lane] = pv;  // this wave's 64 weights, read back by every lane
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int r = 0; r < V_::ROWS; ++r) {
-            float a = acc[r] * alpha;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int64_t nv64 = rng.t1 - (T0 + qq * 16);
-                const int nv = nv64 <= 0 ? 0 : (nv64 >= 16 ? 16 : static_cast<int>(nv64));
-#pragma unroll
-                for (int e = 0; e < V_::VL; ++e) {
-                    u32x4 w = t.v[r][qq][e];
-                    if (nv < 16)
-                        w = keep_bytes(w, BF16 ? (nv - 8 * e) * 2 : nv);
-                    const float *ps = &sm.p[wave][qq * 16 + e * PER];
-                    if constexpr (BF16) {
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            a = __builtin_fmaf(bf16_lo(w[x]), ps[2 * x], a);
-                            a = __builtin_fmaf(bf16_hi(w[x]), ps[2 * x + 1], a);
-                        }
-                    } else {
-                        a = dot16<false>(w, ps, a);
-                    }
-                }
-            }
-            acc[r] = a;
-        }
-        __builtin_amdgcn_wave_barrier();
-    };
-
-    if constexpr (BF16) {
-        for (int i = wave; i < ntiles; i += kWaves) {
-            const int64_t T0 = rng.t0 + static_cast<int64_t>(i) * V_::TT;
-            const TilePages pg = pages_ok(fetch_pages(row, T0, 16, p.log2_page, rng.p_last), p.num_pages, bad);
-            Tile t;
-            issue(T0, pg, t);
-            consume(T0, t);
-        }
-    } else if (wave < ntiles) {
-        const int64_t stride = static_cast<int64_t>(kWaves) * V_::TT;
-        int i = wave;
-        int64_t T0 = rng.t0 + static_cast<int64_t>(i) * V_::TT;
-        TilePages pg = pages_ok(fetch_pages(row, T0, 16, p.log2_page, rng.p_last), p.num_pages, bad);
-        TilePages pgn = fetch_pages(row, T0 + stride, 16, p.log2_page, rng.p_last);
-        Tile ta, tb;
-        issue(T0, pg, ta);
-        // one step: tile i is in `cur`; the next (or tile i again) into `nxt`
-        auto step = [&](Tile &cur, Tile &nxt) {
-            const bool more = i + kWaves < ntiles;
-            TilePages pn = pg;
-            if (more)
-                pn = pages_ok(pgn, p.num_pages, bad);
-            pgn = fetch_pages(row, T0 + 2 * stride, 16, p.log2_page, rng.p_last);
-            issue(more ? T0 + stride : T0, pn, nxt);
-            consume(T0, cur);
-            i += kWaves;
-            T0 += stride;
-            pg = pn;
-            return more;
-        };
-        while (step(ta, tb) && step(tb, ta)) {
-        }
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-        sm.merge.m[wave][0] = m;
-        sm.merge.l[wave][0] = l;
-    }
-#pragma unroll
-    for (int r = 0; r < V_::ROWS; ++r)
-        sm.merge.o[wave][0][lane + 64 * r] = acc[r];
-    return bad;
-}
-
-template <bool BF16, int D, bool APPEND>
-__global__ __launch_bounds__(kThreads) void decode_attn_vec_kernel(AttnParams p)
-{
-    __shared__ VecSmem<D> sm;
-
-    int idx = blockIdx.x;
-    const int s = idx % p.num_splits;
-    idx /= p.num_splits;
-    const int g = idx % p.num_kv_heads;
-    const int b = idx / p.num_kv_heads;
-
-    const SplitRange rng = split_range(p, b, s);
-    if constexpr (APPEND) {
-        const int64_t L = p.context_lens[b];
-        if (rng.state == 0 && rng.t0 < rng.t1 && rng.t1 == L)
-            append_new_token<BF16, D>(p, b, g, L);
-    }
-    int bad = vec_range<BF16, D>(p, sm, b, g, rng);
-    bad = __syncthreads_or(bad);
-    merge_and_write<D>(sm.merge, 1, rng.state, bad, BF16 ? 1.0f : p.v_scale[g],
-                       split_dst<D>(p, b, g, s));
-}
-
-template <bool BF16, int D, bool APPEND>
-__global__ __launch_bounds__(kThreads) void decode_attn_bal_vec_kernel(AttnParams p)
-{
-    __shared__ VecSmem<D> sm;
-    __shared__ BalSmem bs;
-
-    const int g = blockIdx.x % p.num_kv_heads;
-    const int w = blockIdx.x / p.num_kv_heads;
-    const BalRange r = bal_range(p, bs, w, g == 0 && w == 0);
-    int64_t ps = r.ps0;
-    for (int b = r.b0; b < p.batch && ps < r.hi; ++b) {
-        const ReqPages rq = request_pages(p, b);
-        if (rq.n > 0) {
-            const SplitRange rng = piece_range(p, r, ps, rq);
-            if constexpr (APPEND) {
-                if (ps + rq.n <= r.hi)  // the piece ends at the request's last token
-                    append_new_token<BF16, D>(p, b, g, rq.L);
-            }
-            int bad = vec_range<BF16, D>(p, sm, b, g, rng);
-            bad = __syncthreads_or(bad);
-            merge_and_write<D>(sm.merge, 1, 0, bad, BF16 ? 1.0f : p.v_scale[g],
-                               piece_dst<D>(p, r, ps, rq, b, g, w));
-            __syncthreads();  // sm is written again by the next piece
-        }
-        ps += rq.n;
-    }
-}
-
 template <bool BF16, int D, bool APPEND, bool DUP>
 void launch_mfma_t(const AttnParams &p, dim3 grid, dim3 block, bool bal, hipStream_t stream)
 {
@@ -1210,12 +957,7 @@ hipError_t launch_attn_t(const AttnParams &p, hipStream_t stream)
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
-    if (p.group == 1) {
-        if (bal)
-            hipLaunchKernelGGL((decode_attn_bal_vec_kernel<BF16, D, APPEND>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((decode_attn_vec_kernel<BF16, D, APPEND>), grid, block, 0, stream, p);
-    } else if (wave_mode && !APPEND && p.log2_page >= Geo<BF16, D>::LOG2_TT) {
+    if (wave_mode && !APPEND && p.log2_page >= Geo<BF16, D>::LOG2_TT) {
         if (p.group <= 8)
             hipLaunchKernelGGL((decode_attn_mfma_wave_kernel<BF16, D, true, true>), grid, block, 0, stream, p);
         else

@@ -18,8 +18,8 @@ Peaked softmax and dynamic range (device-drawn, seeded; inputs.py recipes):
   data scaled by 2^+-20 (scales amax/448 far from 1, with q scaled the other
   way so the scores stay peaked; outputs compared after undoing the V
   factor), for S = 1, S = 4 and the balanced partition, both pool types, on
-  the BIG-page MFMA path, the 16-token-page path (G = 4) and the vector path
-  (G = 1); and the needle case at 262144 tokens: every wave's first tile holds
+  the BIG-page MFMA path, the 16-token-page path (G = 4) and one query head
+  per KV head (G = 1); and the needle case at 262144 tokens: every wave's first tile holds
   a needle and the other 262,000 tokens each weigh about exp(-17.6) of one,
   below half of fp16's smallest subnormal, so a kernel that rounded P to fp16
   would drop their 0.07% of the mass (x the +4 channel bias: 3e-3 absolute)
@@ -215,7 +215,7 @@ PEAKED = [
        v_bias=4.0),
     # 16-token pages (the page-gathering MFMA path), G = 4
     _w("q16_vbias_gqa4_p16_8k", 2, 32, 8, 16, 8192, q_mult=16.0, v_bias=4.0),
-    # one query head per KV head (the vector path)
+    # one query head per KV head (one live MFMA column)
     _w("q16_vbias_mha_16k", 1, 8, 8, 64, 16384, q_mult=16.0, v_bias=4.0),
 ]
 

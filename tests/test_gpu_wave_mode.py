@@ -2,8 +2,10 @@
 the GPU (4 x num_cus split units), every wave takes whole splits of one
 (request, KV head) and writes their partial rows itself, and the combine
 merges them.  The library picks the mode from the launch size; these batches
-are sized to select it (48 requests x 8 KV heads x 16 or 7 splits on 256
-CUs: 6 or 2 splits per wave, with a shorter last chunk), with ragged lengths
+are sized to select it on 256 CUs (48 requests x 8 KV heads x 16 or 7
+splits: 6 or 2 splits per wave, with a shorter last chunk; and one query
+head per KV head, 12 requests x 32 KV heads x 16 or 3 splits: two splits or
+one per wave), with ragged lengths
 (requests that end inside a split, splits past a request's end), one aborted
 request, both pool types; every output against the oracle, and the pools
 byte for byte.  The same requests through the work-group mode (one request
@@ -24,11 +26,15 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
+GROUPS = {"g8": (48, 64, 8), "g1": (12, 32, 32)}   # requests, query heads, KV heads
+
+
 @pytest.mark.parametrize("kv_dtype", [ops.KV_FP8_E4M3, ops.KV_BF16], ids=["fp8", "bf16"])
-@pytest.mark.parametrize("splits", [16, 7])
-def test_wave_mode_matches_oracle(kv_dtype, splits):
-    w = I.Workload("wavemode", 48, 64, 8, 128, 64, 300, 4096, pool_factor=1.2, stale_requests=1)
-    print(f"wave mode: dtype={kv_dtype} splits={splits}", flush=True)
+@pytest.mark.parametrize("group,splits", [("g8", 16), ("g8", 7), ("g1", 16), ("g1", 3)])
+def test_wave_mode_matches_oracle(kv_dtype, group, splits):
+    B, Hq, Hkv = GROUPS[group]
+    w = I.Workload("wavemode", B, Hq, Hkv, 128, 64, 300, 4096, pool_factor=1.2, stale_requests=1)
+    print(f"wave mode: dtype={kv_dtype} {group} splits={splits}", flush=True)
     lengths = I.context_lengths(w, 901)
     lengths[7] = 4096                                  # max_pages_per_req = 64
     inp = I.make_decode_inputs(w, 901, lengths=lengths)
@@ -59,6 +65,10 @@ def test_wave_mode_matches_oracle(kv_dtype, splits):
                               step.batch.context_lens[b:b + 1].contiguous(), status[b:b + 1].contiguous())
         o1, l1 = ops.paged_decode_attn(step.cache, one, step.q[b:b + 1].contiguous(), sm, splits)
         torch.cuda.synchronize()
-        ok1, ma, _ = allclose_report(o1.cpu().numpy(), ro[b:b + 1])
-        ok2, la, _ = allclose_report(l1.cpu().numpy(), rl[b:b + 1])
+        o1, l1 = o1.cpu().numpy(), l1.cpu().numpy()
+        if st[b] != 0:   # the aborted request: fixed outputs
+            assert np.all(o1 == 0) and np.all(np.isneginf(l1)), f"aborted request {b} alone"
+            continue
+        ok1, ma, _ = allclose_report(o1, ro[b:b + 1])
+        ok2, la, _ = allclose_report(l1, rl[b:b + 1])
         assert ok1 and ok2, f"request {b} alone: out {ma}, lse {la}"
