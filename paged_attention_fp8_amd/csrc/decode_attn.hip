@@ -856,12 +856,29 @@ __device__ __forceinline__ void mfma_range(const AttnParams &p, MergeSmem<D> *sm
         flush();
 }
 
+// MI355X deals the work-groups of a launch to its 8 XCDs in turn (block i to
+// XCD i mod 8).  This renumbering hands XCD x the x-th contiguous range of
+// the launch's n work units instead (ranges of n/8, the first n mod 8 one
+// longer), so that the units of one request -- all its KV heads and splits,
+// which read the same pages -- share an XCD.  Measured on equal-length
+// batches: 64 x 16k e4m3 about 0.6% faster, the bf16 twin and the balanced
+// partition about 2%, one query head per KV head 1-3%.  A ragged batch at
+// one split per request loses about 2% (the XCDs then carry unequal bytes),
+// which the balanced partition is for.  Any n: a bijection of [0, n).
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_unit(int i, int n)
+{
+    const int x = i % kXcds, k = i / kXcds, q = n / kXcds, r = n % kXcds;
+    return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
 template <bool BF16, int D, bool BIG, bool APPEND, bool DUP>
 __global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel(AttnParams p)
 {
     __shared__ MergeSmem<D> sm;
 
-    int idx = blockIdx.x;
+    int idx = xcd_unit(blockIdx.x, gridDim.x);
     const int s = idx % p.num_splits;
     idx /= p.num_splits;
     const int g = idx % p.num_kv_heads;
@@ -908,8 +925,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_bal_mfma_kernel(AttnP
     __shared__ MergeSmem<D> sm;
     __shared__ BalSmem bs;
 
-    const int g = blockIdx.x % p.num_kv_heads;
-    const int w = blockIdx.x / p.num_kv_heads;
+    const int u = xcd_unit(blockIdx.x, gridDim.x);
+    const int g = u % p.num_kv_heads;
+    const int w = u / p.num_kv_heads;
     const BalRange r = bal_range(p, bs, w, g == 0 && w == 0);
     int64_t ps = r.ps0;
     for (int b = r.b0; b < p.batch && ps < r.hi; ++b) {
