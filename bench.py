@@ -731,6 +731,11 @@ def gqa4_4k(args, dev):
     return res
 
 
+def _mha_g1_workload():
+    from paged_attention_fp8_amd import inputs as I
+    return I.Workload("mha_g1_16k_b8", 8, 32, 32, 128, 64, 16384, 16384, pool_factor=1.0)
+
+
 def mha_g1(args, dev):
     """One query head per KV head (one live MFMA column of the group): 8
     requests of 16,384 tokens, 32 heads, head_dim 128, 64-token pages,
@@ -739,7 +744,7 @@ def mha_g1(args, dev):
     import torch
     from paged_attention_fp8_amd import inputs as I
     from paged_attention_fp8_amd import ops
-    w = I.Workload("mha_g1_16k_b8", 8, 32, 32, 128, 64, 16384, 16384, pool_factor=1.0)
+    w = _mha_g1_workload()
     res = {"workload": "mha_g1_16k_b8: 8 requests x 16384 tokens, 32 query heads = 32 KV heads, head_dim 128, "
                        "64-token pages, flushed caches"}
     for kv_dtype, name in ((ops.KV_FP8_E4M3, "e4m3"), (ops.KV_BF16, "bf16")):
@@ -801,6 +806,8 @@ def _preset_bytes(name):
         return _attn_workload_bytes(I.WORKLOADS["gqa4_4k_outliers"], SEED, 1)
     if name == "decode_attn_bal_e4m3_ragged_32k":
         return _attn_workload_bytes(I.WORKLOADS["gqa8_ragged_32k"], SEED, 1)
+    if name == "decode_attn_e4m3_mha_16k_b8":
+        return _attn_workload_bytes(_mha_g1_workload(), SEED, 1)
     if name == "kv_fill_e4m3_handoff_8k_b8":
         return _handoff_bytes()
     if name == "int4_gemv_row_28672x8192_m1":
@@ -833,6 +840,10 @@ COUNTER_PRESETS = {
         what="e4m3 attention, balanced partition, 32 ragged requests of 1k-32k tokens",
         args="--only fp8_vs_bf16 --steps 3 --warmup 1",
         kernel="decode_attn_bal_mfma_kernel<false, 128, true, false, true>", sources=_ATTN),
+    "decode_attn_e4m3_mha_16k_b8": dict(
+        what="e4m3 attention with one query head per KV head, 8 requests x 16384 tokens, 32 heads",
+        args="--only mha_g1 --steps 3 --warmup 1",
+        kernel="decode_attn_mfma_kernel<false, 128, true, false, true>", sources=_ATTN),
     "kv_fill_e4m3_handoff_8k_b8": dict(
         what="kv_quant_fill of 8 prompts x 8192 bf16 tokens into e4m3 pages",
         args="--only prefill_handoff --steps 3 --warmup 1",
