@@ -608,7 +608,7 @@ pafp8_status int4_gemv(const uint16_t *x, int32_t M, const uint8_t *w_packed, co
         const int32_t m = M - m0 < 64 ? M - m0 : 64;
         const hipError_t e = pafp8::launch_int4_gemv(x + static_cast<int64_t>(m0) * K, m, w_packed,
                                                      scales, N, K, y + static_cast<int64_t>(m0) * N,
-                                                     stream);
+                                                     device_cu_count(), stream);
         if (e != hipSuccess)
             return hip_status(e, "int4_gemv launch");
     }

@@ -118,21 +118,27 @@ __device__ __forceinline__ bf16x8 int4x8_to_bf16_plus136(uint32_t w)
 // 136 + q (fewer VALU operations, features of each 8-block paired (i, i+4) in
 // both operands) and the 136 taken back out by MFMAs of the same x against a
 // constant -136, which the matrix cores absorb while they idle at few rows.
-template <int MT, int PF, bool PLUS136>
-__global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
+// WAVES: waves per work-group; the first tiles_per_wg of them own a tile
+// each, and the others (8-wave work-groups owning 5-7 tiles) only help
+// stage x, so that a launch can give every CU the same number of tiles.
+template <int MT, int PF, bool PLUS136, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void int4_gemv_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ w,
-    const uint16_t *__restrict__ scales, int N, int K, float *__restrict__ y)
+    const uint16_t *__restrict__ scales, int N, int K, float *__restrict__ y, int tiles_per_wg)
 {
+    constexpr int THREADS = 64 * WAVES;
     constexpr int XC = MT == 1 ? 4 : (MT == 2 ? 2 : 1);  // groups per staged x chunk
     constexpr int XS = XC * kGroup + 8;                  // LDS row stride (bf16), 16 bytes of padding
-    constexpr int XP = MT * XC;                          // 16-byte x pieces per thread per chunk
+    constexpr int XP = MT * XC * kGemvWaves / WAVES;     // 16-byte x pieces per thread per chunk
+    static_assert(MT * XC * kGemvWaves % WAVES == 0, "a chunk of x splits evenly over the threads");
     __shared__ __align__(16) uint16_t xs[2][MT * 16 * XS];
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int tid = threadIdx.x;
     const int n_tiles = N / 16;
-    const int nt = blockIdx.x * kGemvWaves + wave;  // this wave's 16-row tile
-    const bool live = nt < n_tiles;
+    const int nt = blockIdx.x * tiles_per_wg + wave;  // this wave's 16-row tile
+    const bool owner = wave < tiles_per_wg;           // wave-uniform
+    const bool live = owner && nt < n_tiles;
     const int G = K / kGroup;
     const int c = lane & 15, kq = lane >> 4;
 
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
     auto load_x = [&](int ch) {
 #pragma unroll
         for (int it = 0; it < XP; ++it) {
-            const int idx = tid + it * kGemvThreads;
+            const int idx = tid + it * THREADS;
             const int m = idx / (XC * kGroup / 8), c8 = idx % (XC * kGroup / 8);
             const int mr = m < M ? m : M - 1;
             xr[it] = load16(x + static_cast<int64_t>(mr) * K + static_cast<int64_t>(ch) * XC * kGroup + c8 * 8);
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
     auto store_x = [&](int buf) {
 #pragma unroll
         for (int it = 0; it < XP; ++it) {
-            const int idx = tid + it * kGemvThreads;
+            const int idx = tid + it * THREADS;
             const int m = idx / (XC * kGroup / 8), c8 = idx % (XC * kGroup / 8);
             u32x4 v = m < M ? xr[it] : u32x4{0u, 0u, 0u, 0u};
             if (PLUS136) {
@@ -168,6 +174,19 @@ __global__ __launch_bounds__(kGemvThreads) void int4_gemv_kernel(
         }
     };
 
+    if (!owner) {
+        // a helper wave: the same x staging and barriers as the owners' loop
+        load_x(0);
+        store_x(0);
+        __syncthreads();
+        const int last_ch = G / XC - 1;
+        for (int ch = 0; ch <= last_ch; ++ch) {
+            load_x(ch + 1 <= last_ch ? ch + 1 : last_ch);
+            store_x((ch + 1) & 1);
+            __syncthreads();
+        }
+        return;
+    }
     const uint8_t *wb = w + (static_cast<int64_t>(live ? nt : 0) * G) * 1024 + lane * 16;
     const uint16_t *sp = scales + (live ? nt : 0) * 16 + c;
     f32x4 acc[MT];
@@ -602,10 +621,27 @@ __global__ __launch_bounds__(256) void int4_pack_kernel(const uint32_t *__restri
 }  // namespace
 
 hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const uint16_t *scales,
-                            int N, int K, float *y, hipStream_t stream)
+                            int N, int K, float *y, int num_cus, hipStream_t stream)
 {
     const int n_tiles = N / 16;
     const dim3 grid((n_tiles + kGemvWaves - 1) / kGemvWaves);
+    // 2-16 rows: tiles per work-group (4 to 8) so that the busiest CU holds
+    // the fewest tiles, one work-group per CU at a time counted; ties go to
+    // more tiles per work-group (x staged fewer times).  28672 rows of
+    // weights on 256 CUs: 7 tiles, 256 work-groups, against 448 four-tile
+    // work-groups on which three CUs in four hold 8 tiles.
+    int tpw = kGemvWaves;
+    {
+        int64_t best = -1;
+        for (int t = 8; t >= kGemvWaves; --t) {
+            const int64_t wgs = (n_tiles + t - 1) / t;
+            const int64_t busiest = (wgs + num_cus - 1) / num_cus * t;
+            if (best < 0 || busiest < best) {
+                best = busiest;
+                tpw = t;
+            }
+        }
+    }
     const int mt = (M + 15) / 16;
     const bool pf8 = (K / kGroup) % 8 == 0;   // K % 512 == 0 gives a multiple of 4
     if (M == 1) {
@@ -616,16 +652,24 @@ hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const ui
     }
 #define PAFP8_GEMV(MT_)                                                                            \
     if (pf8)                                                                                       \
-        hipLaunchKernelGGL((int4_gemv_kernel<MT_, 8, (MT_ <= 2)>), grid, dim3(kGemvThreads), 0, stream, \
-                           x, M, w, scales, N, K, y);                                             \
+        hipLaunchKernelGGL((int4_gemv_kernel<MT_, 8, (MT_ <= 2), kGemvWaves>), grid, dim3(kGemvThreads), 0, \
+                           stream, x, M, w, scales, N, K, y, kGemvWaves);                         \
     else                                                                                           \
-        hipLaunchKernelGGL((int4_gemv_kernel<MT_, 4, (MT_ <= 2)>), grid, dim3(kGemvThreads), 0, stream, \
-                           x, M, w, scales, N, K, y);
+        hipLaunchKernelGGL((int4_gemv_kernel<MT_, 4, (MT_ <= 2), kGemvWaves>), grid, dim3(kGemvThreads), 0, \
+                           stream, x, M, w, scales, N, K, y, kGemvWaves);
     // 17-64 rows on 32x32 tiles (K a multiple of 1024: whole prefetch rings
     // in each quarter of K; and 32-bit buffer offsets into x and the scales)
     const bool wide = (K / kGroup / 4) % 2 == 0 && static_cast<int64_t>(K) * 64 * 2 < INT32_MAX &&
                       static_cast<int64_t>(K / kGroup + 1) * N * 2 < INT32_MAX;
-    if (mt == 1) {
+    if (mt == 1 && tpw > kGemvWaves) {
+        const dim3 grid8((n_tiles + tpw - 1) / tpw);
+        if (pf8)
+            hipLaunchKernelGGL((int4_gemv_kernel<1, 8, true, 8>), grid8, dim3(8 * 64), 0, stream, x, M, w,
+                               scales, N, K, y, tpw);
+        else
+            hipLaunchKernelGGL((int4_gemv_kernel<1, 4, true, 8>), grid8, dim3(8 * 64), 0, stream, x, M, w,
+                               scales, N, K, y, tpw);
+    } else if (mt == 1) {
         PAFP8_GEMV(1)
     } else if (mt == 2 && wide) {
         hipLaunchKernelGGL((int4_gemv_wide_kernel<1>), dim3((n_tiles + 7) / 8), dim3(kWideThreads), 0, stream, x,

@@ -69,7 +69,7 @@ hipError_t launch_kv_write(bool bf16_pool, int head_dim, const WriteParams &p,
 
 // INT4 weight streaming: y[M][N] = x[M][K] . (q * s)^T, w in packed blocks.
 hipError_t launch_int4_gemv(const uint16_t *x, int M, const uint8_t *w, const uint16_t *scales,
-                            int N, int K, float *y, hipStream_t stream);
+                            int N, int K, float *y, int num_cus, hipStream_t stream);
 hipError_t launch_int4_pack(const uint8_t *src, uint8_t *dst, int N, int K, hipStream_t stream);
 
 // Measurement: a bare read of bytes (a multiple of kStreamReadTile) by

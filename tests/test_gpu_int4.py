@@ -105,6 +105,22 @@ def test_gemv_full_size_decode_shape():
         assert np.all(err <= bound), (err.max(), (err / bound).max())
 
 
+@pytest.mark.parametrize("M,N,K", [(8, 20480, 1536), (16, 24576, 1024), (2, 28688, 2048),
+                                   (16, 32768, 512), (9, 28672, 1536)])
+def test_gemv_tiles_per_work_group(M, N, K):
+    """2-16 rows with the tile count per work-group chosen from the CU count
+    (on 256 CUs: 5, 6, 8 with a last work-group holding one live tile, 8,
+    and 7), both prefetch depths: every output within the bound."""
+    say(f"int4 gemv tiles per work-group: M={M} N={N} K={K}")
+    q, x, s = _case(M, N, K, 31 * M + N + K)
+    packed = int4_blocks(q)
+    y = ops.int4_gemv(_dev_bf16(x), _dev_u8(packed), _dev_bf16(s), N, K).cpu().numpy()
+    ref = oracle.int4_gemv(x, packed, s, N, K)
+    err = np.abs(y - ref)
+    bound = _bound(q, x, s)
+    assert np.all(err <= bound), (err.max(), (err / bound).max())
+
+
 def test_gemv_edges():
     say("int4 gemv: empty and invalid shapes")
     x = torch.zeros((0, 512), dtype=torch.bfloat16, device=DEV)
