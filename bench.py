@@ -814,6 +814,8 @@ def _preset_bytes(name):
         return _int4_bytes(1)
     if name == "int4_gemv_28672x8192_m64":
         return _int4_bytes(64)
+    if name == "int4_gemv_28672x8192_m16":
+        return _int4_bytes(16)
     raise KeyError(name)
 
 
@@ -853,6 +855,10 @@ COUNTER_PRESETS = {
         what="INT4 weight-streaming GEMV, one row of x, 28672 x 8192 weights",
         args="--only int4_decode_gemv --steps 3 --warmup 1",
         kernel="int4_gemv_row_kernel", sources=("int4_gemv.hip", "pafp8_device.hpp")),
+    "int4_gemv_28672x8192_m16": dict(
+        what="INT4 weight-streaming GEMV, 8 and 16 rows of x (bytes counted at 16), 28672 x 8192 weights",
+        args="--only int4_decode_gemv --steps 3 --warmup 1",
+        kernel="int4_gemv_kernel<1, 8, true, 8>", sources=("int4_gemv.hip", "pafp8_device.hpp")),
     "int4_gemv_28672x8192_m64": dict(
         what="INT4 weight-streaming GEMV, 64 rows of x, 28672 x 8192 weights",
         args="--only int4_decode_gemv --steps 3 --warmup 1",
