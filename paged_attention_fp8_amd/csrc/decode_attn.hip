@@ -24,17 +24,16 @@
 //    soon as P.V has consumed this tile's V; page ids arrive through scalar
 //    loads a tile ahead, so they never queue behind the vector loads;
 //  * Q.K^T and P.V run on 16x16x32 MFMAs and the whole query group shares
-//    one K/V tile held in registers.  Q.K^T takes
-//    the tile's tokens as rows and the group's heads as columns (K decoded
-//    exactly to bf16; Q is bf16 already); P.V takes head dims as rows (V
-//    exact in bf16, P split into a bf16 high and low part; with at most 8
-//    heads in the group the low part rides in the MFMA columns the group
-//    leaves free, otherwise it takes a second MFMA).
-//    Token order inside a tile is permuted so that
-//    the scores an MFMA leaves in a lane are exactly the P operand that lane
-//    feeds to the next MFMA, and the head a lane owns never changes: the
-//    online softmax needs two cross-lane max exchanges per tile and no other
-//    data movement;
+//    one K/V tile held in registers.  Q.K^T takes the tile's tokens as rows
+//    and the group's heads as columns (K decoded exactly to bf16; Q is bf16
+//    already); P.V takes head dims as rows (V exact in bf16, P split into a
+//    bf16 high and low part; with at most 8 heads in the group the low part
+//    rides in the MFMA columns the group leaves free, otherwise it takes a
+//    second MFMA).  Token order inside a tile is permuted so that the scores
+//    an MFMA leaves in a lane are exactly the P operand that lane feeds to
+//    the next MFMA, and the head a lane owns never changes: the online
+//    softmax needs two cross-lane max exchanges per tile and no other data
+//    movement;
 //  * one query head per KV head (G == 1) takes the same MFMA kernels with
 //    one live column: the matrix cores have the idle columns to spare, and
 //    the tile's conversions and loads are what they are at any G, whereas
