@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _draw(n, seed=2026):
+def _draw(n, seed=2026, batch=(1, 7)):
     g = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -32,7 +32,7 @@ def _draw(n, seed=2026):
         while Hkv * G > 64:
             G //= 2
         P = int(g.choice([16, 32, 64, 128, 256]))
-        B = int(g.integers(1, 7))
+        B = int(g.integers(*batch))
         lens = g.integers(1, 3000, B)
         lens[g.integers(0, B)] = P * int(g.integers(1, 12))      # an exact page multiple
         if B > 2:
@@ -42,7 +42,9 @@ def _draw(n, seed=2026):
     return out
 
 
-CONFIGS = _draw(48)
+# 48 small batches, and 32 of 7-24 requests, whose grids (requests x KV
+# heads x splits) are dealt to the XCDs in uneven ranges
+CONFIGS = _draw(48) + [(48 + c[0],) + c[1:] for c in _draw(32, seed=2031, batch=(7, 25))]
 
 
 def _id(c):
