@@ -624,6 +624,12 @@ class ReadCeiling:
                 "read_frac": n / (best[0] * 1e-6) / 1e9 / PEAK_HBM_GBS}
 
 
+# A stream that also writes runs fastest on fine grids (one 16 KiB tile per
+# work-group at the hand-off's size: 57.7 us against 62.1 us at 1024), so its
+# ceiling tries them too; the read-only stream is best at 256-512.
+READ_WRITE_GRIDS = (256, 1024, 4096, 16384)
+
+
 def _read_write_ceiling(rc, src_bytes, ratio, steps, warmup):
     """The bare read of src_bytes with a write of src_bytes / ratio
     (ops.stream_read_write), launched and timed like the hand-off: back to
@@ -635,7 +641,7 @@ def _read_write_ceiling(rc, src_bytes, ratio, steps, warmup):
     if n + n // ratio > rc.CAPACITY:
         raise ValueError("read_write: %d bytes exceed the buffer" % n)
     best = None
-    for g in rc.GRIDS:
+    for g in READ_WRITE_GRIDS:
         rc.ops.stream_read_write(src, dst, g)
         settle()
         for _ in range(warmup):
