@@ -9,6 +9,8 @@ for byte:
                       append taken into the attention launch
   gqa8_16k_b32        the bf16 twin, 32 x 16384 tokens in the same 2 GiB
   gqa8_16k_b{1,8,16}  the small concurrency points, e4m3 and bf16
+  mha_g1_16k_b8       8 x 16384 tokens, 32 query heads = 32 KV heads, both
+                      pools, one split and 8 (wave-per-split mode)
   gqa8_256k_b4        4 x 262144 tokens, one stale request, at the stated 64
                       splits and at the library default
 
@@ -174,6 +176,25 @@ def test_small_concurrency_points_every_output(batch, kv_dtype):
         pools_match(step, inp, pool, status, kv_dtype)
         compare_all(out, lse, ro, rl, f"default splits ({'append in launch' if fused else 'separate'})")
         del step
+
+
+@pytest.mark.parametrize("kv_dtype", [ops.KV_FP8_E4M3, ops.KV_BF16], ids=["fp8", "bf16"])
+def test_one_query_head_per_kv_head_every_output(kv_dtype):
+    """The bench's one-query-head-per-KV-head workload (8 x 16k tokens, 32
+    heads, a group of one on the MFMA kernels): every output at the library
+    default (one split) and at 8 splits, which on 256 CUs runs the
+    wave-per-split mode (2048 splits, two per wave)."""
+    w = I.Workload("mha_g1_16k_b8", 8, 32, 32, 128, 64, 16384, 16384, pool_factor=1.0)
+    say(f"workload {w.name} dtype={kv_dtype}")
+    inp = I.make_device_decode_inputs(w, 1020, DEV)
+    pool, ro, rl, status = full_oracle(inp, kv_dtype)
+    step = H.build_step(inp, kv_dtype, DEV, poison=True)
+    sm = 1.0 / math.sqrt(w.head_dim)
+    for splits in (0, 8):
+        out, lse, _ = H.decode_step(step, sm, splits)
+        torch.cuda.synchronize()
+        compare_all(out, lse, ro, rl, f"splits={splits or 'default'}")
+    pools_match(step, inp, pool, status, kv_dtype)
 
 
 def test_long_context_256k_every_live_output():
