@@ -872,8 +872,12 @@ __device__ __forceinline__ int xcd_unit(int i, int n)
     return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 
+// Three work-groups per CU where the registers allow it without spilling:
+// pages of a whole tile, except the e4m3 kernel that also appends for groups
+// of more than 8 heads.
 template <bool BF16, int D, bool BIG, bool APPEND, bool DUP>
-__global__ __launch_bounds__(kThreads, BIG ? 3 : 2) void decode_attn_mfma_kernel(AttnParams p)
+__global__ __launch_bounds__(kThreads, (BIG && (BF16 || DUP || !APPEND)) ? 3 : 2) void decode_attn_mfma_kernel(
+    AttnParams p)
 {
     __shared__ MergeSmem<D> sm;
 
