@@ -104,6 +104,31 @@ def test_balanced_matches_oracle(w, kv_dtype, groups):
     compare(out, lse, ro, rl, f"{w.name} W={groups}")
 
 
+@pytest.mark.parametrize("kv_dtype", [ops.KV_FP8_E4M3, ops.KV_BF16], ids=["fp8", "bf16"])
+def test_large_batch_matches_oracle(kv_dtype):
+    """999 short ragged requests (1-300 tokens, GQA 16/2, 16-token pages):
+    launch grids of 1998 to 5994 work-groups, not multiples of the 8 XCDs
+    they are dealt to, at the library's default split, 3 splits, and the
+    balanced partition (whose work-groups scan all 999 lengths)."""
+    w = I.Workload("many_short", 999, 16, 2, 128, 16, 1, 300, pool_factor=1.3)
+    say(f"attn large batch: dtype={kv_dtype}")
+    inp = I.make_decode_inputs(w, 31)
+    step = H.build_step(inp, kv_dtype, DEV, poison=True)
+    sm = 1.0 / math.sqrt(w.head_dim)
+    ref = None
+    for splits in (0, 3, -ops.default_balanced_groups(w.kv_heads)):
+        out, lse, status = run_gpu(step, sm, splits)
+        assert np.all(status == 0)
+        if ref is None:
+            ref = oracle_pool(inp, kv_dtype, poison=True)
+            assert pools_equal(step, ref, kv_dtype), "caches differ"
+            ks = inp.k_scale if kv_dtype == ops.KV_FP8_E4M3 else None
+            vs = inp.v_scale if kv_dtype == ops.KV_FP8_E4M3 else None
+            ro, rl = oracle.paged_attention(ref, inp.q, inp.batch.page_table, inp.batch.context_lens,
+                                            sm, ks, vs)
+        compare(out, lse, ro, rl, f"999 requests, splits={splits}")
+
+
 def test_balanced_edge_requests():
     """Balanced partition with aborted, empty and invalid requests between live
     ones, a page id outside the pool inside a cut request, and the library's
