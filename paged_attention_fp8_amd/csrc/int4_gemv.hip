@@ -18,8 +18,10 @@
 // v_mfma_f32_16x16x32_bf16 over the block.
 //
 // 2 to 16 rows of x (and up to 64 when K is not a multiple of 1024): a
-// work-group of 4 waves owns 64 output rows (one 16-row tile per wave) over
-// all of K (int4_gemv_kernel).  Per group of 128 features the work-group
+// work-group owns 4 to 8 tiles of 16 output rows (one tile per wave) over
+// all of K (int4_gemv_kernel); at 2-16 rows the launch picks the tile count
+// that gives every CU the same number of tiles where it can (8-wave
+// work-groups, spare waves staging x).  Per group of 128 features the work-group
 // stages x[0:16*MT][group] in LDS; each wave expands its 1 KiB block to
 // bf16, runs 4 MFMAs per 16-row tile of x and adds s times the group's
 // partial sums into its fp32 accumulators.  Up to 32 rows the expansion is
