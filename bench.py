@@ -1162,10 +1162,15 @@ def main():
         }
         del q
         torch.cuda.empty_cache()
-        result["concurrency_sweep"] = concurrency_sweep(args, dev, head=p)
+        # an extra that raises is recorded in the line, and the rest still run
         for name, fn in EXTRAS.items():
-            if name != "concurrency_sweep":
-                result[name] = fn(args, dev)
+            try:
+                result[name] = (concurrency_sweep(args, dev, head=p) if name == "concurrency_sweep"
+                                else fn(args, dev))
+            except Exception as e:   # noqa: BLE001 -- reported, not hidden
+                log(f"extra {name} failed: {type(e).__name__}: {e}")
+                result[name] = {"error": f"{type(e).__name__}: {e}"}
+                torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(result), flush=True)
